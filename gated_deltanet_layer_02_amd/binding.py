@@ -1,0 +1,183 @@
+"""Thin ctypes binding of libgdn.so (include/gdn.h).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels of
+libgdn.so.  Tensors are torch device tensors (PyTorch supplies device memory
+and streams); a missing library raises instead of falling back to anything.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libgdn.so")
+
+GDN_OK = 0
+GDN_F32, GDN_BF16 = 0, 1
+GDN_FLAG_L2NORM_QK = 0x1
+GDN_PREFILL_MAX_STAGES = 6
+STAGE_NAMES = {0: "chunk_table", 1: "chunk_prep", 2: "state_sweep", 3: "gated_norm",
+               4: "conv_state", 5: "state_copy"}
+
+STATUS_NAMES = {0: "GDN_OK", 1: "GDN_ERR_NULL_ARG", 2: "GDN_ERR_BAD_SHAPE",
+                3: "GDN_ERR_UNSUPPORTED", 4: "GDN_ERR_BAD_DTYPE", 5: "GDN_ERR_MISALIGNED",
+                6: "GDN_ERR_WORKSPACE", 7: "GDN_ERR_HIP", 8: "GDN_ERR_ALIAS",
+                9: "GDN_ERR_BAD_VALUE"}
+
+EXPORTED = ["gdn_status_string", "gdn_prefill_workspace_size", "gdn_prefill",
+            "gdn_prefill_profiled", "gdn_decode"]
+
+
+class GdnError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: {gdn_status_string(code)}")
+        self.code = code
+
+
+class Desc(ctypes.Structure):
+    """gdn_desc."""
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32),
+        ("total_tokens", ctypes.c_int64),
+        ("num_k_heads", ctypes.c_int32),
+        ("num_v_heads", ctypes.c_int32),
+        ("head_k_dim", ctypes.c_int32),
+        ("head_v_dim", ctypes.c_int32),
+        ("conv_kernel", ctypes.c_int32),
+        ("io_dtype", ctypes.c_int32),
+        ("state_dtype", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("l2_eps", ctypes.c_float),
+        ("norm_eps", ctypes.c_float),
+        ("flags", ctypes.c_uint32),
+    ]
+
+
+def make_desc(num_seqs: int, total_tokens: int, num_k_heads: int = 16, num_v_heads: int = 32,
+              io_dtype: int = GDN_BF16, state_dtype: int = GDN_F32, scale: float = 1.0,
+              l2_eps: float = 1e-6, norm_eps: float = 1e-6, l2norm: bool = True,
+              head_dim: int = 128, conv_kernel: int = 4) -> Desc:
+    return Desc(num_seqs=num_seqs, total_tokens=total_tokens, num_k_heads=num_k_heads,
+                num_v_heads=num_v_heads, head_k_dim=head_dim, head_v_dim=head_dim,
+                conv_kernel=conv_kernel, io_dtype=io_dtype, state_dtype=state_dtype,
+                scale=scale, l2_eps=l2_eps, norm_eps=norm_eps,
+                flags=GDN_FLAG_L2NORM_QK if l2norm else 0)
+
+
+_lib = None
+
+
+def lib():
+    """Load libgdn.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "gated_deltanet_layer_02_amd.build.build()")
+        l = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        dp = ctypes.POINTER(Desc)
+        l.gdn_status_string.restype = ctypes.c_char_p
+        l.gdn_status_string.argtypes = [ctypes.c_int]
+        l.gdn_prefill_workspace_size.restype = ctypes.c_int
+        l.gdn_prefill_workspace_size.argtypes = [dp, ctypes.POINTER(sz)]
+        l.gdn_prefill.restype = ctypes.c_int
+        l.gdn_prefill.argtypes = [dp] + [vp] * 14 + [vp, sz, vp]
+        l.gdn_prefill_profiled.restype = ctypes.c_int
+        l.gdn_prefill_profiled.argtypes = [dp] + [vp] * 14 + [vp, sz, vp, vp, vp, vp]
+        l.gdn_decode.restype = ctypes.c_int
+        l.gdn_decode.argtypes = [dp] + [vp] * 11 + [i32, vp, vp]
+        _lib = l
+    return _lib
+
+
+def gdn_status_string(code: int) -> str:
+    try:
+        return lib().gdn_status_string(int(code)).decode()
+    except RuntimeError:
+        return STATUS_NAMES.get(int(code), f"status {code}")
+
+
+def gdn_prefill_workspace_size(desc: Desc) -> int:
+    n = ctypes.c_size_t(0)
+    rc = lib().gdn_prefill_workspace_size(ctypes.byref(desc), ctypes.byref(n))
+    if rc != GDN_OK:
+        raise GdnError(rc, "gdn_prefill_workspace_size")
+    return int(n.value)
+
+
+def _p(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _ws_bytes(workspace) -> int:
+    if workspace is None:
+        return 0
+    if isinstance(workspace, tuple):      # (pointer, bytes)
+        return int(workspace[1])
+    return workspace.numel() * workspace.element_size()
+
+
+def _ws_ptr(workspace):
+    if isinstance(workspace, tuple):
+        return workspace[0]
+    return _p(workspace)
+
+
+def gdn_prefill(desc: Desc, q, k, v, g, beta, *, z=None, conv_w=None, norm_w=None,
+                cu_seqlens=None, initial_state=None, conv_state_in=None, out=None,
+                final_state=None, conv_state_out=None, workspace=None, stream=None,
+                check: bool = True) -> int:
+    rc = lib().gdn_prefill(ctypes.byref(desc), _p(q), _p(k), _p(v), _p(g), _p(beta), _p(z),
+                           _p(conv_w), _p(norm_w), _p(cu_seqlens), _p(initial_state),
+                           _p(conv_state_in), _p(out), _p(final_state), _p(conv_state_out),
+                           _ws_ptr(workspace), _ws_bytes(workspace), _stream(stream))
+    if check and rc != GDN_OK:
+        raise GdnError(rc, "gdn_prefill")
+    return rc
+
+
+def gdn_prefill_profiled(desc: Desc, q, k, v, g, beta, *, events: Sequence[int], z=None,
+                         conv_w=None, norm_w=None, cu_seqlens=None, initial_state=None,
+                         conv_state_in=None, out=None, final_state=None, conv_state_out=None,
+                         workspace=None, stream=None):
+    """Returns the stage ids recorded between events[i] and events[i+1]."""
+    ev = (ctypes.c_void_p * (GDN_PREFILL_MAX_STAGES + 1))(*events)
+    ns = ctypes.c_int32(0)
+    ids = (ctypes.c_int32 * GDN_PREFILL_MAX_STAGES)()
+    rc = lib().gdn_prefill_profiled(ctypes.byref(desc), _p(q), _p(k), _p(v), _p(g), _p(beta),
+                                    _p(z), _p(conv_w), _p(norm_w), _p(cu_seqlens),
+                                    _p(initial_state), _p(conv_state_in), _p(out),
+                                    _p(final_state), _p(conv_state_out), _ws_ptr(workspace),
+                                    _ws_bytes(workspace), _stream(stream), ev,
+                                    ctypes.byref(ns), ids)
+    if rc != GDN_OK:
+        raise GdnError(rc, "gdn_prefill_profiled")
+    return [int(ids[i]) for i in range(ns.value)]
+
+
+def gdn_decode(desc: Desc, q, k, v, g, beta, *, state, out, z=None, conv_w=None, norm_w=None,
+               conv_state=None, state_slots=None, num_state_slots: Optional[int] = None,
+               stream=None, check: bool = True) -> int:
+    if num_state_slots is None:
+        num_state_slots = desc.num_seqs
+    rc = lib().gdn_decode(ctypes.byref(desc), _p(q), _p(k), _p(v), _p(g), _p(beta), _p(z),
+                          _p(conv_w), _p(norm_w), _p(state), _p(conv_state), _p(state_slots),
+                          int(num_state_slots), _p(out), _stream(stream))
+    if check and rc != GDN_OK:
+        raise GdnError(rc, "gdn_decode")
+    return rc

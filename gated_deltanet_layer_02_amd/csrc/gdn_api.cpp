@@ -1,0 +1,251 @@
+// gdn_api.cpp -- the C ABI of libgdn.so: argument validation (host only, before
+// anything is enqueued), workspace sizing and kernel dispatch.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/gdn.h"
+#include "gdn_internal.hpp"
+
+namespace {
+
+using gdn::PrefillLayout;
+
+constexpr int64_t kMaxTokens = (int64_t(1) << 31) - 1;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct Range {
+    uintptr_t lo = 0, hi = 0;   // [lo, hi)
+    Range() = default;
+    Range(const void* p, size_t bytes) : lo(reinterpret_cast<uintptr_t>(p)), hi(lo + bytes) {}
+    bool overlaps(const Range& o) const { return lo < hi && o.lo < o.hi && lo < o.hi && o.lo < hi; }
+};
+
+size_t io_size(gdn_dtype t) { return t == GDN_BF16 ? 2 : 4; }
+
+gdn_status check_desc_common(const gdn_desc* d) {
+    if (d == nullptr) return GDN_ERR_NULL_ARG;
+    if (d->num_seqs < 1 || d->num_k_heads < 1 || d->num_v_heads < 1) return GDN_ERR_BAD_SHAPE;
+    if (d->num_v_heads % d->num_k_heads != 0) return GDN_ERR_BAD_SHAPE;
+    if (d->total_tokens < 0 || d->total_tokens > kMaxTokens) return GDN_ERR_BAD_SHAPE;
+    if ((int64_t)d->num_v_heads * d->num_seqs > (int64_t(1) << 24)) return GDN_ERR_BAD_SHAPE;
+    if (d->num_k_heads > 4096 || d->num_v_heads > 4096) return GDN_ERR_BAD_SHAPE;
+    if (d->head_k_dim != gdn::kD || d->head_v_dim != gdn::kD) return GDN_ERR_UNSUPPORTED;
+    if (d->conv_kernel != gdn::kConvK) return GDN_ERR_UNSUPPORTED;
+    if (d->flags & ~GDN_FLAG_L2NORM_QK) return GDN_ERR_UNSUPPORTED;
+    if (d->io_dtype != GDN_F32 && d->io_dtype != GDN_BF16) return GDN_ERR_BAD_DTYPE;
+    if (d->state_dtype != GDN_F32 && d->state_dtype != GDN_BF16) return GDN_ERR_BAD_DTYPE;
+    if (!isfinite(d->scale) || !isfinite(d->l2_eps) || !isfinite(d->norm_eps)) return GDN_ERR_BAD_VALUE;
+    if (d->l2_eps < 0.f || d->norm_eps < 0.f) return GDN_ERR_BAD_VALUE;
+    return GDN_OK;
+}
+
+// chunk slots of the prep grid: exact for one sequence, a bound for varlen
+int64_t chunk_slots(const gdn_desc* d, bool varlen) {
+    if (!varlen) return (d->total_tokens + gdn::kChunk - 1) / gdn::kChunk;
+    return d->total_tokens / gdn::kChunk + d->num_seqs;
+}
+
+PrefillLayout prefill_layout(const gdn_desc* d, bool varlen) {
+    const size_t C = (size_t)chunk_slots(d, varlen);
+    const size_t Hk = d->num_k_heads, Hv = d->num_v_heads;
+    const size_t mt = io_size(d->io_dtype);       // bytes per MFMA operand element
+    const size_t frag = 8 * mt * 64;              // one fragment of a wave
+    PrefillLayout L{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t at = off; off = round_up(off + bytes, 256); return at; };
+    L.chunk_off = take(sizeof(int32_t) * ((size_t)d->num_seqs + 1));
+    L.Qf = take(C * Hk * 16 * frag);
+    L.KTf = take(C * Hk * 16 * frag);
+    L.Wf = take(C * Hv * 16 * frag);
+    L.Pf = take(C * Hv * 8 * frag);
+    L.Uf = take(C * Hv * 8 * 4 * 64 * 4 * mt);
+    L.gates = take(C * Hv * 128 * sizeof(float));
+    L.total = off;
+    return L;
+}
+
+gdn_status prefill_impl(const gdn_desc* d, const void* q, const void* k, const void* v,
+                        const float* g, const float* beta, const void* z, const void* conv_w,
+                        const void* norm_w, const int32_t* cu_seqlens, const float* initial_state,
+                        const void* conv_state_in, void* out, float* final_state,
+                        void* conv_state_out, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream, hipEvent_t* events, int32_t* num_stages,
+                        int32_t* stage_ids) {
+    gdn_status st = check_desc_common(d);
+    if (st != GDN_OK) return st;
+    if (d->state_dtype != GDN_F32) return GDN_ERR_BAD_DTYPE;
+    const int64_t T = d->total_tokens;
+    const int64_t N = d->num_seqs, Hk = d->num_k_heads, Hv = d->num_v_heads;
+    if (T > 0 && (!q || !k || !v || !g || !beta || !out)) return GDN_ERR_NULL_ARG;
+    if ((z == nullptr) != (norm_w == nullptr)) return GDN_ERR_NULL_ARG;
+    if (cu_seqlens == nullptr && N != 1) return GDN_ERR_NULL_ARG;
+    if (workspace == nullptr && workspace_bytes > 0) return GDN_ERR_WORKSPACE;
+    if (events != nullptr && num_stages == nullptr) return GDN_ERR_NULL_ARG;
+    const void* tensors[] = {q, k, v, g, beta, z, conv_w, norm_w, cu_seqlens, initial_state,
+                             conv_state_in, out, final_state, conv_state_out};
+    for (const void* p : tensors)
+        if (p && !aligned16(p)) return GDN_ERR_MISALIGNED;
+    if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255u)) return GDN_ERR_MISALIGNED;
+
+    const bool varlen = cu_seqlens != nullptr;
+    const PrefillLayout L = prefill_layout(d, varlen);
+    if (workspace == nullptr || workspace_bytes < L.total) return GDN_ERR_WORKSPACE;
+
+    // outputs must not overlap the inputs they are computed from
+    const size_t es = io_size(d->io_dtype);
+    const Range rout(out, (size_t)T * Hv * gdn::kD * es);
+    const Range rin[] = {Range(q, (size_t)T * Hk * gdn::kD * es), Range(k, (size_t)T * Hk * gdn::kD * es),
+                         Range(v, (size_t)T * Hv * gdn::kD * es), Range(z, z ? (size_t)T * Hv * gdn::kD * es : 0),
+                         Range(workspace, L.total)};
+    for (const Range& r : rin)
+        if (out && rout.overlaps(r)) return GDN_ERR_ALIAS;
+    const size_t state_bytes = (size_t)N * Hv * gdn::kD * gdn::kD * sizeof(float);
+    if (final_state && Range(final_state, state_bytes).overlaps(Range(workspace, L.total))) return GDN_ERR_ALIAS;
+    if (final_state && out && Range(final_state, state_bytes).overlaps(rout)) return GDN_ERR_ALIAS;
+    if (final_state && initial_state && final_state != initial_state &&
+        Range(final_state, state_bytes).overlaps(Range(initial_state, state_bytes)))
+        return GDN_ERR_ALIAS;
+
+    char* ws = static_cast<char*>(workspace);
+    gdn::PrefillPlan p{};
+    p.io_bf16 = d->io_dtype == GDN_BF16;
+    p.conv = conv_w != nullptr;
+    p.gated = z != nullptr;
+    p.total_tokens = T;
+    p.chunk_slots = (int32_t)(T > 0 ? chunk_slots(d, varlen) : 0);
+    p.z = z;
+    p.norm_w = norm_w;
+    p.norm_eps = d->norm_eps;
+
+    gdn::PrepArgs& a = p.prep;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+    a.conv_w = conv_w; a.conv_state_in = conv_state_in;
+    a.cu = cu_seqlens;
+    a.chunk_off = varlen ? reinterpret_cast<int32_t*>(ws + L.chunk_off) : nullptr;
+    a.Qf = ws + L.Qf; a.KTf = ws + L.KTf; a.Wf = ws + L.Wf; a.Pf = ws + L.Pf; a.Uf = ws + L.Uf;
+    a.gates = reinterpret_cast<float*>(ws + L.gates);
+    a.T = (int32_t)T; a.N = (int32_t)N; a.Hk = (int32_t)Hk; a.Hv = (int32_t)Hv;
+    a.use_l2 = (d->flags & GDN_FLAG_L2NORM_QK) ? 1 : 0;
+    a.scale = d->scale; a.l2_eps = d->l2_eps;
+
+    gdn::SweepArgs& s = p.sweep;
+    s.Qf = a.Qf; s.KTf = a.KTf; s.Wf = a.Wf; s.Pf = a.Pf; s.Uf = a.Uf; s.gates = a.gates;
+    s.initial_state = initial_state; s.final_state = final_state;
+    s.out = out; s.cu = cu_seqlens; s.chunk_off = a.chunk_off;
+    s.T = a.T; s.N = a.N; s.Hk = a.Hk; s.Hv = a.Hv;
+
+    gdn::ConvStateArgs& c = p.conv_state;
+    c.q = q; c.k = k; c.v = v; c.conv_state_in = conv_state_in; c.conv_state_out = conv_state_out;
+    c.cu = cu_seqlens; c.T = a.T; c.N = a.N; c.Hk = a.Hk; c.Hv = a.Hv;
+
+    gdn::StageRecorder rec;
+    rec.events = events;
+    rec.ids = stage_ids;
+    const hipError_t e = gdn::launch_prefill(p, stream, rec);
+    if (num_stages) *num_stages = rec.count;
+    return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gdn_status_string(gdn_status s) {
+    switch (s) {
+        case GDN_OK: return "GDN_OK";
+        case GDN_ERR_NULL_ARG: return "GDN_ERR_NULL_ARG: a required pointer is NULL";
+        case GDN_ERR_BAD_SHAPE: return "GDN_ERR_BAD_SHAPE: counts out of range or inconsistent";
+        case GDN_ERR_UNSUPPORTED: return "GDN_ERR_UNSUPPORTED: head dim, conv kernel or flag not supported";
+        case GDN_ERR_BAD_DTYPE: return "GDN_ERR_BAD_DTYPE: dtype not supported by this call";
+        case GDN_ERR_MISALIGNED: return "GDN_ERR_MISALIGNED: tensor not 16-byte / workspace not 256-byte aligned";
+        case GDN_ERR_WORKSPACE: return "GDN_ERR_WORKSPACE: workspace missing or too small";
+        case GDN_ERR_HIP: return "GDN_ERR_HIP: a HIP runtime call failed";
+        case GDN_ERR_ALIAS: return "GDN_ERR_ALIAS: an output overlaps an input";
+        case GDN_ERR_BAD_VALUE: return "GDN_ERR_BAD_VALUE: non-finite or negative scalar";
+    }
+    return "GDN: unknown status";
+}
+
+gdn_status gdn_prefill_workspace_size(const gdn_desc* d, size_t* bytes) {
+    if (bytes == nullptr) return GDN_ERR_NULL_ARG;
+    const gdn_status st = check_desc_common(d);
+    if (st != GDN_OK) return st;
+    // the varlen bound covers the single-sequence layout as well
+    *bytes = prefill_layout(d, true).total;
+    return GDN_OK;
+}
+
+gdn_status gdn_prefill(const gdn_desc* d, const void* q, const void* k, const void* v,
+                       const float* g, const float* beta, const void* z, const void* conv_w,
+                       const void* norm_w, const int32_t* cu_seqlens, const float* initial_state,
+                       const void* conv_state_in, void* out, float* final_state,
+                       void* conv_state_out, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
+    return prefill_impl(d, q, k, v, g, beta, z, conv_w, norm_w, cu_seqlens, initial_state,
+                        conv_state_in, out, final_state, conv_state_out, workspace, workspace_bytes,
+                        stream, nullptr, nullptr, nullptr);
+}
+
+gdn_status gdn_prefill_profiled(const gdn_desc* d, const void* q, const void* k, const void* v,
+                                const float* g, const float* beta, const void* z,
+                                const void* conv_w, const void* norm_w, const int32_t* cu_seqlens,
+                                const float* initial_state, const void* conv_state_in, void* out,
+                                float* final_state, void* conv_state_out, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream, hipEvent_t* events,
+                                int32_t* num_stages, int32_t* stage_ids) {
+    if (events == nullptr || num_stages == nullptr) return GDN_ERR_NULL_ARG;
+    return prefill_impl(d, q, k, v, g, beta, z, conv_w, norm_w, cu_seqlens, initial_state,
+                        conv_state_in, out, final_state, conv_state_out, workspace, workspace_bytes,
+                        stream, events, num_stages, stage_ids);
+}
+
+gdn_status gdn_decode(const gdn_desc* d, const void* q, const void* k, const void* v,
+                      const float* g, const float* beta, const void* z, const void* conv_w,
+                      const void* norm_w, void* state, void* conv_state,
+                      const int32_t* state_slots, int32_t num_state_slots, void* out,
+                      hipStream_t stream) {
+    gdn_status st = check_desc_common(d);
+    if (st != GDN_OK) return st;
+    if (d->total_tokens != d->num_seqs) return GDN_ERR_BAD_SHAPE;
+    if (!q || !k || !v || !g || !beta || !state || !out) return GDN_ERR_NULL_ARG;
+    if ((z == nullptr) != (norm_w == nullptr)) return GDN_ERR_NULL_ARG;
+    if (num_state_slots < 1) return GDN_ERR_BAD_SHAPE;
+    if (state_slots == nullptr && num_state_slots < d->num_seqs) return GDN_ERR_BAD_SHAPE;
+    const void* tensors[] = {q, k, v, g, beta, z, conv_w, norm_w, state, conv_state, state_slots, out};
+    for (const void* p : tensors)
+        if (p && !aligned16(p)) return GDN_ERR_MISALIGNED;
+    const int64_t N = d->num_seqs, Hk = d->num_k_heads, Hv = d->num_v_heads;
+    const size_t es = io_size(d->io_dtype);
+    const size_t ss = d->state_dtype == GDN_BF16 ? 2 : 4;
+    const Range rout(out, (size_t)N * Hv * gdn::kD * es);
+    const Range rstate(state, (size_t)num_state_slots * Hv * gdn::kD * gdn::kD * ss);
+    const Range rins[] = {Range(q, (size_t)N * Hk * gdn::kD * es), Range(k, (size_t)N * Hk * gdn::kD * es),
+                          Range(v, (size_t)N * Hv * gdn::kD * es), Range(z, z ? (size_t)N * Hv * gdn::kD * es : 0),
+                          rstate};
+    for (const Range& r : rins)
+        if (rout.overlaps(r)) return GDN_ERR_ALIAS;
+    if (conv_state) {
+        const Range rcs(conv_state, (size_t)num_state_slots * (gdn::kConvK - 1) *
+                                        (2 * Hk + Hv) * gdn::kD * es);
+        if (rcs.overlaps(rstate) || rcs.overlaps(rout)) return GDN_ERR_ALIAS;
+    }
+
+    gdn::DecodeArgs a{};
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.z = z; a.conv_w = conv_w;
+    a.norm_w = norm_w; a.state = state; a.conv_state = conv_state; a.slots = state_slots;
+    a.out = out;
+    a.N = (int32_t)N; a.Hk = (int32_t)Hk; a.Hv = (int32_t)Hv;
+    a.use_l2 = (d->flags & GDN_FLAG_L2NORM_QK) ? 1 : 0;
+    a.scale = d->scale; a.l2_eps = d->l2_eps; a.norm_eps = d->norm_eps;
+    const hipError_t e = gdn::launch_decode(a, d->io_dtype == GDN_BF16, d->state_dtype == GDN_BF16,
+                                            conv_w != nullptr, stream);
+    return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+}  // extern "C"

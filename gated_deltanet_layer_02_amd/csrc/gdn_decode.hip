@@ -1,0 +1,196 @@
+// gdn_decode.hip -- one new token per sequence against the cached recurrent
+// state and conv state (SGLang cookbook, Configuration Tips: the per-request
+// state cache, fp32 by default or bf16 via --mamba-ssm-dtype).
+//
+// One workgroup per (sequence, key head): it owns the conv-state channels of
+// that key head's q and k and of its value heads' v, so every conv-state
+// element has one reader and one writer.  Per value head the 128 x 128 state
+// is streamed through registers once: row i (a dv index, dk contiguous) needs
+// two dot products with the old row,
+//   d_k = S_i . k,  d_q = S_i . q,
+// after which  u_i = b (v_i - a d_k),  S_i <- a S_i + u_i k,
+//   o_i = S_i(new) . q = a d_q + u_i (k . q),
+// which is the delta rule S <- a S (I - b k k^T) + b v k^T, o = S q
+// (hyper.ai story on Qwen3-Next, Gated DeltaNet paragraph), read and written
+// once: the kernel is bound by HBM bandwidth.
+#include <hip/hip_runtime.h>
+
+#include "gdn_common.hpp"
+#include "gdn_internal.hpp"
+
+namespace gdn {
+
+// state element types
+__device__ __forceinline__ void load_row8(const float* p, float* o) { load8(p, o); }
+__device__ __forceinline__ void load_row8(const uint16_t* p, float* o) { load8(p, o); }
+__device__ __forceinline__ void store_row8(float* p, const float* x) { store8(p, x); }
+__device__ __forceinline__ void store_row8(uint16_t* p, const float* x) { store8(p, x); }
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+    return x;
+}
+__device__ __forceinline__ float sum16(float x) {
+    x += __shfl_xor(x, 1);
+    x += __shfl_xor(x, 2);
+    x += __shfl_xor(x, 4);
+    x += __shfl_xor(x, 8);
+    return x;
+}
+
+template <class IO, class ST, bool kConv>
+__global__ __launch_bounds__(256) void gdn_decode_kernel(DecodeArgs a) {
+    __shared__ float s_qk[2 * kD];   // conv'd q | k of this key head
+    __shared__ float s_v[kD];        // conv'd v of the current value head
+    __shared__ float s_zw[kD];       // norm_w * SiLU(z) of the current value head
+    __shared__ float s_o[kD];
+
+    const int tid = threadIdx.x;
+    const int n = blockIdx.x / a.Hk, hk = blockIdx.x % a.Hk;
+    const int group = a.Hv / a.Hk;
+    const int slot = a.slots ? a.slots[n] : n;
+    const int Cch = 2 * a.Hk * kD + a.Hv * kD;
+    const IO* q = static_cast<const IO*>(a.q);
+    const IO* k = static_cast<const IO*>(a.k);
+    const IO* v = static_cast<const IO*>(a.v);
+    const IO* z = static_cast<const IO*>(a.z);
+    const IO* conv_w = static_cast<const IO*>(a.conv_w);
+    const IO* norm_w = static_cast<const IO*>(a.norm_w);
+    IO* cs = static_cast<IO*>(a.conv_state);
+    IO* out = static_cast<IO*>(a.out);
+    ST* state = static_cast<ST*>(a.state);
+
+    // conv (kernel 4) + SiLU of one channel; shifts the raw token into the conv state
+    auto conv_channel = [&](int ch, float x) -> float {
+        float h[kConvK - 1];
+#pragma unroll
+        for (int j = 0; j < kConvK - 1; ++j)
+            h[j] = cs ? io_to_f32(cs[((size_t)slot * (kConvK - 1) + j) * Cch + ch]) : 0.f;
+        if (cs) {
+#pragma unroll
+            for (int j = 0; j < kConvK - 2; ++j)
+                cs[((size_t)slot * (kConvK - 1) + j) * Cch + ch] = f32_to_io<IO>(h[j + 1]);
+            cs[((size_t)slot * (kConvK - 1) + kConvK - 2) * Cch + ch] = f32_to_io<IO>(x);
+        }
+        if (!kConv) return x;
+        float acc = 0.f;
+#pragma unroll
+        for (int j = 0; j < kConvK - 1; ++j) acc = fmaf(io_to_f32(conv_w[(size_t)ch * kConvK + j]), h[j], acc);
+        acc = fmaf(io_to_f32(conv_w[(size_t)ch * kConvK + kConvK - 1]), x, acc);
+        return silu_f32(acc);
+    };
+
+    // q and k of key head hk
+    {
+        const int which = tid >> 7, i = tid & (kD - 1);
+        const int ch = which * a.Hk * kD + hk * kD + i;
+        const float x = io_to_f32((which ? k : q)[((size_t)n * a.Hk + hk) * kD + i]);
+        s_qk[tid] = conv_channel(ch, x);
+    }
+    __syncthreads();
+
+    // L2 normalisation factors and k.q (every wave computes them)
+    const int lane = tid & 63;
+    float rq = 1.f, rk = 1.f;
+    {
+        const float q0 = s_qk[lane], q1 = s_qk[64 + lane];
+        const float k0 = s_qk[kD + lane], k1 = s_qk[kD + 64 + lane];
+        const float qq = wave_sum(q0 * q0 + q1 * q1);
+        const float kk = wave_sum(k0 * k0 + k1 * k1);
+        if (a.use_l2) {
+            rq = rsqrt_f32(qq + a.l2_eps);
+            rk = rsqrt_f32(kk + a.l2_eps);
+        }
+    }
+    rq *= a.scale;
+    const int l16 = tid & 15, rbase = tid >> 4;   // 16 lanes per state row, 8 dk each
+    float kf[8], qf[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        kf[e] = s_qk[kD + 8 * l16 + e] * rk;
+        qf[e] = s_qk[8 * l16 + e] * rq;
+    }
+    float kq = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) kq = fmaf(kf[e], qf[e], kq);
+    kq = sum16(kq);
+
+#pragma unroll 1
+    for (int vh = 0; vh < group; ++vh) {
+        const int h = hk * group + vh;
+        if (tid < kD) {
+            const int ch = 2 * a.Hk * kD + h * kD + tid;
+            s_v[tid] = conv_channel(ch, io_to_f32(v[((size_t)n * a.Hv + h) * kD + tid]));
+        } else if (z != nullptr || norm_w != nullptr) {
+            const int i = tid - kD;
+            const float zz = z ? silu_f32(io_to_f32(z[((size_t)n * a.Hv + h) * kD + i])) : 1.f;
+            const float ww = norm_w ? io_to_f32(norm_w[i]) : 1.f;
+            s_zw[i] = zz * ww;
+        }
+        const float aa = exp_f32(a.g[(size_t)n * a.Hv + h]);
+        const float bb = a.beta[(size_t)n * a.Hv + h];
+
+        ST* srow = state + (((size_t)slot * a.Hv + h) * kD) * kD + 8 * l16;
+        float Sr[8][8];
+#pragma unroll
+        for (int p = 0; p < 8; ++p) load_row8(srow + (size_t)(rbase + 16 * p) * kD, Sr[p]);
+        __syncthreads();   // s_v, s_zw ready
+
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+            const int i = rbase + 16 * p;
+            float dk = 0.f, dq = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                dk = fmaf(Sr[p][e], kf[e], dk);
+                dq = fmaf(Sr[p][e], qf[e], dq);
+            }
+            dk = sum16(dk);
+            dq = sum16(dq);
+            const float u = bb * (s_v[i] - aa * dk);
+            float nr[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) nr[e] = fmaf(aa, Sr[p][e], u * kf[e]);
+            store_row8(srow + (size_t)i * kD, nr);
+            if (l16 == 0) s_o[i] = fmaf(aa, dq, u * kq);
+        }
+        __syncthreads();   // s_o ready
+
+        if (tid < 64) {
+            const float o0 = s_o[tid], o1 = s_o[64 + tid];
+            IO* dst = out + ((size_t)n * a.Hv + h) * kD;
+            if (z != nullptr || norm_w != nullptr) {
+                const float ms = wave_sum(o0 * o0 + o1 * o1) * (1.0f / kD);
+                const float r = rsqrt_f32(ms + a.norm_eps);
+                dst[tid] = f32_to_io<IO>(o0 * r * s_zw[tid]);
+                dst[64 + tid] = f32_to_io<IO>(o1 * r * s_zw[64 + tid]);
+            } else {
+                dst[tid] = f32_to_io<IO>(o0);
+                dst[64 + tid] = f32_to_io<IO>(o1);
+            }
+        }
+        __syncthreads();   // before the next head reuses s_v, s_zw, s_o
+    }
+}
+
+template <class IO, class ST>
+static hipError_t launch_typed(const DecodeArgs& a, bool conv, hipStream_t stream) {
+    const dim3 grid(a.N * a.Hk);
+    if (conv)
+        hipLaunchKernelGGL((gdn_decode_kernel<IO, ST, true>), grid, dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL((gdn_decode_kernel<IO, ST, false>), grid, dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeArgs& a, bool io_bf16, bool state_bf16, bool conv,
+                         hipStream_t stream) {
+    if (io_bf16)
+        return state_bf16 ? launch_typed<uint16_t, uint16_t>(a, conv, stream)
+                          : launch_typed<uint16_t, float>(a, conv, stream);
+    return state_bf16 ? launch_typed<float, uint16_t>(a, conv, stream)
+                      : launch_typed<float, float>(a, conv, stream);
+}
+
+}  // namespace gdn

@@ -1,0 +1,111 @@
+"""Device buffers for one layer call, allocated with torch and passed to
+libgdn.so through the binding.  Host arrays use the io conventions of the
+library: bf16 as uint16 bit patterns, fp32 as float32, indices as int32.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import numpy as np
+
+from . import binding as B
+
+
+def to_device(a: Optional[np.ndarray], device="cuda"):
+    import torch
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
+    if a.dtype in (np.float32, np.int32):
+        return torch.from_numpy(a).to(device)
+    raise TypeError(f"unsupported host dtype {a.dtype}")
+
+
+def to_host(t) -> np.ndarray:
+    """Device tensor -> numpy, bf16 as uint16 bit patterns."""
+    import torch
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def empty_like_io(shape, io_bf16: bool, device="cuda"):
+    import torch
+    return torch.empty(shape, dtype=torch.bfloat16 if io_bf16 else torch.float32, device=device)
+
+
+class PrefillCall:
+    """All device buffers of one gdn_prefill call built from host arrays."""
+
+    def __init__(self, x: dict, *, Hk: int, Hv: int, io_bf16: bool, l2norm: bool = True,
+                 scale: float = 1.0, l2_eps: float = 1e-6, norm_eps: float = 1e-6,
+                 want_final_state: bool = True, want_conv_state: bool = True,
+                 pass_cu: Optional[bool] = None, device="cuda"):
+        import torch
+        self.cu_host = np.asarray(x["cu_seqlens"], dtype=np.int32)
+        self.N = len(self.cu_host) - 1
+        self.T = int(self.cu_host[-1])
+        self.Hk, self.Hv, self.io_bf16 = Hk, Hv, io_bf16
+        d = device
+        self.q, self.k, self.v = (to_device(x[n], d) for n in ("q", "k", "v"))
+        self.g, self.beta = to_device(x["g"], d), to_device(x["beta"], d)
+        self.z, self.conv_w, self.norm_w = (to_device(x.get(n), d) for n in ("z", "conv_w", "norm_w"))
+        self.initial_state = to_device(x.get("state"), d)
+        self.conv_state_in = to_device(x.get("conv_state"), d)
+        if pass_cu is None:
+            pass_cu = self.N > 1
+        self.cu = to_device(self.cu_host, d) if pass_cu else None
+        self.desc = B.make_desc(self.N, self.T, Hk, Hv, B.GDN_BF16 if io_bf16 else B.GDN_F32,
+                                B.GDN_F32, scale, l2_eps, norm_eps, l2norm)
+        self.out = empty_like_io((max(self.T, 1), Hv, 128), io_bf16, d)
+        self.final_state = (torch.empty((self.N, Hv, 128, 128), dtype=torch.float32, device=d)
+                            if want_final_state else None)
+        Cch = 2 * Hk * 128 + Hv * 128
+        self.conv_state_out = (empty_like_io((self.N, 3, Cch), io_bf16, d)
+                               if want_conv_state else None)
+        nbytes = B.gdn_prefill_workspace_size(self.desc)
+        self.workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=d)
+
+    def kwargs(self):
+        return dict(z=self.z, conv_w=self.conv_w, norm_w=self.norm_w, cu_seqlens=self.cu,
+                    initial_state=self.initial_state, conv_state_in=self.conv_state_in,
+                    out=self.out, final_state=self.final_state,
+                    conv_state_out=self.conv_state_out, workspace=self.workspace)
+
+    def run(self, stream=None):
+        B.gdn_prefill(self.desc, self.q, self.k, self.v, self.g, self.beta, stream=stream,
+                      **self.kwargs())
+
+    def run_profiled(self, events, stream=None):
+        return B.gdn_prefill_profiled(self.desc, self.q, self.k, self.v, self.g, self.beta,
+                                      events=events, stream=stream, **self.kwargs())
+
+
+class DecodeCall:
+    """All device buffers of one gdn_decode call built from host arrays."""
+
+    def __init__(self, x: dict, *, Hk: int, Hv: int, io_bf16: bool, state_bf16: bool,
+                 l2norm: bool = True, scale: float = 1.0, l2_eps: float = 1e-6,
+                 norm_eps: float = 1e-6, slots: Optional[np.ndarray] = None,
+                 num_state_slots: Optional[int] = None, device="cuda"):
+        d = device
+        self.N = int(np.asarray(x["q"]).shape[0])
+        self.q, self.k, self.v = (to_device(x[n], d) for n in ("q", "k", "v"))
+        self.g, self.beta = to_device(x["g"], d), to_device(x["beta"], d)
+        self.z, self.conv_w, self.norm_w = (to_device(x.get(n), d) for n in ("z", "conv_w", "norm_w"))
+        self.state = to_device(x["state"], d)
+        self.conv_state = to_device(x.get("conv_state"), d)
+        self.slots = to_device(None if slots is None else np.asarray(slots, np.int32), d)
+        self.num_state_slots = num_state_slots if num_state_slots is not None else self.state.shape[0]
+        self.desc = B.make_desc(self.N, self.N, Hk, Hv, B.GDN_BF16 if io_bf16 else B.GDN_F32,
+                                B.GDN_BF16 if state_bf16 else B.GDN_F32, scale, l2_eps, norm_eps,
+                                l2norm)
+        self.out = empty_like_io((self.N, Hv, 128), io_bf16, d)
+
+    def run(self, stream=None):
+        B.gdn_decode(self.desc, self.q, self.k, self.v, self.g, self.beta, state=self.state,
+                     out=self.out, z=self.z, conv_w=self.conv_w, norm_w=self.norm_w,
+                     conv_state=self.conv_state, state_slots=self.slots,
+                     num_state_slots=self.num_state_slots, stream=stream)

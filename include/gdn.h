@@ -1,0 +1,183 @@
+/*
+ * gdn.h -- C ABI of the Gated DeltaNet layer library (libgdn.so) for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The layer (the linear-attention layer that makes up three of every four
+ * layers of Qwen3-Next; hyper.ai story on the Qwen3-Next Transformers merge,
+ * Gated DeltaNet paragraph) computes, per sequence n, value head h and key
+ * head hk = h / (Hv/Hk):
+ *   1. a causal depthwise conv over the last K = 4 raw tokens of every q, k, v
+ *      channel, then SiLU (same story: causal convolution; model-atlas page for
+ *      Qwen3-Coder-Next, raw config.json table: linear_conv_kernel_dim 4);
+ *   2. L2 normalisation of q and k per token and key head, then q *= scale;
+ *   3. the gated delta rule on a dv x dk state S per value head
+ *        S_t = a_t S_{t-1} (I - b_t k_t k_t^T) + b_t v_t k_t^T,  o_t = S_t q_t,
+ *      a_t = exp(g_t) the decay gate, b_t = beta_t the update-strength gate
+ *      (same story: beta gates the strength of the update; kv_mem is the
+ *      memory read at the new key);
+ *   4. the z-gated RMSNorm of o_t over dv (eps 1e-6: rms_norm_eps in the raw
+ *      config.json table; Zero-Centered RMSNorm in the story):
+ *        out_t = o_t / sqrt(mean(o_t^2) + norm_eps) * norm_w * SiLU(z_t).
+ * Head shapes are those of the same config table: 16 key heads, 32 value
+ * heads, key and value head dim 128.  Prefill uses the chunked form with
+ * chunk 64 (FLA_CHUNK_SIZE in the SGLang cookbook's Mamba Radix Cache tip);
+ * the recurrent state is fp32, optionally bf16 in decode (--mamba-ssm-dtype
+ * in the cookbook's Configuration Tips: bf16 saves cache, fp32 is the more
+ * accurate default).
+ *
+ * Conventions common to every entry point
+ *  - Pointers to tensors are DEVICE pointers owned by the caller.  The library
+ *    never allocates, frees or synchronises; scratch memory comes from the
+ *    caller's workspace.  It keeps no mutable global state: concurrent calls
+ *    on different streams are safe when their buffers do not overlap.
+ *  - Calls are asynchronous in the order of `stream`.  GDN_OK means the work
+ *    was enqueued.
+ *  - Every argument is validated on the host before anything is enqueued; on
+ *    an error nothing runs and no output is touched.  The library never reads
+ *    device memory from the host, so the contents of cu_seqlens and
+ *    state_slots are preconditions (below), not checked.
+ *  - Every tensor pointer must be 16-byte aligned; the workspace 256-byte
+ *    aligned.
+ *  - Layouts are row-major, last index contiguous.  Channel order of the conv
+ *    weights and conv states: q (Hk*dk) | k (Hk*dk) | v (Hv*dv).
+ *  - bf16 stores round to nearest even.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GDN_OK = 0,
+    GDN_ERR_NULL_ARG = 1,     /* a required pointer is NULL, or z / norm_w given alone */
+    GDN_ERR_BAD_SHAPE = 2,    /* counts out of range, Hv % Hk != 0, T_total != N in decode */
+    GDN_ERR_UNSUPPORTED = 3,  /* head dims other than 128, conv kernel other than 4, unknown flags */
+    GDN_ERR_BAD_DTYPE = 4,    /* unknown dtype, or a state dtype the call does not support */
+    GDN_ERR_MISALIGNED = 5,   /* a tensor not 16-byte aligned, or workspace not 256-byte aligned */
+    GDN_ERR_WORKSPACE = 6,    /* workspace NULL or smaller than gdn_prefill_workspace_size */
+    GDN_ERR_HIP = 7,          /* a HIP launch or event call failed */
+    GDN_ERR_ALIAS = 8,        /* an output overlaps an input in a way the call does not allow */
+    GDN_ERR_BAD_VALUE = 9     /* a non-finite scale or eps, or a negative eps */
+} gdn_status;
+
+typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+
+/* L2-normalise q and k (step 2).  Without it q and k enter the recurrence as
+ * they leave the conv (or as given, without conv); scale is still applied. */
+#define GDN_FLAG_L2NORM_QK 0x1u
+
+typedef struct {
+    int32_t num_seqs;       /* N >= 1 */
+    int64_t total_tokens;   /* prefill: T_total = cu_seqlens[N] >= 0, < 2^31;  decode: == N */
+    int32_t num_k_heads;    /* Hk >= 1 */
+    int32_t num_v_heads;    /* Hv >= 1, Hv % Hk == 0 */
+    int32_t head_k_dim;     /* dk: 128 */
+    int32_t head_v_dim;     /* dv: 128 */
+    int32_t conv_kernel;    /* K: 4 */
+    gdn_dtype io_dtype;     /* q, k, v, z, out, conv_w, norm_w, conv states */
+    gdn_dtype state_dtype;  /* recurrent state: prefill F32; decode F32 or BF16 */
+    float scale;            /* multiplies q after normalisation; 1.0 leaves q as is */
+    float l2_eps;           /* step 2: x / sqrt(sum x^2 + l2_eps) */
+    float norm_eps;         /* step 4 */
+    uint32_t flags;         /* GDN_FLAG_* */
+} gdn_desc;
+
+/* Human-readable name of a status code (static storage). */
+const char* gdn_status_string(gdn_status s);
+
+/* Bytes of device workspace gdn_prefill needs for descriptor d (a bound that
+ * depends on N and T_total only through total_tokens / 64 + N chunks). */
+gdn_status gdn_prefill_workspace_size(const gdn_desc* d, size_t* bytes);
+
+/* Number of kernels gdn_prefill_profiled brackets with events (see below). */
+#define GDN_PREFILL_MAX_STAGES 6
+
+/*
+ * Prefill: every token of N packed sequences.
+ *   q, k           [T_total, Hk, dk] io dtype, raw (before the conv)
+ *   v              [T_total, Hv, dv] io dtype, raw
+ *   g, beta        [T_total, Hv] fp32: g is the log-decay (a = exp(g)), beta is b
+ *   z              [T_total, Hv, dv] io dtype, gate input        } both NULL:
+ *   norm_w         [dv] io dtype, effective RMSNorm weight       } out = o
+ *   conv_w         [Cch, K] io dtype, Cch = 2*Hk*dk + Hv*dv; NULL: no conv
+ *   cu_seqlens     [N+1] int32 device; cu[0] = 0, non-decreasing, cu[N] =
+ *                  T_total (precondition).  NULL allowed only when N == 1.
+ *   initial_state  [N, Hv, dv, dk] fp32; NULL: zeros
+ *   conv_state_in  [N, K-1, Cch] io dtype, oldest token first; NULL: zeros
+ *   out            [T_total, Hv, dv] io dtype
+ *   final_state    [N, Hv, dv, dk] fp32 or NULL; may equal initial_state
+ *   conv_state_out [N, K-1, Cch] io dtype or NULL; may equal conv_state_in.
+ *                  Holds the K-1 most recent raw tokens of (conv_state_in,
+ *                  sequence tokens): a bit-exact copy of inputs.
+ *   workspace      gdn_prefill_workspace_size bytes, contents ignored.
+ * Zero-length sequences pass their states through.  Any other overlap
+ * between outputs and inputs is GDN_ERR_ALIAS (out against q, k, v, z) or
+ * undefined.
+ */
+gdn_status gdn_prefill(const gdn_desc* d,
+                       const void* q, const void* k, const void* v,
+                       const float* g, const float* beta,
+                       const void* z, const void* conv_w, const void* norm_w,
+                       const int32_t* cu_seqlens,
+                       const float* initial_state, const void* conv_state_in,
+                       void* out, float* final_state, void* conv_state_out,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * gdn_prefill with per-kernel timing: events[0..GDN_PREFILL_MAX_STAGES]
+ * (caller-created hipEvent_t) are recorded on `stream` before each kernel of
+ * the call and after the last one; *num_stages receives the number of kernels
+ * launched (s), so events[0..s] were recorded and stage i ran between
+ * events[i] and events[i+1].  stage_ids[i] (GDN_STAGE_*) names stage i.
+ */
+enum {
+    GDN_STAGE_CHUNK_TABLE = 0,   /* chunk offsets of the packed sequences */
+    GDN_STAGE_CHUNK_PREP = 1,    /* conv, SiLU, L2, gates, K K^T, UT transform: W, U~, P */
+    GDN_STAGE_STATE_SWEEP = 2,   /* sequential chunk sweep: U, O, state update */
+    GDN_STAGE_GATED_NORM = 3,    /* z-gated RMSNorm of the output */
+    GDN_STAGE_CONV_STATE = 4,    /* conv state out */
+    GDN_STAGE_STATE_COPY = 5     /* initial -> final state of empty problems */
+};
+gdn_status gdn_prefill_profiled(const gdn_desc* d,
+                                const void* q, const void* k, const void* v,
+                                const float* g, const float* beta,
+                                const void* z, const void* conv_w, const void* norm_w,
+                                const int32_t* cu_seqlens,
+                                const float* initial_state, const void* conv_state_in,
+                                void* out, float* final_state, void* conv_state_out,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                hipEvent_t* events, int32_t* num_stages, int32_t* stage_ids);
+
+/*
+ * Decode: one new token for each of N sequences against cached states.
+ *   q, k           [N, Hk, dk] io dtype, raw
+ *   v, z           [N, Hv, dv] io dtype (z NULL together with norm_w: out = o)
+ *   g, beta        [N, Hv] fp32
+ *   conv_w, norm_w as in gdn_prefill
+ *   state          [S, Hv, dv, dk] state dtype (F32 or BF16), updated in place
+ *   conv_state     [S, K-1, Cch] io dtype, updated in place (shifted by one
+ *                  token); NULL: zero history and nothing written
+ *   state_slots    [N] int32 device: row of state / conv_state used by
+ *                  sequence n; NULL: row n.  Precondition: distinct, in
+ *                  [0, S).  num_state_slots = S (>= N when state_slots is NULL).
+ *   out            [N, Hv, dv] io dtype
+ */
+gdn_status gdn_decode(const gdn_desc* d,
+                      const void* q, const void* k, const void* v,
+                      const float* g, const float* beta,
+                      const void* z, const void* conv_w, const void* norm_w,
+                      void* state, void* conv_state,
+                      const int32_t* state_slots, int32_t num_state_slots,
+                      void* out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GDN_H */

@@ -1,0 +1,154 @@
+"""The C ABI on the host: libgdn.so loads, exports exactly what include/gdn.h
+declares, and rejects bad arguments before enqueuing anything.  No GPU: every
+call below fails validation, which runs before any HIP call, so the fake
+device addresses are never dereferenced.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import gated_deltanet_layer_02_amd as gdn
+from gated_deltanet_layer_02_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return set(re.findall(r"^\s*(?:const\s+)?[a-z_]+\*?\s+\*?(gdn_[a-z_]+)\s*\(", src, flags=re.M))
+
+
+def test_library_exports_every_declared_symbol():
+    decl = declared_functions()
+    assert decl == set(B.EXPORTED), decl
+    nm = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
+                        text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s(gdn_\w+)", nm))
+    assert decl <= exported, decl - exported
+    lib = gdn.lib()
+    for name in decl:
+        assert getattr(lib, name) is not None
+
+
+def test_status_strings():
+    for code, name in B.STATUS_NAMES.items():
+        assert gdn.gdn_status_string(code).startswith(name)
+    assert "unknown" in gdn.gdn_status_string(99)
+
+
+def test_workspace_size_grows_with_tokens():
+    sizes = []
+    for T in (0, 1, 64, 65, 4096, 65536):
+        sizes.append(gdn.gdn_prefill_workspace_size(B.make_desc(1, T)))
+    assert sizes == sorted(sizes) and sizes[-1] > sizes[0]
+    # fp32 io doubles the fragment storage
+    s_bf = gdn.gdn_prefill_workspace_size(B.make_desc(1, 4096, io_dtype=B.GDN_BF16))
+    s_f = gdn.gdn_prefill_workspace_size(B.make_desc(1, 4096, io_dtype=B.GDN_F32))
+    assert s_f > 1.9 * s_bf
+
+
+FAKE = 1 << 40          # 256-byte aligned fake device address; never dereferenced
+STEP = 1 << 34          # distance between fake tensors (no overlaps)
+
+
+def _ptrs(n, base=FAKE):
+    return [base + i * STEP for i in range(n)]
+
+
+def _prefill_rc(desc, **over):
+    names = ["q", "k", "v", "g", "beta", "z", "conv_w", "norm_w", "cu", "S0", "cs_in", "out",
+             "S1", "cs_out"]
+    vals = dict(zip(names, _ptrs(len(names))))
+    ws, ws_bytes = FAKE + 20 * STEP, 1 << 33
+    vals.update({k: v for k, v in over.items() if k in vals})
+    ws = over.get("ws", ws)
+    ws_bytes = over.get("ws_bytes", ws_bytes)
+    lib = gdn.lib()
+    args = [vals[n] for n in names]
+    return lib.gdn_prefill(ctypes.byref(desc), *args, ws, ws_bytes, None)
+
+
+def test_prefill_validation_errors():
+    cases = [
+        (dict(num_seqs=0), {}, 2),
+        (dict(num_k_heads=3), {}, 2),                    # 32 % 3 != 0
+        (dict(total_tokens=-1), {}, 2),
+        (dict(head_k_dim=64), {}, 3),
+        (dict(head_v_dim=256), {}, 3),
+        (dict(conv_kernel=3), {}, 3),
+        (dict(flags=0x8), {}, 3),
+        (dict(io_dtype=5), {}, 4),
+        (dict(state_dtype=B.GDN_BF16), {}, 4),           # prefill state is fp32
+        (dict(scale=float("nan")), {}, 9),
+        (dict(l2_eps=-1.0), {}, 9),
+        ({}, dict(q=None), 1),
+        ({}, dict(beta=None), 1),
+        ({}, dict(out=None), 1),
+        ({}, dict(z=None), 1),                            # z without norm_w
+        ({}, dict(cu=None), 1),                           # N = 2 needs cu_seqlens
+        ({}, dict(q=FAKE + 8), 5),
+        ({}, dict(ws=FAKE + 20 * STEP + 16), 5),          # workspace 256-byte alignment
+        ({}, dict(ws_bytes=1024), 6),
+        ({}, dict(ws=None), 6),
+        ({}, dict(out=FAKE), 8),                          # out aliases q
+        ({}, dict(S1=FAKE + 11 * STEP), 8),               # final_state aliases out
+    ]
+    for dover, pover, want in cases:
+        dd = B.make_desc(2, 100)
+        for k, v in dover.items():
+            setattr(dd, k, v)
+        rc = _prefill_rc(dd, **pover)
+        assert rc == want, (dover, pover, rc, want)
+    # NULL descriptor
+    lib = gdn.lib()
+    assert lib.gdn_prefill(None, *([None] * 14), None, 0, None) == 1
+    # workspace-size query validates too
+    n = ctypes.c_size_t()
+    bad = B.make_desc(1, 10, head_dim=64)
+    assert lib.gdn_prefill_workspace_size(ctypes.byref(bad), ctypes.byref(n)) == 3
+    assert lib.gdn_prefill_workspace_size(ctypes.byref(B.make_desc(1, 10)), None) == 1
+
+
+def test_prefill_profiled_needs_events():
+    d = B.make_desc(1, 10)
+    lib = gdn.lib()
+    rc = lib.gdn_prefill_profiled(ctypes.byref(d), *_ptrs(14), FAKE + 20 * STEP, 1 << 33, None,
+                                  None, None, None)
+    assert rc == 1
+
+
+def _decode_rc(desc, num_slots=None, **over):
+    names = ["q", "k", "v", "g", "beta", "z", "conv_w", "norm_w", "state", "cs", "slots"]
+    vals = dict(zip(names, _ptrs(len(names))))
+    vals["slots"] = None
+    vals.update({k: v for k, v in over.items() if k in vals})
+    out = over.get("out", FAKE + 30 * STEP)
+    lib = gdn.lib()
+    ns = desc.num_seqs if num_slots is None else num_slots
+    return lib.gdn_decode(ctypes.byref(desc), *[vals[n] for n in names], ns, out, None)
+
+
+def test_decode_validation_errors():
+    cases = [
+        (dict(total_tokens=5), {}, None, 2),             # decode: T_total == N
+        (dict(head_k_dim=96), {}, None, 3),
+        (dict(state_dtype=7), {}, None, 4),
+        ({}, dict(state=None), None, 1),
+        ({}, dict(q=None), None, 1),
+        ({}, dict(norm_w=None), None, 1),
+        ({}, dict(v=FAKE + 4), None, 5),
+        ({}, {}, 3, 2),                                    # fewer slots than sequences
+        ({}, dict(out=FAKE + 8 * STEP), None, 8),         # out aliases the state
+        ({}, dict(cs=FAKE + 8 * STEP), None, 8),          # conv state aliases the state
+    ]
+    for dover, pover, ns, want in cases:
+        d = B.make_desc(4, 4, state_dtype=B.GDN_BF16)
+        for k, v in dover.items():
+            setattr(d, k, v)
+        rc = _decode_rc(d, ns, **pover)
+        assert rc == want, (dover, pover, rc, want)
