@@ -1,0 +1,311 @@
+#!/usr/bin/env python3
+"""Benchmark of the Gated DeltaNet layer on one MI355X.
+
+Headline: prefill tokens/s of the Qwen3-Next-shaped layer (T = 4096, 16 key /
+32 value heads, head dim 128, conv 4, gated RMSNorm, fp32 state), one step =
+one gdn_prefill call over the whole batch, inputs resident in HBM.  Also
+reported: per-kernel times (HIP events recorded on the launch stream), the
+roofline of the dominant kernel, decode state GB/s (256 sequences, fp32 and
+bf16 state) and the fp64 CPU oracle on a bounded sample as a baseline.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12          # B/s, MI355X HBM3E
+MFMA_BF16_PEAK = 2.5e15    # flop/s, dense bf16 MFMA
+D = 128
+CHUNK = 64
+
+# Algorithmic work per (token, value head), dense 64x64 tile count.
+FLOP_SWEEP = 6 * D * D + 2 * CHUNK * D           # W S^T, Q S^T, K^T U, P U
+FLOP_PREP = 2 * CHUNK * D + 2 * CHUNK * D + (2 * CHUNK * D + 2 * CHUNK * D) // 2  # W, U~, (KK^T, QK^T)/2
+FLOP_LAYER = 180224                               # whole chunked layer
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_SOURCES = ["gated_deltanet_layer_02_amd/csrc/gdn_prefill.hip",
+                  "gated_deltanet_layer_02_amd/csrc/gdn_common.hpp",
+                  "gated_deltanet_layer_02_amd/csrc/gdn_internal.hpp"]
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    cur = source_hash(KERNEL_SOURCES)
+    for line in open(path):
+        m = re.match(r"\|\s*(\w+)\s*\|\s*([0-9a-f]{16})\s*\|\s*([0-9.eE+]+)\s*\|\s*([0-9.eE+]+)\s*\|", line)
+        if m and m.group(1) == kernel and m.group(2) == cur:
+            return float(m.group(3)) + float(m.group(4))
+    return None
+
+
+class Hip:
+    """hipEvent API of the HIP runtime torch already loaded."""
+
+    def __init__(self):
+        self.l = ctypes.CDLL("libamdhip64.so.7")
+        self.l.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.l.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                               ctypes.c_void_p]
+        self.l.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.l.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        assert self.l.hipEventCreate(ctypes.byref(e)) == 0
+        return e.value
+
+    def record(self, e, stream):
+        assert self.l.hipEventRecord(e, stream) == 0
+
+    def ms(self, a, b):
+        f = ctypes.c_float()
+        assert self.l.hipEventElapsedTime(ctypes.byref(f), a, b) == 0
+        return f.value
+
+    def destroy(self, e):
+        self.l.hipEventDestroy(e)
+
+
+def clone_call(call):
+    """Same inputs in fresh buffers (another buffer set for rotation)."""
+    import copy
+    c = copy.copy(call)
+    for n in ("q", "k", "v", "g", "beta", "z", "conv_w", "norm_w", "initial_state",
+              "conv_state_in", "out", "final_state", "conv_state_out", "workspace", "cu"):
+        t = getattr(call, n)
+        setattr(c, n, None if t is None else t.clone())
+    return c
+
+
+def bench_prefill(args, hip):
+    import torch
+    import gdn_synth as gs
+    from gated_deltanet_layer_02_amd.binding import STAGE_NAMES
+    from gated_deltanet_layer_02_amd.tensors import PrefillCall
+
+    p = gs.configs()["C1"]
+    log(f"[bench] generating {p.name} inputs")
+    x = gs.generate(p)
+    base = PrefillCall(x, Hk=p.Hk, Hv=p.Hv, io_bf16=True)
+    sets = [base] + [clone_call(base) for _ in range(args.buffer_sets - 1)]
+    stream = torch.cuda.current_stream().cuda_stream
+    nev = 7
+    log(f"[bench] warmup {args.warmup} steps")
+    warm_ev = [hip.event() for _ in range(nev)]
+    for i in range(args.warmup):
+        sets[i % len(sets)].run_profiled(warm_ev, stream=stream)
+    torch.cuda.synchronize()
+
+    events = [[hip.event() for _ in range(nev)] for _ in range(args.steps)]
+    stage_ids = None
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        stage_ids = sets[i % len(sets)].run_profiled(events[i], stream=stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    ns = len(stage_ids)
+    stage_ms = {STAGE_NAMES[s]: 0.0 for s in stage_ids}
+    gpu_ms = 0.0
+    for ev in events:
+        for j, s in enumerate(stage_ids):
+            stage_ms[STAGE_NAMES[s]] += hip.ms(ev[j], ev[j + 1]) / args.steps
+        gpu_ms += hip.ms(ev[0], ev[ns]) / args.steps
+    for ev in events + [warm_ev]:
+        for e in ev:
+            hip.destroy(e)
+
+    T, Hv, Hk, N = p.T, p.Hv, p.Hk, p.N
+    io_bytes = (2 * T * Hk * D + 3 * T * Hv * D) * 2 + 2 * T * Hv * 4 \
+        + p.Cch * 4 * 2 + D * 2 + N * Hv * D * D * 4 + N * 3 * p.Cch * 2
+    dominant = max(stage_ms, key=stage_ms.get)
+    dom_s = stage_ms[dominant] * 1e-3
+    if dominant == "state_sweep":
+        achieved, peak, unit, bound = FLOP_SWEEP * T * Hv / dom_s, MFMA_BF16_PEAK, "TFLOP/s", "mfma"
+    elif dominant == "chunk_prep":
+        achieved, peak, unit, bound = FLOP_PREP * T * Hv / dom_s, MFMA_BF16_PEAK, "TFLOP/s", "mfma"
+    else:   # gated norm: reads o and z, writes out
+        achieved, peak, unit, bound = 3 * T * Hv * D * 2 / dom_s, HBM_PEAK, "GB/s", "hbm"
+    scale = 1e12 if unit == "TFLOP/s" else 1e9
+    traffic = measured_traffic(dominant)
+    roof = {"bound": bound, "achieved": round(achieved / scale, 2), "peak": peak / scale,
+            "unit": unit, "frac": round(achieved / peak, 4), "traffic": traffic,
+            "kernel": dominant, "kernel_us": round(stage_ms[dominant] * 1e3, 2)}
+    path = {"gpu_us_per_step": round(gpu_ms * 1e3, 2),
+            "hbm_algorithmic_bytes": io_bytes,
+            "hbm_frac": round(io_bytes / (gpu_ms * 1e-3) / HBM_PEAK, 4),
+            "mfma_frac_dense_tile": round(FLOP_LAYER * T * Hv / (gpu_ms * 1e-3) / MFMA_BF16_PEAK, 4)}
+    return dict(p=p, x=x, ms_per_step=ms_per_step, tokens_per_s=T / (ms_per_step * 1e-3),
+                stages_us={k: round(v * 1e3, 2) for k, v in stage_ms.items()},
+                roofline=roof, path=path, buffer_sets=len(sets))
+
+
+def bench_decode(args, hip, cfg):
+    import torch
+    import gdn_synth as gs
+    from gated_deltanet_layer_02_amd.tensors import DecodeCall
+
+    p = gs.configs()[cfg]
+    log(f"[bench] decode {p.name}")
+    x = gs.generate(p)
+    dc = DecodeCall(x, Hk=p.Hk, Hv=p.Hv, io_bf16=True, state_bf16=p.state_dtype == gs.BF16)
+    stream = torch.cuda.current_stream().cuda_stream
+    for _ in range(3):
+        dc.run(stream=stream)
+    torch.cuda.synchronize()
+    reps = max(5, args.steps)
+    evs = [hip.event() for _ in range(reps + 1)]
+    hip.record(evs[0], stream)
+    for i in range(reps):
+        dc.run(stream=stream)
+        hip.record(evs[i + 1], stream)
+    torch.cuda.synchronize()
+    times = sorted(hip.ms(evs[i], evs[i + 1]) for i in range(reps))
+    for e in evs:
+        hip.destroy(e)
+    t = times[len(times) // 2] * 1e-3
+    sb = 2 if p.state_dtype == gs.BF16 else 4
+    state_bytes = 2 * p.N * p.Hv * D * D * sb
+    other = (2 * p.N * p.Hk * D + 3 * p.N * p.Hv * D) * 2 + 2 * p.N * p.Hv * 4 \
+        + 2 * p.N * 3 * p.Cch * 2 + p.Cch * 4 * 2
+    return {"state_dtype": p.state_dtype, "us": round(t * 1e6, 2),
+            "state_GBps": round(state_bytes / t / 1e9, 1),
+            "total_GBps": round((state_bytes + other) / t / 1e9, 1),
+            "tokens_per_s": round(p.N / t, 1),
+            "roofline": {"bound": "hbm", "achieved": round((state_bytes + other) / t / 1e9, 1),
+                         "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                         "frac": round((state_bytes + other) / t / HBM_PEAK, 4), "traffic": None}}
+
+
+def cpu_baseline(pres, target_s: float):
+    """The fp64 oracle on the first S tokens of the same C1 inputs, all heads."""
+    import numpy as np
+    from oracle import oracle
+    p, x = pres["p"], pres["x"]
+
+    def run(S):
+        xs = {n: (a[:S] if n in ("q", "k", "v", "z", "g", "beta") else a) for n, a in x.items()}
+        xs["cu_seqlens"] = np.array([0, S], dtype=np.int32)
+        t0 = time.perf_counter()
+        oracle.run_problem(p, xs)
+        return time.perf_counter() - t0
+
+    S = 64
+    t = run(S)
+    S = int(min(p.T, max(64, S * target_s / max(t, 1e-3))))
+    log(f"[bench] cpu baseline: oracle on {S} tokens x {p.Hv} heads")
+    t = run(S)
+    threads = min(oracle.max_threads(), p.N * p.Hv)
+    cpu = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": round(S / t, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {S} of {p.T} tokens of the same workload, all {p.Hv} value heads, "
+                      f"fp64, OpenMP over heads; {t:.1f} s wall",
+            "host_cpu": cpu, "host_logical_cpus": os.cpu_count()}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--buffer-sets", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run a 512 MiB device-to-device copy first (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    hip = Hip()
+
+    if args.calibrate_copy:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] calibration copy: 3 x 512 MiB device-to-device")
+        del src, dst
+
+    pres = bench_prefill(args, hip)
+    dec = None
+    if not args.no_decode:
+        dec = {"metric": "decode state GB/s", "fp32_state": bench_decode(args, hip, "C4"),
+               "bf16_state": bench_decode(args, hip, "C4b")}
+    cpu = None if args.no_cpu_baseline else cpu_baseline(pres, args.cpu_seconds)
+
+    p = pres["p"]
+    line = {
+        "metric": "GatedDeltaNet prefill tokens/s (T=4096, 16k/32v heads)",
+        "value": round(pres["tokens_per_s"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(pres["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "prefill, 1 sequence of 4096 tokens, 16 key / 32 value heads, "
+                               "head dim 128, conv 4 + SiLU, L2 q/k, z-gated RMSNorm, fp32 state",
+                   "T": p.T, "num_seqs": p.N, "Hk": p.Hk, "Hv": p.Hv, "chunk": CHUNK,
+                   "io": "bf16", "state": "fp32", "buffer_sets": pres["buffer_sets"]},
+        "roofline": pres["roofline"],
+        "cpu_baseline": cpu,
+        "stages_us": pres["stages_us"],
+        "path": pres["path"],
+        "decode": dec,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

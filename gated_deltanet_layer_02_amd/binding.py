@@ -18,7 +18,7 @@ GDN_F32, GDN_BF16 = 0, 1
 GDN_FLAG_L2NORM_QK = 0x1
 GDN_PREFILL_MAX_STAGES = 6
 STAGE_NAMES = {0: "chunk_table", 1: "chunk_prep", 2: "state_sweep", 3: "gated_norm",
-               4: "conv_state", 5: "state_copy"}
+               4: "conv_state"}
 
 STATUS_NAMES = {0: "GDN_OK", 1: "GDN_ERR_NULL_ARG", 2: "GDN_ERR_BAD_SHAPE",
                 3: "GDN_ERR_UNSUPPORTED", 4: "GDN_ERR_BAD_DTYPE", 5: "GDN_ERR_MISALIGNED",

@@ -60,12 +60,8 @@ PrefillLayout prefill_layout(const gdn_desc* d, bool varlen) {
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t at = off; off = round_up(off + bytes, 256); return at; };
     L.chunk_off = take(sizeof(int32_t) * ((size_t)d->num_seqs + 1));
-    L.Qf = take(C * Hk * 16 * frag);
-    L.KTf = take(C * Hk * 16 * frag);
-    L.Wf = take(C * Hv * 16 * frag);
-    L.Pf = take(C * Hv * 8 * frag);
-    L.Uf = take(C * Hv * 8 * 4 * 64 * 4 * mt);
-    L.gates = take(C * Hv * 128 * sizeof(float));
+    L.KB = take(C * Hk * gdn::kKBUnits * frag);
+    L.VB = take(C * Hv * gdn::kVBUnits * frag);
     L.total = off;
     return L;
 }
@@ -83,7 +79,7 @@ gdn_status prefill_impl(const gdn_desc* d, const void* q, const void* k, const v
     const int64_t T = d->total_tokens;
     const int64_t N = d->num_seqs, Hk = d->num_k_heads, Hv = d->num_v_heads;
     if (T > 0 && (!q || !k || !v || !g || !beta || !out)) return GDN_ERR_NULL_ARG;
-    if ((z == nullptr) != (norm_w == nullptr)) return GDN_ERR_NULL_ARG;
+    if (T > 0 && (z == nullptr) != (norm_w == nullptr)) return GDN_ERR_NULL_ARG;
     if (cu_seqlens == nullptr && N != 1) return GDN_ERR_NULL_ARG;
     if (workspace == nullptr && workspace_bytes > 0) return GDN_ERR_WORKSPACE;
     if (events != nullptr && num_stages == nullptr) return GDN_ERR_NULL_ARG;
@@ -116,7 +112,7 @@ gdn_status prefill_impl(const gdn_desc* d, const void* q, const void* k, const v
     gdn::PrefillPlan p{};
     p.io_bf16 = d->io_dtype == GDN_BF16;
     p.conv = conv_w != nullptr;
-    p.gated = z != nullptr;
+    p.gated = z != nullptr && norm_w != nullptr;
     p.total_tokens = T;
     p.chunk_slots = (int32_t)(T > 0 ? chunk_slots(d, varlen) : 0);
     p.z = z;
@@ -128,14 +124,13 @@ gdn_status prefill_impl(const gdn_desc* d, const void* q, const void* k, const v
     a.conv_w = conv_w; a.conv_state_in = conv_state_in;
     a.cu = cu_seqlens;
     a.chunk_off = varlen ? reinterpret_cast<int32_t*>(ws + L.chunk_off) : nullptr;
-    a.Qf = ws + L.Qf; a.KTf = ws + L.KTf; a.Wf = ws + L.Wf; a.Pf = ws + L.Pf; a.Uf = ws + L.Uf;
-    a.gates = reinterpret_cast<float*>(ws + L.gates);
+    a.KB = ws + L.KB; a.VB = ws + L.VB;
     a.T = (int32_t)T; a.N = (int32_t)N; a.Hk = (int32_t)Hk; a.Hv = (int32_t)Hv;
     a.use_l2 = (d->flags & GDN_FLAG_L2NORM_QK) ? 1 : 0;
     a.scale = d->scale; a.l2_eps = d->l2_eps;
 
     gdn::SweepArgs& s = p.sweep;
-    s.Qf = a.Qf; s.KTf = a.KTf; s.Wf = a.Wf; s.Pf = a.Pf; s.Uf = a.Uf; s.gates = a.gates;
+    s.KB = a.KB; s.VB = a.VB;
     s.initial_state = initial_state; s.final_state = final_state;
     s.out = out; s.cu = cu_seqlens; s.chunk_off = a.chunk_off;
     s.T = a.T; s.N = a.N; s.Hk = a.Hk; s.Hv = a.Hv;

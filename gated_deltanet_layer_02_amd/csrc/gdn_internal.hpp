@@ -13,27 +13,36 @@ constexpr int kChunk = 64;   // tokens per chunk of the chunked prefill
 constexpr int kD = 128;      // key and value head dim
 constexpr int kConvK = 4;    // conv kernel width
 
-// Chunk-local results of gdn_chunk_prep_kernel, read by the sweep.  Every
-// tensor holds MFMA operand fragments (8 slots per lane, 64 lanes):
-//   Qf  [chunk][Hk][16 = 4 token tiles x 4 dk blocks][64]      A operand of Q S^T
-//   KTf [chunk][Hk][16 = 8 dk tiles x 2 token blocks][64]      A operand of K^T U
-//   Wf  [chunk][Hv][16 = 4 token tiles x 4 dk blocks][64]      A operand of W S^T
-//   Pf  [chunk][Hv][8 = 4 token tiles x 2 token blocks][64]    A operand of P U
-//   Uf  [chunk][Hv][8 dv tiles][4 token tiles][64][4]          U~ in accumulator layout
-//   gates [chunk][Hv][2][64] fp32: exp(G_t), exp(G_n - G_t)
+// Chunk-local results of gdn_chunk_prep_kernel, read by the sweep, stored as
+// MFMA operand fragments: a unit is one fragment of a wave, 64 lanes x 8
+// slots (1 KB for bf16, 2 KB for fp32), so each tensor moves as whole units
+// of 16 B (or 32 B) per lane.
+//   KB [chunk][Hk][32 units]: 0..15  Q    A operand of Q S^T   (token tile mt, dk block p: 4 mt + p)
+//                             16..31 K^T  A operand of K^T U   (dk tile m, token block p: 2 m + p)
+//   VB [chunk][Hv][40 units]: 0..15  W    A operand of W S^T   (4 mt + p)
+//                             16..21 P    A operand of P U, lower blocks (pfrag_index)
+//                             22     gates fp32: exp(G_t) at 0..63, exp(G_n - G_t) at 64..127
+//                             23     unused
+//                             24..39 U~   accumulator layout: dv tile s, token-tile pair pr -> 24 + 2 s + pr
+// One chunk of one head is therefore three contiguous unit ranges.
+constexpr int kKBUnits = 32, kKB_Q = 0, kKB_KT = 16;
+constexpr int kVBUnits = 40, kVB_W = 0, kVB_P = 16, kVB_G = 22, kVB_U = 24;
+constexpr int kPFrags = 6;
+// (token tile mt, token block p) of the lower-triangular P blocks, p <= mt / 2
+__host__ __device__ constexpr int pfrag_index(int mt, int p) { return mt < 2 ? mt : 2 + 2 * (mt - 2) + p; }
+
 struct PrepArgs {
     const void* q; const void* k; const void* v;
     const float* g; const float* beta;
     const void* conv_w; const void* conv_state_in;
     const int32_t* cu; int32_t* chunk_off;
-    void* Qf; void* KTf; void* Wf; void* Pf; void* Uf; float* gates;
+    void* KB; void* VB;
     int32_t T, N, Hk, Hv, use_l2;
     float scale, l2_eps;
 };
 
 struct SweepArgs {
-    const void* Qf; const void* KTf; const void* Wf; const void* Pf; const void* Uf;
-    const float* gates;
+    const void* KB; const void* VB;
     const float* initial_state; float* final_state;
     void* out;
     const int32_t* cu; const int32_t* chunk_off;
@@ -59,7 +68,7 @@ struct PrefillPlan {
 
 // Workspace carve-up of one prefill call.
 struct PrefillLayout {
-    size_t chunk_off, Qf, KTf, Wf, Pf, Uf, gates, total;
+    size_t chunk_off, KB, VB, total;
 };
 
 struct DecodeArgs {

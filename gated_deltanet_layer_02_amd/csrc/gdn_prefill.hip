@@ -13,17 +13,17 @@
 //   S <- gamma_n S + U^T diag(exp(G_n - G)) K
 // Everything except the U / O / S lines is independent of S and runs fully in
 // parallel over (chunk, key head) in gdn_chunk_prep_kernel; the S lines run in
-// gdn_state_sweep_kernel, one wave per (sequence, value head, 16-row slice of
-// the dv rows): rows of S never mix in the delta rule, so the slices are
-// independent and the fp32 state never leaves the wave's registers.
+// the state sweep, one wave per (sequence, value head, 16-row slice of the dv
+// rows): rows of S never mix in the delta rule, so the slices are independent
+// and the fp32 state never leaves the wave's registers.
 //
 // Kernels, in stream order:
-//   gdn_chunk_table_kernel   chunk offsets of packed sequences (varlen only)
-//   gdn_chunk_prep_kernel    conv + SiLU + L2 + scale; gates; K K^T, Q K^T;
-//                            T = (I + A)^-1; W, U~, P; MFMA operand fragments
-//   gdn_state_sweep_kernel   sequential chunk sweep; writes O and final states
-//   gdn_gated_norm_kernel    z-gated RMSNorm of O, in place (when gated)
-//   gdn_conv_state_kernel    conv state out (when requested)
+//   gdn_chunk_table_kernel      chunk offsets of packed sequences (varlen only)
+//   gdn_chunk_prep_kernel       conv + SiLU + L2 + scale; gates; K K^T, Q K^T;
+//                               T = (I + A)^-1; W, U~, P as MFMA fragments
+//   gdn_state_sweep_*_kernel    sequential chunk sweep; writes O, final states
+//   gdn_gated_norm_kernel       z-gated RMSNorm of O, in place (when gated)
+//   gdn_conv_state_kernel       conv state out (when requested)
 #include <hip/hip_runtime.h>
 
 #include "gdn_common.hpp"
@@ -86,17 +86,28 @@ __device__ __forceinline__ bool locate_chunk(const PrepArgs& a, int c, int& n, i
 // ===========================================================================
 // chunk prep
 // ===========================================================================
+// LDS of one workgroup.  Rows are padded so that the fragment reads (16
+// lanes on 16 rows, same column) spread over the banks.  The q / k row tiles
+// are only needed until K K^T and K Q^T are formed; their space is then
+// reused for A and T (fp32).
 template <class MT>
 struct PrepSmem {
-    static constexpr int kPad = sizeof(MT) == 2 ? 8 : 4;
-    MT q[kChunk][kD + kPad];     // normalised, scaled q rows
-    MT k[kChunk][kD + kPad];     // normalised k rows
-    MT kt[kD][kChunk + kPad];    // the same k, transposed (token contiguous)
-    MT vt[kD][kChunk + kPad];    // conv'd v of one value head, transposed
-    float a[kChunk][kChunk];     // A, then T = (I + A)^-1
-    float G[kChunk];             // inclusive cumsum of g
-    float b[kChunk];             // beta
-    float bg[kChunk];            // beta * exp(G)
+    static constexpr int kRowPad = sizeof(MT) == 2 ? 16 : 8;   // elements
+    static constexpr int kColPad = sizeof(MT) == 2 ? 4 : 4;
+    static constexpr int kLdA = kChunk + 4;                    // fp32 row stride of A, T
+    union QA {
+        MT q[kChunk][kD + kRowPad];        // normalised, scaled q rows
+        float t[kChunk][kLdA];             // T = (I + A)^-1
+    } qa;
+    union KA {
+        MT k[kChunk][kD + kRowPad];        // normalised k rows
+        float a[kChunk][kLdA];             // A
+    } ka;
+    MT kt[kD][kChunk + kColPad];           // normalised k, transposed (token contiguous)
+    MT vt[kD][kChunk + kColPad];           // conv'd v of one value head, transposed
+    float G[kChunk];                       // inclusive cumsum of g
+    float b[kChunk];                       // beta
+    float bg[kChunk];                      // beta * exp(G)
 };
 
 __device__ __forceinline__ float reduce16(float x) {
@@ -107,61 +118,95 @@ __device__ __forceinline__ float reduce16(float x) {
     return x;
 }
 
-// conv (kernel 4) + SiLU of 8 consecutive channels of one token, or the raw
-// value without conv.  src points at [T][heads][128]; col = head*128 + 8*cg.
+// Raw rows of 8 channels for 4 consecutive tokens and the 3 before them.
+// src is [T][heads][128]; col = head * 128 + 8 cg; chan = the conv channel
+// of the first of the 8 columns.  Rows before the sequence start come from
+// the conv state (or are zero); rows past the chunk's last valid token are
+// not read.
 template <class IO, bool kConv>
-__device__ __forceinline__ void conv8(const IO* __restrict__ src, int heads, int col, int chan,
-                                      int tt, int seq_start, int n, int Cch,
-                                      const IO* __restrict__ conv_w, const IO* __restrict__ csin,
-                                      float* y) {
-    if (!kConv) {
-        load8(src + (size_t)tt * heads * kD + col, y);
-        return;
-    }
-    float w[4][8];   // w[r][e]: tap r of channel chan + e
-    {
-        float raw[32];
+struct Quad {
+    float x[7][8];    // x[i]: local token tq - 3 + i
+    float w[4][8];    // w[r][e]: tap r of channel chan + e
+    __device__ __forceinline__ void load(const IO* __restrict__ src, int heads, int col, int chan,
+                                         int t0, int tq, int len, int seq_start, int n, int Cch,
+                                         const IO* __restrict__ conv_w,
+                                         const IO* __restrict__ csin) {
+        const int first = kConv ? 0 : 3;
 #pragma unroll
-        for (int h4 = 0; h4 < 4; ++h4) load8(conv_w + (size_t)chan * kConvK + 8 * h4, raw + 8 * h4);
+        for (int i = first; i < 7; ++i) {
+            const int lt = tq - 3 + i;           // local token
+            const int ts = t0 + lt;              // absolute token
+            if (lt < len && ts >= seq_start) {
+                load8(src + (size_t)ts * heads * kD + col, x[i]);
+            } else if (lt < len && csin != nullptr) {
+                load8(csin + ((size_t)n * (kConvK - 1) + (kConvK - 1 + ts - seq_start)) * Cch + chan, x[i]);
+            } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) w[r][e] = raw[e * 4 + r];
-    }
-    float acc[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-#pragma unroll
-    for (int r = 0; r < kConvK; ++r) {
-        const int ts = tt - (kConvK - 1) + r;
-        float x[8];
-        if (ts >= seq_start) {
-            load8(src + (size_t)ts * heads * kD + col, x);
-        } else if (csin != nullptr) {
-            load8(csin + ((size_t)n * (kConvK - 1) + (kConvK - 1 + ts - seq_start)) * Cch + chan, x);
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = 0.f;
+                for (int e = 0; e < 8; ++e) x[i][e] = 0.f;
+            }
         }
+        if (kConv) {
+            float raw[32];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = fmaf(w[r][e], x[e], acc[e]);
+            for (int h4 = 0; h4 < 4; ++h4) load8(conv_w + (size_t)chan * kConvK + 8 * h4, raw + 8 * h4);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) w[r][e] = raw[e * 4 + r];
+        }
     }
+    // conv + SiLU of token tq + tt (or the raw token without conv)
+    __device__ __forceinline__ void out(int tt, float* y) const {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) y[e] = silu_f32(acc[e]);
+        for (int e = 0; e < 8; ++e) {
+            if (kConv) {
+                float acc = 0.f;
+#pragma unroll
+                for (int r = 0; r < kConvK; ++r) acc = fmaf(w[r][e], x[tt + r][e], acc);
+                y[e] = silu_f32(acc);
+            } else {
+                y[e] = x[tt + 3][e];
+            }
+        }
+    }
+};
+
+// acc = X(16x16, LDS rows ldx) * Y(16x16, LDS rows ldy) in fp32 MFMA, K split
+// as k = 4 g + s over the four 16x16x4 instructions s.
+__device__ __forceinline__ f32x4 mm16_lds(const float* X, int ldx, const float* Y, int ldy,
+                                          f32x4 acc, int l16, int g4) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(X + l16 * ldx + 4 * g4);
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], Y[(4 * g4 + s) * ldy + l16], acc, 0, 0, 0);
+    return acc;
+}
+// acc = X(16x16, LDS) * E, E an accumulator tile (lane (n, g) holds rows 4 g + s)
+__device__ __forceinline__ f32x4 mm16_acc(const float* X, int ldx, const f32x4& E, int l16, int g4) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(X + l16 * ldx + 4 * g4);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], E[s], acc, 0, 0, 0);
+    return acc;
 }
 
 template <class IO, bool kConv>
-__global__ __launch_bounds__(256) void gdn_chunk_prep_kernel(PrepArgs a) {
+__global__ __launch_bounds__(256, 2) void gdn_chunk_prep_kernel(PrepArgs a) {
     typedef typename MathOf<IO>::T MT;
+    typedef Frag<MT> F;
+    typedef PrepSmem<MT> Smem;
     extern __shared__ __attribute__((aligned(16))) unsigned char gdn_prep_smem[];
-    PrepSmem<MT>& sm = *reinterpret_cast<PrepSmem<MT>*>(gdn_prep_smem);
+    Smem& sm = *reinterpret_cast<Smem*>(gdn_prep_smem);
+    constexpr int LD = Smem::kLdA;
 
     const int c = blockIdx.x, hk = blockIdx.y;
     int n, t0, len, seq_start;
     if (!locate_chunk(a, c, n, t0, len, seq_start)) return;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, g4 = lane >> 4;
+    const int cg = tid & 15, tq = 4 * (tid >> 4);     // 8 channels, 4 tokens per thread
     const int Hk = a.Hk, Hv = a.Hv, group = Hv / Hk;
     const int Cch = 2 * Hk * kD + Hv * kD;
     const IO* q = static_cast<const IO*>(a.q);
@@ -171,69 +216,66 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep_kernel(PrepArgs a) {
     const IO* csin = static_cast<const IO*>(a.conv_state_in);
 
     // ---- 1. q and k: conv + SiLU, L2 normalisation, scale ----
-#pragma unroll 1
-    for (int it = 0; it < 8; ++it) {
-        const int item = it * 256 + tid;
-        const int which = item >> 10;          // 0: q, 1: k
-        const int t = (item >> 4) & 63;
-        const int cg = item & 15;
-        float y[8];
-        if (t < len) {
-            conv8<IO, kConv>(which ? k : q, Hk, hk * kD + 8 * cg, which * Hk * kD + hk * kD + 8 * cg,
-                             t0 + t, seq_start, n, Cch, conv_w, csin, y);
+    {
+        Quad<IO, kConv> xq, xk;
+        xq.load(q, Hk, hk * kD + 8 * cg, hk * kD + 8 * cg, t0, tq, len, seq_start, n, Cch, conv_w, csin);
+        xk.load(k, Hk, hk * kD + 8 * cg, Hk * kD + hk * kD + 8 * cg, t0, tq, len, seq_start, n, Cch,
+                conv_w, csin);
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            const int t = tq + tt;
+            float yq[8], yk[8];
+            xq.out(tt, yq);
+            xk.out(tt, yk);
             if (a.use_l2) {
-                float ss = 0.f;
+                float sq = 0.f, sk = 0.f;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) ss = fmaf(y[e], y[e], ss);
-                ss = reduce16(ss);
-                const float r = rsqrt_f32(ss + a.l2_eps);
+                for (int e = 0; e < 8; ++e) {
+                    sq = fmaf(yq[e], yq[e], sq);
+                    sk = fmaf(yk[e], yk[e], sk);
+                }
+                sq = reduce16(sq);
+                sk = reduce16(sk);
+                const float rq = rsqrt_f32(sq + a.l2_eps), rk = rsqrt_f32(sk + a.l2_eps);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) y[e] *= r;
+                for (int e = 0; e < 8; ++e) {
+                    yq[e] *= rq;
+                    yk[e] *= rk;
+                }
             }
-            if (which == 0) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) y[e] *= a.scale;
-            }
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) y[e] = 0.f;
-        }
-        if (which == 0) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) sm.q[t][8 * cg + e] = static_cast<MT>(y[e]);
-        } else {
+            const bool valid = t < len;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                sm.k[t][8 * cg + e] = static_cast<MT>(y[e]);
-                sm.kt[8 * cg + e][t] = static_cast<MT>(y[e]);
+                yq[e] = valid ? yq[e] * a.scale : 0.f;
+                yk[e] = valid ? yk[e] : 0.f;
+                sm.qa.q[t][8 * cg + e] = static_cast<MT>(yq[e]);
+                sm.ka.k[t][8 * cg + e] = static_cast<MT>(yk[e]);
+                sm.kt[8 * cg + e][t] = static_cast<MT>(yk[e]);
             }
         }
     }
     __syncthreads();
 
-    // ---- 2. Q and K^T operand fragments for the sweep; K K^T and K Q^T ----
-    typedef Frag<MT> F;
-    F* Qf = static_cast<F*>(a.Qf) + ((size_t)c * Hk + hk) * 16 * 64;
-    F* KTf = static_cast<F*>(a.KTf) + ((size_t)c * Hk + hk) * 16 * 64;
+    // ---- 2. Q and K^T fragments for the sweep; K K^T and K Q^T ----
+    F* KB = static_cast<F*>(a.KB) + ((size_t)c * Hk + hk) * kKBUnits * 64 + lane;
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
         const int fi = wave * 4 + f;
-        {   // Q: A operand, rows = tokens (tile fi/4), K = dk block fi%4
+        {   // Q: rows = tokens (tile fi / 4), K = dk block fi % 4
             const int row = 16 * (fi >> 2) + l16, kb = 32 * (fi & 3);
             F fr;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) fr.v[j] = sm.q[row][kb + kidx(g4, j)];
-            frag_store(Qf + fi * 64 + lane, fr);
+            for (int j = 0; j < 8; ++j) fr.v[j] = sm.qa.q[row][kb + kidx(g4, j)];
+            frag_store(KB + (kKB_Q + fi) * 64, fr);
         }
-        {   // K^T: A operand, rows = dk (tile fi/2), K = token block fi%2
+        {   // K^T: rows = dk (tile fi / 2), K = token block fi % 2
             const int row = 16 * (fi >> 1) + l16, kb = 32 * (fi & 1);
             F fr;
 #pragma unroll
             for (int j = 0; j < 8; ++j) fr.v[j] = sm.kt[row][kb + kidx(g4, j)];
-            frag_store(KTf + fi * 64 + lane, fr);
+            frag_store(KB + (kKB_KT + fi) * 64, fr);
         }
     }
-
     f32x4 KK[4], KQ[4];
     {
         F kf[4][4], qf[4];
@@ -242,81 +284,85 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep_kernel(PrepArgs a) {
 #pragma unroll
             for (int p = 0; p < 4; ++p)
 #pragma unroll
-                for (int j = 0; j < 8; ++j) kf[ti][p].v[j] = sm.k[16 * ti + l16][32 * p + kidx(g4, j)];
+                for (int j = 0; j < 8; ++j) kf[ti][p].v[j] = sm.ka.k[16 * ti + l16][32 * p + kidx(g4, j)];
 #pragma unroll
         for (int p = 0; p < 4; ++p)
 #pragma unroll
-            for (int j = 0; j < 8; ++j) qf[p].v[j] = sm.q[16 * wave + l16][32 * p + kidx(g4, j)];
+            for (int j = 0; j < 8; ++j) qf[p].v[j] = sm.qa.q[16 * wave + l16][32 * p + kidx(g4, j)];
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti) {
             KK[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
             KQ[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
-                mma(KK[ti], kf[wave][p], kf[ti][p]);   // rows t (tile wave), cols i (tile ti)
-                mma(KQ[ti], kf[ti][p], qf[p]);         // rows i (tile ti), cols t (tile wave)
+                F kw;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) kw.v[j] = sm.ka.k[16 * wave + l16][32 * p + kidx(g4, j)];
+                mma(KK[ti], kw, kf[ti][p]);        // rows t (tile wave), cols i (tile ti)
+                mma(KQ[ti], kf[ti][p], qf[p]);     // rows i (tile ti), cols t (tile wave)
             }
         }
     }
+    __syncthreads();   // q / k rows are dead from here on; their LDS holds A and T
 
     // ---- 3. per value head of this key head ----
-    const IO* conv_w_v = conv_w;
 #pragma unroll 1
     for (int vh = 0; vh < group; ++vh) {
         const int h = hk * group + vh;
         const size_t cv = (size_t)c * Hv + h;
+        F* VB = static_cast<F*>(a.VB) + cv * kVBUnits * 64 + lane;
+        float* gates = reinterpret_cast<float*>(static_cast<F*>(a.VB) + (cv * kVBUnits + kVB_G) * 64);
 
-        // 3a. v: conv + SiLU, transposed into LDS
-#pragma unroll 1
-        for (int it = 0; it < 4; ++it) {
-            const int item = it * 256 + tid;
-            const int t = item >> 4, cg = item & 15;
-            float y[8];
-            if (t < len) {
-                conv8<IO, kConv>(v, Hv, h * kD + 8 * cg, 2 * Hk * kD + h * kD + 8 * cg, t0 + t,
-                                 seq_start, n, Cch, conv_w_v, csin, y);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) y[e] = 0.f;
+        // 3a. v: conv + SiLU, transposed into LDS; gates
+        {
+            Quad<IO, kConv> xv;
+            xv.load(v, Hv, h * kD + 8 * cg, 2 * Hk * kD + h * kD + 8 * cg, t0, tq, len, seq_start, n,
+                    Cch, conv_w, csin);
+            float gl = 0.f, bl = 0.f;
+            if (wave == 0 && lane < len) {
+                gl = a.g[(size_t)(t0 + lane) * Hv + h];
+                bl = a.beta[(size_t)(t0 + lane) * Hv + h];
             }
 #pragma unroll
-            for (int e = 0; e < 8; ++e) sm.vt[8 * cg + e][t] = static_cast<MT>(y[e]);
-        }
-
-        // 3b. gates: G = inclusive cumsum of g over the chunk (padding: g = b = 0)
-        if (wave == 0) {
-            const bool valid = lane < len;
-            float G = valid ? a.g[(size_t)(t0 + lane) * Hv + h] : 0.f;
-            const float bl = valid ? a.beta[(size_t)(t0 + lane) * Hv + h] : 0.f;
+            for (int tt = 0; tt < 4; ++tt) {
+                float y[8];
+                xv.out(tt, y);
+                const bool valid = tq + tt < len;
 #pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float x = __shfl_up(G, off);
-                if (lane >= off) G += x;
+                for (int e = 0; e < 8; ++e) sm.vt[8 * cg + e][tq + tt] = static_cast<MT>(valid ? y[e] : 0.f);
             }
-            const float Gn = __shfl(G, 63);
-            const float gam = exp_f32(G);
-            sm.G[lane] = G;
-            sm.b[lane] = bl;
-            sm.bg[lane] = bl * gam;
-            a.gates[cv * 128 + lane] = gam;
-            a.gates[cv * 128 + 64 + lane] = exp_f32(Gn - G);
+            if (wave == 0) {   // G = inclusive cumsum of g over the chunk (padding: g = b = 0)
+                float G = gl;
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const float x = __shfl_up(G, off);
+                    if (lane >= off) G += x;
+                }
+                const float Gn = __shfl(G, 63);
+                const float gam = exp_f32(G);
+                sm.G[lane] = G;
+                sm.b[lane] = bl;
+                sm.bg[lane] = bl * gam;
+                gates[lane] = gam;
+                gates[64 + lane] = exp_f32(Gn - G);
+            }
         }
         __syncthreads();
 
-        // 3c. A rows of this wave's token tile; P fragments
+        // 3b. A rows of this wave's token tile; P fragments
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 16 * wave + 4 * g4 + r, i = 16 * ti + l16;
-                sm.a[t][i] = (i < t) ? sm.b[t] * KK[ti][r] * exp_f32(sm.G[t] - sm.G[i]) : 0.f;
+                sm.ka.a[t][i] = (i < t) ? sm.b[t] * KK[ti][r] * exp_f32(sm.G[t] - sm.G[i]) : 0.f;
             }
         {
-            F* Pf = static_cast<F*>(a.Pf) + cv * 8 * 64;
             const int t = 16 * wave + l16;
             const float Gt = sm.G[t];
 #pragma unroll
             for (int p = 0; p < 2; ++p) {
+                if (p > (wave >> 1)) continue;   // block above the diagonal: zero
                 F fr;
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
@@ -324,79 +370,95 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep_kernel(PrepArgs a) {
                     const float x = KQ[2 * p + (j >> 2)][j & 3];
                     fr.set(j, (i <= t) ? x * exp_f32(Gt - sm.G[i]) : 0.f);
                 }
-                frag_store(Pf + (wave * 2 + p) * 64 + lane, fr);
+                frag_store(VB + (kVB_P + pfrag_index(wave, p)) * 64, fr);
             }
         }
         __syncthreads();
 
-        // 3d. T = (I + A)^-1 by forward substitution; lane j owns column j
-        if (wave == 0) {
-            float X[kChunk];
+        // 3c. T = (I + A)^-1, blocked by 16: diagonal blocks by forward
+        //     substitution, then T_rs = -T_rr sum_{m=s}^{r-1} A_rm T_ms level by level.
+        if (wave == 0) {   // diagonal blocks: lane = (block, column)
+            const int bb = lane >> 4, j = l16;
+            float X[16];
 #pragma unroll
-            for (int t = 0; t < kChunk; ++t) {
-                float s = (t == lane) ? 1.f : 0.f;
+            for (int r = 0; r < 16; ++r) {
+                float s = (r == j) ? 1.f : 0.f;
 #pragma unroll
-                for (int m = 0; m < t; ++m) s = fmaf(-sm.a[t][m], X[m], s);
-                X[t] = s;
+                for (int m = 0; m < r; ++m) s = fmaf(-sm.ka.a[16 * bb + r][16 * bb + m], X[m], s);
+                X[r] = s;
             }
 #pragma unroll
-            for (int t = 0; t < kChunk; ++t) sm.a[t][lane] = X[t];
+            for (int r = 0; r < 16; ++r) sm.qa.t[16 * bb + r][16 * bb + j] = X[r];
+        } else {           // zero the blocks above the diagonal
+            for (int e = tid - 64; e < 6 * 256; e += 192) {
+                const int blk = e >> 8, r = (e >> 4) & 15, col = e & 15;
+                const int br = blk < 3 ? 0 : (blk < 5 ? 1 : 2);
+                const int bc = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3);
+                sm.qa.t[16 * br + r][16 * bc + col] = 0.f;
+            }
         }
         __syncthreads();
+#pragma unroll
+        for (int d = 1; d < 4; ++d) {   // blocks (r, s) with r - s = d, one per wave
+            if (wave < 4 - d) {
+                const int s = wave, r = wave + d;
+                f32x4 E = {0.f, 0.f, 0.f, 0.f};
+                for (int m = s; m < r; ++m)
+                    E = mm16_lds(&sm.ka.a[16 * r][16 * m], LD, &sm.qa.t[16 * m][16 * s], LD, E, l16, g4);
+                const f32x4 Trs = mm16_acc(&sm.qa.t[16 * r][16 * r], LD, E, l16, g4);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sm.qa.t[16 * r + 4 * g4 + i][16 * s + l16] = -Trs[i];
+            }
+            __syncthreads();
+        }
 
-        // 3e. W^T = K^T diag(b gamma) T^T: rows dk, cols = this wave's tokens.
-        //     Its accumulator tiles are the sweep's A fragments of W.
+        // 3d. W^T = K^T diag(b gamma) T^T (rows dk, cols = this wave's tokens):
+        //     its accumulator tiles are the sweep's A fragments of W.
+        //     U~ = T diag(b) V (rows = this wave's tokens, cols dv).
         {
             const int t = 16 * wave + l16;
-            F bfr[2];
+            const int np = wave < 2 ? 1 : 2;    // token blocks with nonzero T
+            F bw[2], au[2];
 #pragma unroll
-            for (int p = 0; p < 2; ++p)
+            for (int p = 0; p < 2; ++p) {
+                if (p >= np) continue;
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     const int i = 32 * p + kidx(g4, j);
-                    bfr[p].set(j, sm.a[t][i] * sm.bg[i]);
+                    const float tv = sm.qa.t[t][i];
+                    bw[p].set(j, tv * sm.bg[i]);
+                    au[p].set(j, tv * sm.b[i]);
                 }
+            }
             f32x4 Wt[8];
 #pragma unroll
             for (int m = 0; m < 8; ++m) {
                 Wt[m] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int p = 0; p < 2; ++p) {
+                    if (p >= np) continue;
                     F afr;
 #pragma unroll
                     for (int j = 0; j < 8; ++j) afr.v[j] = sm.kt[16 * m + l16][32 * p + kidx(g4, j)];
-                    mma(Wt[m], afr, bfr[p]);
+                    mma(Wt[m], afr, bw[p]);
                 }
             }
-            F* Wf = static_cast<F*>(a.Wf) + cv * 16 * 64;
 #pragma unroll
             for (int pk = 0; pk < 4; ++pk)
-                frag_store(Wf + (wave * 4 + pk) * 64 + lane, acc_to_frag<MT>(Wt[2 * pk], Wt[2 * pk + 1]));
-        }
-
-        // 3f. U~ = T diag(b) V: rows = this wave's tokens, cols dv.
-        {
-            const int t = 16 * wave + l16;
-            F afr[2];
-#pragma unroll
-            for (int p = 0; p < 2; ++p)
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const int i = 32 * p + kidx(g4, j);
-                    afr[p].set(j, sm.a[t][i] * sm.b[i]);
-                }
-            MT* Uf = static_cast<MT*>(a.Uf) + cv * 8 * 4 * 64 * 4;
+                frag_store(VB + (kVB_W + wave * 4 + pk) * 64, acc_to_frag<MT>(Wt[2 * pk], Wt[2 * pk + 1]));
 #pragma unroll
             for (int nt = 0; nt < 8; ++nt) {
                 f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int p = 0; p < 2; ++p) {
+                    if (p >= np) continue;
                     F bfr;
 #pragma unroll
                     for (int j = 0; j < 8; ++j) bfr.v[j] = sm.vt[16 * nt + l16][32 * p + kidx(g4, j)];
-                    mma(acc, afr[p], bfr);
+                    mma(acc, au[p], bfr);
                 }
-                MT* dst = Uf + (((size_t)nt * 4 + wave) * 64 + lane) * 4;
+                // lane (dv, g4) holds U~[16 wave + 4 g4 + r][16 nt + l16]
+                MT* dst = reinterpret_cast<MT*>(VB + (kVB_U + 2 * nt + (wave >> 1)) * 64) + (wave & 1) * 4;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) dst[r] = static_cast<MT>(acc[r]);
             }
@@ -406,36 +468,198 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep_kernel(PrepArgs a) {
 }
 
 // ===========================================================================
-// sequential state sweep: one wave per (sequence, value head, 16 dv rows)
+// sequential state sweep
+//
+// One wave per (sequence, value head, 16-row slice of the dv rows); SW slices
+// of one head share a workgroup.  For bf16 the chunk operands of chunk j+1
+// (three contiguous 1 KB-unit ranges of the workspace) are copied from memory
+// straight into one LDS buffer (global_load_lds, 16 B per lane) while chunk j
+// computes from the other, so each chunk starts with one wait + barrier.
 // ===========================================================================
-template <class IO>
-__global__ __launch_bounds__(64) void gdn_state_sweep_kernel(SweepArgs a) {
-    typedef typename MathOf<IO>::T MT;
-    typedef Frag<MT> F;
+// LDS units of one chunk buffer: KB (Q, K^T), VB units 0..23 (W, P, gates),
+// then the U~ units of the workgroup's slices.
+constexpr int kLdsQ = 0, kLdsKT = 16, kLdsW = 32, kLdsP = 48, kLdsG = 54, kLdsU = 56;
+template <int SW>
+struct SweepLds {
+    static constexpr int kUnits = kLdsU + 2 * SW;       // 1 KB units per chunk buffer
+    static constexpr int kBytes = 2 * kUnits * 1024;    // double buffer
+};
 
-    // XCD-aware unit mapping: the 8 slices of one head share blockIdx.x % 8,
-    // so they run on one XCD and share its L2 for the chunk operands.
-    const int x = blockIdx.x;
-    const int u = (x >> 6) * 8 + (x & 7);
-    const int s = (x >> 3) & 7;
-    if (u >= a.N * a.Hv) return;
-    const int n = u / a.Hv, h = u % a.Hv;
-    const int hk = h / (a.Hv / a.Hk);
-    const int lane = threadIdx.x, l16 = lane & 15, g4 = lane >> 4;
+typedef __attribute__((address_space(3))) bf16x8 lds_b16x8;
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+typedef __attribute__((address_space(3))) float lds_f32;
 
-    int seq_start, L, c_begin;
+// XCD-aware mapping of blockIdx.x to (unit u = n*Hv + h, slice group sg): the
+// slice groups of one head share blockIdx.x % 8, so they run on one XCD and
+// share its L2 for the chunk operands.
+__device__ __forceinline__ void sweep_unit(int x, int groups, int& u, int& sg) {
+    u = (x / (8 * groups)) * 8 + (x & 7);
+    sg = (x >> 3) % groups;
+}
+
+struct SweepSeq {
+    int seq_start, L, c_begin, nch;
+};
+__device__ __forceinline__ SweepSeq sweep_seq(const SweepArgs& a, int n) {
+    SweepSeq q;
     if (a.cu == nullptr) {
-        seq_start = 0;
-        L = a.T;
-        c_begin = 0;
+        q.seq_start = 0;
+        q.L = a.T;
+        q.c_begin = 0;
     } else {
-        seq_start = a.cu[n];
-        L = a.cu[n + 1] - seq_start;
-        c_begin = a.chunk_off[n];
+        q.seq_start = a.cu[n];
+        q.L = a.cu[n + 1] - q.seq_start;
+        q.c_begin = a.chunk_off[n];
     }
-    const int nch = (L + kChunk - 1) / kChunk;
+    q.nch = (q.L + kChunk - 1) / kChunk;
+    return q;
+}
 
-    // S^T tiles: S[m][r] = state[dv = 16 s + l16][dk = 16 m + 4 g4 + r]
+// One chunk of the sweep for the 16 dv rows of this wave, given its operands:
+//   U = U~ - W S^T;  O = diag(gamma) Q S^T + P U;  S <- gamma_n S + K^T diag(e) U
+// S[m] holds rows dk = 16 m + 4 g4 + r, column dv = l16 of S^T.
+template <class MT, class FW, class FQ, class FK, class FP, class FU, class FG>
+__device__ __forceinline__ void sweep_chunk(f32x4 (&S)[8], f32x4 (&O)[4], FW&& wfrag, FQ&& qfrag,
+                                            FK&& ktfrag, FP&& pfrag, FU&& uinit, FG&& gate4,
+                                            float gamma_n) {
+    typedef Frag<MT> F;
+    F Sb[4], Sn[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        Sb[p] = acc_to_frag<MT>(S[2 * p], S[2 * p + 1]);
+        Sn[p] = acc_to_frag<MT>(-S[2 * p], -S[2 * p + 1]);
+    }
+    f32x4 U[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+        U[mt] = uinit(mt);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) mma(U[mt], wfrag(mt * 4 + p), Sn[p]);
+    }
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+        O[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int p = 0; p < 4; ++p) mma(O[mt], qfrag(mt * 4 + p), Sb[p]);
+        O[mt] *= gate4(mt);
+    }
+    F Ub[2], Ud[2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        Ub[p] = acc_to_frag<MT>(U[2 * p], U[2 * p + 1]);
+        Ud[p] = acc_to_frag<MT>(U[2 * p] * gate4(4 + 2 * p), U[2 * p + 1] * gate4(5 + 2 * p));
+    }
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int p = 0; p <= (mt >> 1); ++p) mma(O[mt], pfrag(pfrag_index(mt, p)), Ub[p]);
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        S[m] *= gamma_n;
+#pragma unroll
+        for (int p = 0; p < 2; ++p) mma(S[m], ktfrag(m * 2 + p), Ud[p]);
+    }
+}
+
+template <class IO>
+__device__ __forceinline__ void store_o(IO* out, const f32x4 (&O)[4], int t0, int len, int Hv,
+                                        int h, int s, int l16, int g4) {
+    IO* base = out + ((size_t)t0 * Hv + h) * kD + 16 * s + l16;
+    const size_t row = (size_t)Hv * kD;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = 16 * mt + 4 * g4 + r;
+            if (t < len) base[t * row] = f32_to_io<IO>(O[mt][r]);
+        }
+}
+
+// Copies of chunk c's operands into an LDS buffer: three contiguous unit
+// ranges; wave w of SW issues units w, w + SW, ... of each range.
+template <int SW>
+__device__ __forceinline__ void sweep_issue(const SweepArgs& a, size_t ck, size_t cv, int sg,
+                                            int wave, int lane, lds_b16x8* __restrict__ buf) {
+    const bf16x8* kb = static_cast<const bf16x8*>(a.KB) + ck * kKBUnits * 64 + lane;
+    const bf16x8* vb = static_cast<const bf16x8*>(a.VB) + cv * kVBUnits * 64 + lane;
+    const bf16x8* ub = vb + (kVB_U + 2 * SW * sg) * 64;
+#pragma unroll
+    for (int i = 0; i < kKBUnits / SW; ++i) {
+        const int u = i * SW + wave;
+        __builtin_amdgcn_global_load_lds(kb + u * 64, buf + u * 64, 16, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < kVB_U / SW; ++i) {
+        const int u = i * SW + wave;
+        __builtin_amdgcn_global_load_lds(vb + u * 64, buf + (kLdsW + u) * 64, 16, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int u = 2 * wave + i;
+        __builtin_amdgcn_global_load_lds(ub + u * 64, buf + (kLdsU + u) * 64, 16, 0, 0);
+    }
+}
+
+// One chunk: wait for its operands, start copying the next chunk's into the
+// other buffer, compute.  cur / nxt are distinct buffers (__restrict__), so
+// the compiler adds no waits of its own; the explicit one below orders them.
+template <int SW>
+__device__ __forceinline__ void sweep_lds_step(const SweepArgs& a, const SweepSeq& q, int j, int h,
+                                               int hk, int sg, int wave, f32x4 (&S)[8],
+                                               lds_b16x8* __restrict__ cur,
+                                               lds_b16x8* __restrict__ nxt) {
+    const int lane = threadIdx.x & 63, l16 = lane & 15, g4 = lane >> 4;
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copies into cur have landed
+    __syncthreads();                      // every wave's have; nobody still reads nxt
+    asm volatile("" ::: "memory");
+    if (j + 1 < q.nch) {
+        const size_t c1 = (size_t)q.c_begin + j + 1;
+        sweep_issue<SW>(a, c1 * a.Hk + hk, c1 * a.Hv + h, sg, wave, lane, nxt);
+    }
+    const lds_b16x8* W = cur + kLdsW * 64 + lane;
+    const lds_b16x8* Q = cur + kLdsQ * 64 + lane;
+    const lds_b16x8* KT = cur + kLdsKT * 64 + lane;
+    const lds_b16x8* P = cur + kLdsP * 64 + lane;
+    const lds_f32* G = reinterpret_cast<const lds_f32*>(cur + kLdsG * 64);
+    const lds_b16x8* UU = cur + (kLdsU + 2 * wave) * 64 + lane;
+    const bf16x8 u01 = UU[0], u23 = UU[64];
+    typedef Frag<bf16> F;
+    f32x4 O[4];
+    sweep_chunk<bf16>(
+        S, O, [&](int f) { F x; x.v = W[f * 64]; return x; },
+        [&](int f) { F x; x.v = Q[f * 64]; return x; },
+        [&](int f) { F x; x.v = KT[f * 64]; return x; },
+        [&](int f) { F x; x.v = P[f * 64]; return x; },
+        [&](int mt) {
+            const bf16x8& u = mt < 2 ? u01 : u23;
+            const int o = (mt & 1) * 4;
+            return f32x4{(float)u[o], (float)u[o + 1], (float)u[o + 2], (float)u[o + 3]};
+        },
+        [&](int i) {   // 0..3: exp(G) rows of token tile i; 4..7: exp(G_n - G) of tile i - 4
+            return *reinterpret_cast<const lds_f32x4*>(G + (i >> 2) * 64 + 16 * (i & 3) + 4 * g4);
+        },
+        G[63]);
+    const int s = sg * SW + wave;
+    store_o(static_cast<uint16_t*>(a.out), O, q.seq_start + j * kChunk, min(kChunk, q.L - j * kChunk),
+            a.Hv, h, s, l16, g4);
+}
+
+template <int SW>
+__global__ __launch_bounds__(64 * SW) void gdn_state_sweep_lds_kernel(SweepArgs a) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char gdn_sweep_smem[];
+    lds_b16x8* buf0 = (lds_b16x8*)(gdn_sweep_smem);   // generic -> LDS address space
+    lds_b16x8* buf1 = buf0 + SweepLds<SW>::kUnits * 64;
+
+    int u, sg;
+    sweep_unit(blockIdx.x, 8 / SW, u, sg);
+    if (u >= a.N * a.Hv) return;
+    const int n = u / a.Hv, h = u % a.Hv, hk = h / (a.Hv / a.Hk);
+    // the wave index is uniform; readfirstlane lets the compiler keep it in an SGPR
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, l16 = lane & 15, g4 = lane >> 4;
+    const int s = sg * SW + wave;
+    const SweepSeq q = sweep_seq(a, n);
+
     f32x4 S[8];
     const size_t srow = (((size_t)n * a.Hv + h) * kD + 16 * s + l16) * kD;
     if (a.initial_state != nullptr) {
@@ -447,92 +671,65 @@ __global__ __launch_bounds__(64) void gdn_state_sweep_kernel(SweepArgs a) {
         for (int m = 0; m < 8; ++m) S[m] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    IO* out = static_cast<IO*>(a.out);
-    const F* Qf_all = static_cast<const F*>(a.Qf);
-    const F* KTf_all = static_cast<const F*>(a.KTf);
-    const F* Wf_all = static_cast<const F*>(a.Wf);
-    const F* Pf_all = static_cast<const F*>(a.Pf);
-    const MT* Uf_all = static_cast<const MT*>(a.Uf);
-
+    if (q.nch > 0)
+        sweep_issue<SW>(a, (size_t)q.c_begin * a.Hk + hk, (size_t)q.c_begin * a.Hv + h, sg, wave,
+                        lane, buf0);
 #pragma unroll 1
-    for (int j = 0; j < nch; ++j) {
-        const int c = c_begin + j;
-        const int t0 = seq_start + j * kChunk;
-        const int len = min(kChunk, L - j * kChunk);
-        const size_t ck = (size_t)c * a.Hk + hk, cv = (size_t)c * a.Hv + h;
-        const F* Qf = Qf_all + ck * 16 * 64 + lane;
-        const F* KTf = KTf_all + ck * 16 * 64 + lane;
-        const F* Wf = Wf_all + cv * 16 * 64 + lane;
-        const F* Pf = Pf_all + cv * 8 * 64 + lane;
-        const MT* Uf = Uf_all + ((cv * 8 + s) * 4 * 64 + lane) * 4;
-        const float* gates = a.gates + cv * 128;
-
-        // state as B operands (and negated, for U = U~ - W S^T)
-        F Sb[4], Sn[4];
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            Sb[p] = acc_to_frag<MT>(S[2 * p], S[2 * p + 1]);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) Sn[p].set(e, -static_cast<float>(Sb[p].v[e]));
-        }
-
-        // U = U~ - W S^T
-        f32x4 U[4];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            const MT* src = Uf + (size_t)mt * 64 * 4;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) U[mt][r] = static_cast<float>(src[r]);
-#pragma unroll
-            for (int p = 0; p < 4; ++p) mma(U[mt], frag_load(Wf + (mt * 4 + p) * 64), Sn[p]);
-        }
-
-        // O = diag(gamma) Q S^T + P U
-        f32x4 gam[4], eg[4];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            gam[mt] = *reinterpret_cast<const f32x4*>(gates + 16 * mt + 4 * g4);
-            eg[mt] = *reinterpret_cast<const f32x4*>(gates + 64 + 16 * mt + 4 * g4);
-        }
-        const float gamma_n = gates[63];
-        f32x4 O[4];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            O[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int p = 0; p < 4; ++p) mma(O[mt], frag_load(Qf + (mt * 4 + p) * 64), Sb[p]);
-            O[mt] *= gam[mt];
-        }
-        F Ub[2], Ud[2];
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            Ub[p] = acc_to_frag<MT>(U[2 * p], U[2 * p + 1]);
-            Ud[p] = acc_to_frag<MT>(U[2 * p] * eg[2 * p], U[2 * p + 1] * eg[2 * p + 1]);
-        }
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int p = 0; p <= (mt >> 1); ++p) mma(O[mt], frag_load(Pf + (mt * 2 + p) * 64), Ub[p]);
-
-        // S <- gamma_n S + K^T diag(exp(G_n - G)) U
-#pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            S[m] *= gamma_n;
-#pragma unroll
-            for (int p = 0; p < 2; ++p) mma(S[m], frag_load(KTf + (m * 2 + p) * 64), Ud[p]);
-        }
-
-        // O rows of valid tokens
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 16 * mt + 4 * g4 + r;
-                if (t < len)
-                    out[((size_t)(t0 + t) * a.Hv + h) * kD + 16 * s + l16] = f32_to_io<IO>(O[mt][r]);
-            }
+    for (int j = 0; j < q.nch; j += 2) {
+        sweep_lds_step<SW>(a, q, j, h, hk, sg, wave, S, buf0, buf1);
+        if (j + 1 < q.nch) sweep_lds_step<SW>(a, q, j + 1, h, hk, sg, wave, S, buf1, buf0);
     }
 
+    if (a.final_state != nullptr) {
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+            *reinterpret_cast<f32x4*>(a.final_state + srow + 16 * m + 4 * g4) = S[m];
+    }
+}
+
+// fp32 operands: the same sweep with operands read straight from memory
+// (fp32 fragments are 2 KB; this path serves fp32 inputs, not the bf16 layer).
+__global__ __launch_bounds__(64) void gdn_state_sweep_f32_kernel(SweepArgs a) {
+    typedef Frag<float> F;
+    int u, sg;
+    sweep_unit(blockIdx.x, 8, u, sg);
+    if (u >= a.N * a.Hv) return;
+    const int n = u / a.Hv, h = u % a.Hv, hk = h / (a.Hv / a.Hk);
+    const int lane = threadIdx.x, l16 = lane & 15, g4 = lane >> 4;
+    const int s = sg;
+    const SweepSeq q = sweep_seq(a, n);
+
+    f32x4 S[8];
+    const size_t srow = (((size_t)n * a.Hv + h) * kD + 16 * s + l16) * kD;
+    if (a.initial_state != nullptr) {
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+            S[m] = *reinterpret_cast<const f32x4*>(a.initial_state + srow + 16 * m + 4 * g4);
+    } else {
+#pragma unroll
+        for (int m = 0; m < 8; ++m) S[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll 1
+    for (int j = 0; j < q.nch; ++j) {
+        const size_t c = (size_t)q.c_begin + j;
+        const F* KB = static_cast<const F*>(a.KB) + (c * a.Hk + hk) * kKBUnits * 64 + lane;
+        const F* VB = static_cast<const F*>(a.VB) + (c * a.Hv + h) * kVBUnits * 64 + lane;
+        const float* Uf = reinterpret_cast<const float*>(VB + (kVB_U + 2 * s) * 64);
+        const float* G = reinterpret_cast<const float*>(VB - lane + kVB_G * 64);
+        f32x4 O[4];
+        sweep_chunk<float>(
+            S, O, [&](int f) { return frag_load(VB + (kVB_W + f) * 64); },
+            [&](int f) { return frag_load(KB + (kKB_Q + f) * 64); },
+            [&](int f) { return frag_load(KB + (kKB_KT + f) * 64); },
+            [&](int f) { return frag_load(VB + (kVB_P + f) * 64); },
+            [&](int mt) { return *reinterpret_cast<const f32x4*>(Uf + (mt >> 1) * 64 * 8 + (mt & 1) * 4); },
+            [&](int i) {
+                return *reinterpret_cast<const f32x4*>(G + (i >> 2) * 64 + 16 * (i & 3) + 4 * g4);
+            },
+            G[63]);
+        store_o(static_cast<float*>(a.out), O, q.seq_start + j * kChunk,
+                min(kChunk, q.L - j * kChunk), a.Hv, h, s, l16, g4);
+    }
     if (a.final_state != nullptr) {
 #pragma unroll
         for (int m = 0; m < 8; ++m)
@@ -605,6 +802,11 @@ __global__ __launch_bounds__(256) void gdn_conv_state_kernel(ConvStateArgs a) {
 // ===========================================================================
 // host-side launch sequence
 // ===========================================================================
+// One wave per slice (one workgroup per CU) while the waves fit the chip
+// twice over; beyond that four slices of a head share a workgroup and its
+// chunk copies.
+constexpr int kSweepOneWaveMaxWaves = 512;
+
 // Dynamic LDS above 64 KB must be allowed per kernel; done once per kernel.
 static hipError_t allow_dynamic_lds(const void* kern, unsigned bytes) {
     static const hipError_t bf16_conv = hipFuncSetAttribute(
@@ -619,12 +821,17 @@ static hipError_t allow_dynamic_lds(const void* kern, unsigned bytes) {
     static const hipError_t f32_noconv = hipFuncSetAttribute(
         reinterpret_cast<const void*>(gdn_chunk_prep_kernel<float, false>),
         hipFuncAttributeMaxDynamicSharedMemorySize, sizeof(PrepSmem<float>));
+    static const hipError_t sweep1 = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(gdn_state_sweep_lds_kernel<1>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, SweepLds<1>::kBytes);
+    static const hipError_t sweep4 = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(gdn_state_sweep_lds_kernel<4>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, SweepLds<4>::kBytes);
     (void)kern;
     (void)bytes;
-    if (bf16_conv != hipSuccess) return bf16_conv;
-    if (bf16_noconv != hipSuccess) return bf16_noconv;
-    if (f32_conv != hipSuccess) return f32_conv;
-    return f32_noconv;
+    for (hipError_t e : {bf16_conv, bf16_noconv, f32_conv, f32_noconv, sweep1, sweep4})
+        if (e != hipSuccess) return e;
+    return hipSuccess;
 }
 
 template <class IO>
@@ -649,8 +856,17 @@ static hipError_t launch_all(const PrefillPlan& p, hipStream_t stream, StageReco
     {
         if ((e = rec.begin(GDN_STAGE_STATE_SWEEP, stream)) != hipSuccess) return e;
         const int units = p.sweep.N * p.sweep.Hv;
-        const int blocks = ((units + 7) / 8) * 64;
-        hipLaunchKernelGGL(gdn_state_sweep_kernel<IO>, dim3(blocks), dim3(64), 0, stream, p.sweep);
+        const int unit_blocks = (units + 7) / 8 * 8;
+        if (!p.io_bf16) {
+            hipLaunchKernelGGL(gdn_state_sweep_f32_kernel, dim3(unit_blocks * 8), dim3(64), 0, stream,
+                               p.sweep);
+        } else if (units * 8 <= kSweepOneWaveMaxWaves) {
+            hipLaunchKernelGGL(gdn_state_sweep_lds_kernel<1>, dim3(unit_blocks * 8), dim3(64),
+                               SweepLds<1>::kBytes, stream, p.sweep);
+        } else {
+            hipLaunchKernelGGL(gdn_state_sweep_lds_kernel<4>, dim3(unit_blocks * 2), dim3(256),
+                               SweepLds<4>::kBytes, stream, p.sweep);
+        }
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (p.gated && p.total_tokens > 0) {

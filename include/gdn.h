@@ -106,6 +106,7 @@ gdn_status gdn_prefill_workspace_size(const gdn_desc* d, size_t* bytes);
  *   g, beta        [T_total, Hv] fp32: g is the log-decay (a = exp(g)), beta is b
  *   z              [T_total, Hv, dv] io dtype, gate input        } both NULL:
  *   norm_w         [dv] io dtype, effective RMSNorm weight       } out = o
+ *                  (with T_total == 0, q, k, v, g, beta, z, out may be NULL)
  *   conv_w         [Cch, K] io dtype, Cch = 2*Hk*dk + Hv*dv; NULL: no conv
  *   cu_seqlens     [N+1] int32 device; cu[0] = 0, non-decreasing, cu[N] =
  *                  T_total (precondition).  NULL allowed only when N == 1.
@@ -142,8 +143,7 @@ enum {
     GDN_STAGE_CHUNK_PREP = 1,    /* conv, SiLU, L2, gates, K K^T, UT transform: W, U~, P */
     GDN_STAGE_STATE_SWEEP = 2,   /* sequential chunk sweep: U, O, state update */
     GDN_STAGE_GATED_NORM = 3,    /* z-gated RMSNorm of the output */
-    GDN_STAGE_CONV_STATE = 4,    /* conv state out */
-    GDN_STAGE_STATE_COPY = 5     /* initial -> final state of empty problems */
+    GDN_STAGE_CONV_STATE = 4     /* conv state out */
 };
 gdn_status gdn_prefill_profiled(const gdn_desc* d,
                                 const void* q, const void* k, const void* v,

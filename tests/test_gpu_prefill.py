@@ -29,7 +29,9 @@ def test_lengths_full_layer(T):
     check_prefill(p, gs.generate(p))
 
 
-@pytest.mark.parametrize("g_scale,beta", [(0.01, None), (0.0, None), (1.0, 0.0), (0.01, 1.0)])
+# b = 0 is pure decay; its decay is kept weak enough that the fp64 reference
+# state (exp(sum g) S0) stays far above fp32 underflow.
+@pytest.mark.parametrize("g_scale,beta", [(0.01, None), (0.0, None), (0.05, 0.0), (0.01, 1.0)])
 def test_weak_decay_and_extreme_beta(g_scale, beta):
     p = small(f"decay{g_scale}-beta{beta}", [300], init_state_std=0.01, g_scale=g_scale,
               beta_fixed=beta)
