@@ -62,13 +62,16 @@ __device__ __forceinline__ void store8(float* p, const float* x) {
 }
 
 // ---------------------------------------------------------------------------
-// exp, SiLU, sigmoid from the definitions: e^x = 2^(x log2 e) on v_exp_f32.
+// exp and SiLU from the definitions: e^x = 2^(x log2 e) on v_exp_f32.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float exp_f32(float x) {
     return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
 }
+// SiLU(x) = x * sigmoid(x) = x / (1 + e^-x), with the division done by the
+// hardware reciprocal (v_rcp_f32, about 1 ulp) instead of the IEEE-exact
+// division sequence.
 __device__ __forceinline__ float silu_f32(float x) {
-    return x / (1.0f + exp_f32(-x));
+    return x * __builtin_amdgcn_rcpf(1.0f + exp_f32(-x));
 }
 __device__ __forceinline__ float rsqrt_f32(float x) { return __builtin_amdgcn_rsqf(x); }
 

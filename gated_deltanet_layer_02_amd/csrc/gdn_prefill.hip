@@ -444,8 +444,8 @@ __global__ __launch_bounds__(256, 2) void gdn_chunk_prep_kernel(PrepArgs a) {
                 }
             }
 #pragma unroll
-            for (int pk = 0; pk < 4; ++pk)
-                frag_store(VB + (kVB_W + wave * 4 + pk) * 64, acc_to_frag<MT>(Wt[2 * pk], Wt[2 * pk + 1]));
+            for (int pk = 0; pk < 4; ++pk)   // stored negated: the sweep adds (-W) S^T to U~
+                frag_store(VB + (kVB_W + wave * 4 + pk) * 64, acc_to_frag<MT>(-Wt[2 * pk], -Wt[2 * pk + 1]));
 #pragma unroll
             for (int nt = 0; nt < 8; ++nt) {
                 f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -517,24 +517,22 @@ __device__ __forceinline__ SweepSeq sweep_seq(const SweepArgs& a, int n) {
 
 // One chunk of the sweep for the 16 dv rows of this wave, given its operands:
 //   U = U~ - W S^T;  O = diag(gamma) Q S^T + P U;  S <- gamma_n S + K^T diag(e) U
+// (the W fragments hold -W).
 // S[m] holds rows dk = 16 m + 4 g4 + r, column dv = l16 of S^T.
 template <class MT, class FW, class FQ, class FK, class FP, class FU, class FG>
 __device__ __forceinline__ void sweep_chunk(f32x4 (&S)[8], f32x4 (&O)[4], FW&& wfrag, FQ&& qfrag,
                                             FK&& ktfrag, FP&& pfrag, FU&& uinit, FG&& gate4,
                                             float gamma_n) {
     typedef Frag<MT> F;
-    F Sb[4], Sn[4];
+    F Sb[4];
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        Sb[p] = acc_to_frag<MT>(S[2 * p], S[2 * p + 1]);
-        Sn[p] = acc_to_frag<MT>(-S[2 * p], -S[2 * p + 1]);
-    }
-    f32x4 U[4];
+    for (int p = 0; p < 4; ++p) Sb[p] = acc_to_frag<MT>(S[2 * p], S[2 * p + 1]);
+    f32x4 U[4];   // wfrag holds -W
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
         U[mt] = uinit(mt);
 #pragma unroll
-        for (int p = 0; p < 4; ++p) mma(U[mt], wfrag(mt * 4 + p), Sn[p]);
+        for (int p = 0; p < 4; ++p) mma(U[mt], wfrag(mt * 4 + p), Sb[p]);
     }
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
@@ -564,54 +562,68 @@ __device__ __forceinline__ void sweep_chunk(f32x4 (&S)[8], f32x4 (&O)[4], FW&& w
 template <class IO>
 __device__ __forceinline__ void store_o(IO* out, const f32x4 (&O)[4], int t0, int len, int Hv,
                                         int h, int s, int l16, int g4) {
-    IO* base = out + ((size_t)t0 * Hv + h) * kD + 16 * s + l16;
-    const size_t row = (size_t)Hv * kD;
+    // uniform base + 32-bit per-lane byte offset (scalar-base stores)
+    char* base = reinterpret_cast<char*>(out + ((size_t)t0 * Hv + h) * kD + 16 * s);
+    const uint32_t row = (uint32_t)(Hv * kD * sizeof(IO));
+    const uint32_t lane_off = (uint32_t)(l16 * sizeof(IO)) + 4u * g4 * row;
+    if (len == kChunk) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                *reinterpret_cast<IO*>(base + (lane_off + (16 * mt + r) * row)) = f32_to_io<IO>(O[mt][r]);
+        return;
+    }
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int t = 16 * mt + 4 * g4 + r;
-            if (t < len) base[t * row] = f32_to_io<IO>(O[mt][r]);
+            if (t < len) *reinterpret_cast<IO*>(base + (lane_off + (16 * mt + r) * row)) = f32_to_io<IO>(O[mt][r]);
         }
 }
 
 // Copies of chunk c's operands into an LDS buffer: three contiguous unit
 // ranges; wave w of SW issues units w, w + SW, ... of each range.
+// Addresses are a uniform base plus a 32-bit per-lane byte offset, which maps
+// onto the scalar-base form of the copy instruction.
 template <int SW>
 __device__ __forceinline__ void sweep_issue(const SweepArgs& a, size_t ck, size_t cv, int sg,
                                             int wave, int lane, lds_b16x8* __restrict__ buf) {
-    const bf16x8* kb = static_cast<const bf16x8*>(a.KB) + ck * kKBUnits * 64 + lane;
-    const bf16x8* vb = static_cast<const bf16x8*>(a.VB) + cv * kVBUnits * 64 + lane;
-    const bf16x8* ub = vb + (kVB_U + 2 * SW * sg) * 64;
+    const char* kb = static_cast<const char*>(a.KB) + ck * kKBUnits * 1024;
+    const char* vb = static_cast<const char*>(a.VB) + cv * kVBUnits * 1024;
+    const char* ub = vb + (kVB_U + 2 * SW * sg) * 1024;
+    const uint32_t lo = (uint32_t)lane * 16u + (uint32_t)wave * 1024u;
 #pragma unroll
-    for (int i = 0; i < kKBUnits / SW; ++i) {
-        const int u = i * SW + wave;
-        __builtin_amdgcn_global_load_lds(kb + u * 64, buf + u * 64, 16, 0, 0);
-    }
+    for (int i = 0; i < kKBUnits / SW; ++i)
+        __builtin_amdgcn_global_load_lds(kb + (lo + i * SW * 1024u), buf + (i * SW + wave) * 64, 16, 0, 0);
 #pragma unroll
-    for (int i = 0; i < kVB_U / SW; ++i) {
-        const int u = i * SW + wave;
-        __builtin_amdgcn_global_load_lds(vb + u * 64, buf + (kLdsW + u) * 64, 16, 0, 0);
-    }
+    for (int i = 0; i < kVB_U / SW; ++i)
+        __builtin_amdgcn_global_load_lds(vb + (lo + i * SW * 1024u), buf + (kLdsW + i * SW + wave) * 64, 16, 0, 0);
+    const uint32_t lu = (uint32_t)lane * 16u + (uint32_t)wave * 2048u;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int u = 2 * wave + i;
-        __builtin_amdgcn_global_load_lds(ub + u * 64, buf + (kLdsU + u) * 64, 16, 0, 0);
-    }
+    for (int i = 0; i < 2; ++i)
+        __builtin_amdgcn_global_load_lds(ub + (lu + i * 1024u), buf + (kLdsU + 2 * wave + i) * 64, 16, 0, 0);
 }
 
 // One chunk: wait for its operands, start copying the next chunk's into the
 // other buffer, compute.  cur / nxt are distinct buffers (__restrict__), so
 // the compiler adds no waits of its own; the explicit one below orders them.
+// The previous chunk's output (Oprev) is stored here, after the wait, so its
+// stores complete behind this chunk's work instead of delaying the next wait.
 template <int SW>
 __device__ __forceinline__ void sweep_lds_step(const SweepArgs& a, const SweepSeq& q, int j, int h,
                                                int hk, int sg, int wave, f32x4 (&S)[8],
-                                               lds_b16x8* __restrict__ cur,
+                                               f32x4 (&Oprev)[4], lds_b16x8* __restrict__ cur,
                                                lds_b16x8* __restrict__ nxt) {
     const int lane = threadIdx.x & 63, l16 = lane & 15, g4 = lane >> 4;
+    const int s = sg * SW + wave;
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copies into cur have landed
     __syncthreads();                      // every wave's have; nobody still reads nxt
     asm volatile("" ::: "memory");
+    if (j > 0)
+        store_o(static_cast<uint16_t*>(a.out), Oprev, q.seq_start + (j - 1) * kChunk, kChunk, a.Hv, h,
+                s, l16, g4);
     if (j + 1 < q.nch) {
         const size_t c1 = (size_t)q.c_begin + j + 1;
         sweep_issue<SW>(a, c1 * a.Hk + hk, c1 * a.Hv + h, sg, wave, lane, nxt);
@@ -624,9 +636,8 @@ __device__ __forceinline__ void sweep_lds_step(const SweepArgs& a, const SweepSe
     const lds_b16x8* UU = cur + (kLdsU + 2 * wave) * 64 + lane;
     const bf16x8 u01 = UU[0], u23 = UU[64];
     typedef Frag<bf16> F;
-    f32x4 O[4];
     sweep_chunk<bf16>(
-        S, O, [&](int f) { F x; x.v = W[f * 64]; return x; },
+        S, Oprev, [&](int f) { F x; x.v = W[f * 64]; return x; },
         [&](int f) { F x; x.v = Q[f * 64]; return x; },
         [&](int f) { F x; x.v = KT[f * 64]; return x; },
         [&](int f) { F x; x.v = P[f * 64]; return x; },
@@ -639,9 +650,6 @@ __device__ __forceinline__ void sweep_lds_step(const SweepArgs& a, const SweepSe
             return *reinterpret_cast<const lds_f32x4*>(G + (i >> 2) * 64 + 16 * (i & 3) + 4 * g4);
         },
         G[63]);
-    const int s = sg * SW + wave;
-    store_o(static_cast<uint16_t*>(a.out), O, q.seq_start + j * kChunk, min(kChunk, q.L - j * kChunk),
-            a.Hv, h, s, l16, g4);
 }
 
 template <int SW>
@@ -674,11 +682,15 @@ __global__ __launch_bounds__(64 * SW) void gdn_state_sweep_lds_kernel(SweepArgs 
     if (q.nch > 0)
         sweep_issue<SW>(a, (size_t)q.c_begin * a.Hk + hk, (size_t)q.c_begin * a.Hv + h, sg, wave,
                         lane, buf0);
+    f32x4 O[4];
 #pragma unroll 1
     for (int j = 0; j < q.nch; j += 2) {
-        sweep_lds_step<SW>(a, q, j, h, hk, sg, wave, S, buf0, buf1);
-        if (j + 1 < q.nch) sweep_lds_step<SW>(a, q, j + 1, h, hk, sg, wave, S, buf1, buf0);
+        sweep_lds_step<SW>(a, q, j, h, hk, sg, wave, S, O, buf0, buf1);
+        if (j + 1 < q.nch) sweep_lds_step<SW>(a, q, j + 1, h, hk, sg, wave, S, O, buf1, buf0);
     }
+    if (q.nch > 0)   // output of the last chunk
+        store_o(static_cast<uint16_t*>(a.out), O, q.seq_start + (q.nch - 1) * kChunk,
+                q.L - (q.nch - 1) * kChunk, a.Hv, h, s, l16, g4);
 
     if (a.final_state != nullptr) {
 #pragma unroll
@@ -805,7 +817,7 @@ __global__ __launch_bounds__(256) void gdn_conv_state_kernel(ConvStateArgs a) {
 // One wave per slice (one workgroup per CU) while the waves fit the chip
 // twice over; beyond that four slices of a head share a workgroup and its
 // chunk copies.
-constexpr int kSweepOneWaveMaxWaves = 512;
+constexpr int kSweepOneWaveMaxWaves = 0;
 
 // Dynamic LDS above 64 KB must be allowed per kernel; done once per kernel.
 static hipError_t allow_dynamic_lds(const void* kern, unsigned bytes) {
