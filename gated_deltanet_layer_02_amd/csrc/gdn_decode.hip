@@ -20,11 +20,30 @@
 
 namespace gdn {
 
-// state element types
-__device__ __forceinline__ void load_row8(const float* p, float* o) { load8(p, o); }
-__device__ __forceinline__ void load_row8(const uint16_t* p, float* o) { load8(p, o); }
-__device__ __forceinline__ void store_row8(float* p, const float* x) { store8(p, x); }
-__device__ __forceinline__ void store_row8(uint16_t* p, const float* x) { store8(p, x); }
+// State rows are streamed once per call: nontemporal loads and stores keep
+// them from displacing anything in the caches (a read + write stream runs
+// measurably faster this way on MI355X).
+__device__ __forceinline__ void load_row8(const float* p, float* o) {
+    const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    const f32x4 b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p) + 1);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { o[e] = a[e]; o[4 + e] = b[e]; }
+}
+__device__ __forceinline__ void load_row8(const uint16_t* p, float* o) {
+    const u16x8 v = __builtin_nontemporal_load(reinterpret_cast<const u16x8*>(p));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = bf16_bits_to_f32(v[e]);
+}
+__device__ __forceinline__ void store_row8(float* p, const float* x) {
+    __builtin_nontemporal_store(f32x4{x[0], x[1], x[2], x[3]}, reinterpret_cast<f32x4*>(p));
+    __builtin_nontemporal_store(f32x4{x[4], x[5], x[6], x[7]}, reinterpret_cast<f32x4*>(p) + 1);
+}
+__device__ __forceinline__ void store_row8(uint16_t* p, const float* x) {
+    u16x8 v;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = f32_to_bf16_bits(x[e]);
+    __builtin_nontemporal_store(v, reinterpret_cast<u16x8*>(p));
+}
 
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
