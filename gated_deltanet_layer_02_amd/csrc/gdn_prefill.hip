@@ -470,28 +470,31 @@ __global__ __launch_bounds__(256, 2) void gdn_chunk_prep_kernel(PrepArgs a) {
 // ===========================================================================
 // sequential state sweep
 //
-// One wave per (sequence, value head, 16-row slice of the dv rows); SW slices
-// of one head share a workgroup.  For bf16 the chunk operands of chunk j+1
-// (three contiguous 1 KB-unit ranges of the workspace) are copied from memory
-// straight into one LDS buffer (global_load_lds, 16 B per lane) while chunk j
-// computes from the other, so each chunk starts with one wait + barrier.
+// The dv rows of S never mix, so each head's state is cut into eight 16-row
+// tiles; a wave owns NT consecutive tiles and SW waves of one head share a
+// workgroup.  For bf16, the chunk operands of chunk j+1 (three contiguous
+// 1 KB-unit ranges of the workspace) are copied from memory straight into one
+// LDS buffer (global_load_lds, 16 B per lane) while chunk j computes from the
+// other, so each chunk starts with one wait + barrier.  Every operand
+// fragment read from LDS feeds NT MFMAs (one per tile of the wave).
 // ===========================================================================
 // LDS units of one chunk buffer: KB (Q, K^T), VB units 0..23 (W, P, gates),
-// then the U~ units of the workgroup's slices.
+// then the U~ units of the workgroup's tiles.
 constexpr int kLdsQ = 0, kLdsKT = 16, kLdsW = 32, kLdsP = 48, kLdsG = 54, kLdsU = 56;
-template <int SW>
+template <int SW, int NT>
 struct SweepLds {
-    static constexpr int kUnits = kLdsU + 2 * SW;       // 1 KB units per chunk buffer
-    static constexpr int kBytes = 2 * kUnits * 1024;    // double buffer
+    static constexpr int kGroups = 8 / (SW * NT);         // workgroups per head
+    static constexpr int kUnits = kLdsU + 2 * SW * NT;    // 1 KB units per chunk buffer
+    static constexpr int kBytes = 2 * kUnits * 1024;      // double buffer
 };
 
 typedef __attribute__((address_space(3))) bf16x8 lds_b16x8;
 typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
 typedef __attribute__((address_space(3))) float lds_f32;
 
-// XCD-aware mapping of blockIdx.x to (unit u = n*Hv + h, slice group sg): the
-// slice groups of one head share blockIdx.x % 8, so they run on one XCD and
-// share its L2 for the chunk operands.
+// XCD-aware mapping of blockIdx.x to (unit u = n*Hv + h, group sg): the
+// groups of one head share blockIdx.x % 8, so they run on one XCD and share
+// its L2 for the chunk operands.
 __device__ __forceinline__ void sweep_unit(int x, int groups, int& u, int& sg) {
     u = (x / (8 * groups)) * 8 + (x & 7);
     sg = (x >> 3) % groups;
@@ -515,54 +518,92 @@ __device__ __forceinline__ SweepSeq sweep_seq(const SweepArgs& a, int n) {
     return q;
 }
 
-// One chunk of the sweep for the 16 dv rows of this wave, given its operands:
+// One chunk of the sweep for the NT 16-row tiles of this wave:
 //   U = U~ - W S^T;  O = diag(gamma) Q S^T + P U;  S <- gamma_n S + K^T diag(e) U
-// (the W fragments hold -W).
-// S[m] holds rows dk = 16 m + 4 g4 + r, column dv = l16 of S^T.
-template <class MT, class FW, class FQ, class FK, class FP, class FU, class FG>
-__device__ __forceinline__ void sweep_chunk(f32x4 (&S)[8], f32x4 (&O)[4], FW&& wfrag, FQ&& qfrag,
-                                            FK&& ktfrag, FP&& pfrag, FU&& uinit, FG&& gate4,
-                                            float gamma_n) {
+// (the W fragments hold -W).  S[nt][m] holds rows dk = 16 m + 4 g4 + r,
+// column dv = l16 of tile nt of S^T.
+template <class MT, int NT, class FW, class FQ, class FK, class FP, class FU, class FG>
+__device__ __forceinline__ void sweep_chunk(f32x4 (&S)[NT][8], f32x4 (&O)[NT][4], FW&& wfrag,
+                                            FQ&& qfrag, FK&& ktfrag, FP&& pfrag, FU&& uinit,
+                                            FG&& gate4, float gamma_n) {
+    // Every stage reads its A fragments in one batch before its MFMAs, and the
+    // K steps run in the outer loop so independent accumulators alternate
+    // instead of waiting on each other.
     typedef Frag<MT> F;
-    F Sb[4];
+    F Sb[NT][4];
 #pragma unroll
-    for (int p = 0; p < 4; ++p) Sb[p] = acc_to_frag<MT>(S[2 * p], S[2 * p + 1]);
-    f32x4 U[4];   // wfrag holds -W
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int p = 0; p < 4; ++p) Sb[nt][p] = acc_to_frag<MT>(S[nt][2 * p], S[nt][2 * p + 1]);
+    f32x4 U[NT][4];
+    {
+        F w[16], qf[16];
+#pragma unroll
+        for (int f = 0; f < 16; ++f) w[f] = wfrag(f);     // -W
+#pragma unroll
+        for (int f = 0; f < 16; ++f) qf[f] = qfrag(f);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                U[nt][mt] = uinit(nt, mt);
+                O[nt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) mma(U[nt][mt], w[mt * 4 + p], Sb[nt][p]);
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) mma(O[nt][mt], qf[mt * 4 + p], Sb[nt][p]);
+    }
+    F kt[16], pf[kPFrags];
+#pragma unroll
+    for (int f = 0; f < kPFrags; ++f) pf[f] = pfrag(f);
+#pragma unroll
+    for (int f = 0; f < 16; ++f) kt[f] = ktfrag(f);
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-        U[mt] = uinit(mt);
+        const f32x4 gm = gate4(mt);
 #pragma unroll
-        for (int p = 0; p < 4; ++p) mma(U[mt], wfrag(mt * 4 + p), Sb[p]);
+        for (int nt = 0; nt < NT; ++nt) O[nt][mt] *= gm;
     }
+    F Ub[NT][2], Ud[NT][2];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-        O[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-        for (int p = 0; p < 4; ++p) mma(O[mt], qfrag(mt * 4 + p), Sb[p]);
-        O[mt] *= gate4(mt);
-    }
-    F Ub[2], Ud[2];
+        for (int p = 0; p < 2; ++p) {
+            Ub[nt][p] = acc_to_frag<MT>(U[nt][2 * p], U[nt][2 * p + 1]);
+            Ud[nt][p] = acc_to_frag<MT>(U[nt][2 * p] * gate4(4 + 2 * p), U[nt][2 * p + 1] * gate4(5 + 2 * p));
+        }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int m = 0; m < 8; ++m) S[nt][m] *= gamma_n;
+    // S update (8 independent accumulators per tile) interleaved with P U
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
-        Ub[p] = acc_to_frag<MT>(U[2 * p], U[2 * p + 1]);
-        Ud[p] = acc_to_frag<MT>(U[2 * p] * gate4(4 + 2 * p), U[2 * p + 1] * gate4(5 + 2 * p));
-    }
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+        for (int m = 0; m < 8; ++m)
 #pragma unroll
-        for (int p = 0; p <= (mt >> 1); ++p) mma(O[mt], pfrag(pfrag_index(mt, p)), Ub[p]);
+            for (int nt = 0; nt < NT; ++nt) mma(S[nt][m], kt[m * 2 + p], Ud[nt][p]);
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-        S[m] *= gamma_n;
+        for (int mt = 2 * p; mt < 4; ++mt)   // P blocks above the diagonal are zero
 #pragma unroll
-        for (int p = 0; p < 2; ++p) mma(S[m], ktfrag(m * 2 + p), Ud[p]);
+            for (int nt = 0; nt < NT; ++nt) mma(O[nt][mt], pf[pfrag_index(mt, p)], Ub[nt][p]);
     }
 }
 
+// O rows of one 16-row dv tile s (column dv = 16 s + l16) of chunk tokens t0...
 template <class IO>
 __device__ __forceinline__ void store_o(IO* out, const f32x4 (&O)[4], int t0, int len, int Hv,
                                         int h, int s, int l16, int g4) {
-    // uniform base + 32-bit per-lane byte offset (scalar-base stores)
+    // uniform base + 32-bit per-lane byte offset
     char* base = reinterpret_cast<char*>(out + ((size_t)t0 * Hv + h) * kD + 16 * s);
     const uint32_t row = (uint32_t)(Hv * kD * sizeof(IO));
     const uint32_t lane_off = (uint32_t)(l16 * sizeof(IO)) + 4u * g4 * row;
@@ -584,15 +625,15 @@ __device__ __forceinline__ void store_o(IO* out, const f32x4 (&O)[4], int t0, in
 }
 
 // Copies of chunk c's operands into an LDS buffer: three contiguous unit
-// ranges; wave w of SW issues units w, w + SW, ... of each range.
-// Addresses are a uniform base plus a 32-bit per-lane byte offset, which maps
-// onto the scalar-base form of the copy instruction.
-template <int SW>
+// ranges; wave w of SW issues units w, w + SW, ... of the shared ranges and
+// the 2 NT U~ units of its own tiles.  Addresses are a uniform base plus a
+// 32-bit per-lane byte offset (the scalar-base form of the copy instruction).
+template <int SW, int NT>
 __device__ __forceinline__ void sweep_issue(const SweepArgs& a, size_t ck, size_t cv, int sg,
                                             int wave, int lane, lds_b16x8* __restrict__ buf) {
     const char* kb = static_cast<const char*>(a.KB) + ck * kKBUnits * 1024;
     const char* vb = static_cast<const char*>(a.VB) + cv * kVBUnits * 1024;
-    const char* ub = vb + (kVB_U + 2 * SW * sg) * 1024;
+    const char* ub = vb + (kVB_U + 2 * SW * NT * sg) * 1024;
     const uint32_t lo = (uint32_t)lane * 16u + (uint32_t)wave * 1024u;
 #pragma unroll
     for (int i = 0; i < kKBUnits / SW; ++i)
@@ -600,10 +641,10 @@ __device__ __forceinline__ void sweep_issue(const SweepArgs& a, size_t ck, size_
 #pragma unroll
     for (int i = 0; i < kVB_U / SW; ++i)
         __builtin_amdgcn_global_load_lds(vb + (lo + i * SW * 1024u), buf + (kLdsW + i * SW + wave) * 64, 16, 0, 0);
-    const uint32_t lu = (uint32_t)lane * 16u + (uint32_t)wave * 2048u;
+    const uint32_t lu = (uint32_t)lane * 16u + (uint32_t)wave * (2048u * NT);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-        __builtin_amdgcn_global_load_lds(ub + (lu + i * 1024u), buf + (kLdsU + 2 * wave + i) * 64, 16, 0, 0);
+    for (int i = 0; i < 2 * NT; ++i)
+        __builtin_amdgcn_global_load_lds(ub + (lu + i * 1024u), buf + (kLdsU + 2 * NT * wave + i) * 64, 16, 0, 0);
 }
 
 // One chunk: wait for its operands, start copying the next chunk's into the
@@ -611,38 +652,40 @@ __device__ __forceinline__ void sweep_issue(const SweepArgs& a, size_t ck, size_
 // the compiler adds no waits of its own; the explicit one below orders them.
 // The previous chunk's output (Oprev) is stored here, after the wait, so its
 // stores complete behind this chunk's work instead of delaying the next wait.
-template <int SW>
+template <int SW, int NT>
 __device__ __forceinline__ void sweep_lds_step(const SweepArgs& a, const SweepSeq& q, int j, int h,
-                                               int hk, int sg, int wave, f32x4 (&S)[8],
-                                               f32x4 (&Oprev)[4], lds_b16x8* __restrict__ cur,
+                                               int hk, int sg, int wave, f32x4 (&S)[NT][8],
+                                               f32x4 (&Oprev)[NT][4], lds_b16x8* __restrict__ cur,
                                                lds_b16x8* __restrict__ nxt) {
     const int lane = threadIdx.x & 63, l16 = lane & 15, g4 = lane >> 4;
-    const int s = sg * SW + wave;
+    const int s0 = (sg * SW + wave) * NT;   // first tile of this wave
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copies into cur have landed
     __syncthreads();                      // every wave's have; nobody still reads nxt
     asm volatile("" ::: "memory");
-    if (j > 0)
-        store_o(static_cast<uint16_t*>(a.out), Oprev, q.seq_start + (j - 1) * kChunk, kChunk, a.Hv, h,
-                s, l16, g4);
+    if (j > 0) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+            store_o(static_cast<uint16_t*>(a.out), Oprev[nt], q.seq_start + (j - 1) * kChunk, kChunk,
+                    a.Hv, h, s0 + nt, l16, g4);
+    }
     if (j + 1 < q.nch) {
         const size_t c1 = (size_t)q.c_begin + j + 1;
-        sweep_issue<SW>(a, c1 * a.Hk + hk, c1 * a.Hv + h, sg, wave, lane, nxt);
+        sweep_issue<SW, NT>(a, c1 * a.Hk + hk, c1 * a.Hv + h, sg, wave, lane, nxt);
     }
     const lds_b16x8* W = cur + kLdsW * 64 + lane;
     const lds_b16x8* Q = cur + kLdsQ * 64 + lane;
     const lds_b16x8* KT = cur + kLdsKT * 64 + lane;
     const lds_b16x8* P = cur + kLdsP * 64 + lane;
     const lds_f32* G = reinterpret_cast<const lds_f32*>(cur + kLdsG * 64);
-    const lds_b16x8* UU = cur + (kLdsU + 2 * wave) * 64 + lane;
-    const bf16x8 u01 = UU[0], u23 = UU[64];
+    const lds_b16x8* UU = cur + (kLdsU + 2 * NT * wave) * 64 + lane;
     typedef Frag<bf16> F;
-    sweep_chunk<bf16>(
+    sweep_chunk<bf16, NT>(
         S, Oprev, [&](int f) { F x; x.v = W[f * 64]; return x; },
         [&](int f) { F x; x.v = Q[f * 64]; return x; },
         [&](int f) { F x; x.v = KT[f * 64]; return x; },
         [&](int f) { F x; x.v = P[f * 64]; return x; },
-        [&](int mt) {
-            const bf16x8& u = mt < 2 ? u01 : u23;
+        [&](int nt, int mt) {   // U~ of tile nt, token tile mt (pairs of token tiles per unit)
+            const bf16x8 u = UU[(2 * nt + (mt >> 1)) * 64];
             const int o = (mt & 1) * 4;
             return f32x4{(float)u[o], (float)u[o + 1], (float)u[o + 2], (float)u[o + 3]};
         },
@@ -652,50 +695,58 @@ __device__ __forceinline__ void sweep_lds_step(const SweepArgs& a, const SweepSe
         G[63]);
 }
 
-template <int SW>
+template <int SW, int NT>
 __global__ __launch_bounds__(64 * SW) void gdn_state_sweep_lds_kernel(SweepArgs a) {
+    typedef SweepLds<SW, NT> L;
     extern __shared__ __attribute__((aligned(16))) unsigned char gdn_sweep_smem[];
     lds_b16x8* buf0 = (lds_b16x8*)(gdn_sweep_smem);   // generic -> LDS address space
-    lds_b16x8* buf1 = buf0 + SweepLds<SW>::kUnits * 64;
+    lds_b16x8* buf1 = buf0 + L::kUnits * 64;
 
     int u, sg;
-    sweep_unit(blockIdx.x, 8 / SW, u, sg);
+    sweep_unit(blockIdx.x, L::kGroups, u, sg);
     if (u >= a.N * a.Hv) return;
     const int n = u / a.Hv, h = u % a.Hv, hk = h / (a.Hv / a.Hk);
     // the wave index is uniform; readfirstlane lets the compiler keep it in an SGPR
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63, l16 = lane & 15, g4 = lane >> 4;
-    const int s = sg * SW + wave;
+    const int s0 = (sg * SW + wave) * NT;
     const SweepSeq q = sweep_seq(a, n);
 
-    f32x4 S[8];
-    const size_t srow = (((size_t)n * a.Hv + h) * kD + 16 * s + l16) * kD;
-    if (a.initial_state != nullptr) {
+    f32x4 S[NT][8];
+    const size_t hrow = ((size_t)n * a.Hv + h) * kD;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const size_t srow = (hrow + 16 * (s0 + nt) + l16) * kD;
 #pragma unroll
         for (int m = 0; m < 8; ++m)
-            S[m] = *reinterpret_cast<const f32x4*>(a.initial_state + srow + 16 * m + 4 * g4);
-    } else {
-#pragma unroll
-        for (int m = 0; m < 8; ++m) S[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+            S[nt][m] = a.initial_state != nullptr
+                           ? *reinterpret_cast<const f32x4*>(a.initial_state + srow + 16 * m + 4 * g4)
+                           : f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
     if (q.nch > 0)
-        sweep_issue<SW>(a, (size_t)q.c_begin * a.Hk + hk, (size_t)q.c_begin * a.Hv + h, sg, wave,
-                        lane, buf0);
-    f32x4 O[4];
+        sweep_issue<SW, NT>(a, (size_t)q.c_begin * a.Hk + hk, (size_t)q.c_begin * a.Hv + h, sg, wave,
+                            lane, buf0);
+    f32x4 O[NT][4];
 #pragma unroll 1
     for (int j = 0; j < q.nch; j += 2) {
-        sweep_lds_step<SW>(a, q, j, h, hk, sg, wave, S, O, buf0, buf1);
-        if (j + 1 < q.nch) sweep_lds_step<SW>(a, q, j + 1, h, hk, sg, wave, S, O, buf1, buf0);
+        sweep_lds_step<SW, NT>(a, q, j, h, hk, sg, wave, S, O, buf0, buf1);
+        if (j + 1 < q.nch) sweep_lds_step<SW, NT>(a, q, j + 1, h, hk, sg, wave, S, O, buf1, buf0);
     }
-    if (q.nch > 0)   // output of the last chunk
-        store_o(static_cast<uint16_t*>(a.out), O, q.seq_start + (q.nch - 1) * kChunk,
-                q.L - (q.nch - 1) * kChunk, a.Hv, h, s, l16, g4);
-
+    if (q.nch > 0) {   // output of the last chunk
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+            store_o(static_cast<uint16_t*>(a.out), O[nt], q.seq_start + (q.nch - 1) * kChunk,
+                    q.L - (q.nch - 1) * kChunk, a.Hv, h, s0 + nt, l16, g4);
+    }
     if (a.final_state != nullptr) {
 #pragma unroll
-        for (int m = 0; m < 8; ++m)
-            *reinterpret_cast<f32x4*>(a.final_state + srow + 16 * m + 4 * g4) = S[m];
+        for (int nt = 0; nt < NT; ++nt) {
+            const size_t srow = (hrow + 16 * (s0 + nt) + l16) * kD;
+#pragma unroll
+            for (int m = 0; m < 8; ++m)
+                *reinterpret_cast<f32x4*>(a.final_state + srow + 16 * m + 4 * g4) = S[nt][m];
+        }
     }
 }
 
@@ -711,16 +762,13 @@ __global__ __launch_bounds__(64) void gdn_state_sweep_f32_kernel(SweepArgs a) {
     const int s = sg;
     const SweepSeq q = sweep_seq(a, n);
 
-    f32x4 S[8];
+    f32x4 S[1][8];
     const size_t srow = (((size_t)n * a.Hv + h) * kD + 16 * s + l16) * kD;
-    if (a.initial_state != nullptr) {
 #pragma unroll
-        for (int m = 0; m < 8; ++m)
-            S[m] = *reinterpret_cast<const f32x4*>(a.initial_state + srow + 16 * m + 4 * g4);
-    } else {
-#pragma unroll
-        for (int m = 0; m < 8; ++m) S[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int m = 0; m < 8; ++m)
+        S[0][m] = a.initial_state != nullptr
+                      ? *reinterpret_cast<const f32x4*>(a.initial_state + srow + 16 * m + 4 * g4)
+                      : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 1
     for (int j = 0; j < q.nch; ++j) {
         const size_t c = (size_t)q.c_begin + j;
@@ -728,24 +776,24 @@ __global__ __launch_bounds__(64) void gdn_state_sweep_f32_kernel(SweepArgs a) {
         const F* VB = static_cast<const F*>(a.VB) + (c * a.Hv + h) * kVBUnits * 64 + lane;
         const float* Uf = reinterpret_cast<const float*>(VB + (kVB_U + 2 * s) * 64);
         const float* G = reinterpret_cast<const float*>(VB - lane + kVB_G * 64);
-        f32x4 O[4];
-        sweep_chunk<float>(
+        f32x4 O[1][4];
+        sweep_chunk<float, 1>(
             S, O, [&](int f) { return frag_load(VB + (kVB_W + f) * 64); },
             [&](int f) { return frag_load(KB + (kKB_Q + f) * 64); },
             [&](int f) { return frag_load(KB + (kKB_KT + f) * 64); },
             [&](int f) { return frag_load(VB + (kVB_P + f) * 64); },
-            [&](int mt) { return *reinterpret_cast<const f32x4*>(Uf + (mt >> 1) * 64 * 8 + (mt & 1) * 4); },
+            [&](int, int mt) { return *reinterpret_cast<const f32x4*>(Uf + (mt >> 1) * 64 * 8 + (mt & 1) * 4); },
             [&](int i) {
                 return *reinterpret_cast<const f32x4*>(G + (i >> 2) * 64 + 16 * (i & 3) + 4 * g4);
             },
             G[63]);
-        store_o(static_cast<float*>(a.out), O, q.seq_start + j * kChunk,
+        store_o(static_cast<float*>(a.out), O[0], q.seq_start + j * kChunk,
                 min(kChunk, q.L - j * kChunk), a.Hv, h, s, l16, g4);
     }
     if (a.final_state != nullptr) {
 #pragma unroll
         for (int m = 0; m < 8; ++m)
-            *reinterpret_cast<f32x4*>(a.final_state + srow + 16 * m + 4 * g4) = S[m];
+            *reinterpret_cast<f32x4*>(a.final_state + srow + 16 * m + 4 * g4) = S[0][m];
     }
 }
 
@@ -814,10 +862,10 @@ __global__ __launch_bounds__(256) void gdn_conv_state_kernel(ConvStateArgs a) {
 // ===========================================================================
 // host-side launch sequence
 // ===========================================================================
-// One wave per slice (one workgroup per CU) while the waves fit the chip
-// twice over; beyond that four slices of a head share a workgroup and its
-// chunk copies.
-constexpr int kSweepOneWaveMaxWaves = 0;
+// bf16 sweep: 4 waves x 2 tiles = one head per workgroup (one copy of the
+// chunk operands per head and chunk; each LDS fragment feeds two MFMAs).
+constexpr int kSweepSW = 4, kSweepNT = 1;
+typedef SweepLds<kSweepSW, kSweepNT> SweepCfg;
 
 // Dynamic LDS above 64 KB must be allowed per kernel; done once per kernel.
 static hipError_t allow_dynamic_lds(const void* kern, unsigned bytes) {
@@ -833,15 +881,12 @@ static hipError_t allow_dynamic_lds(const void* kern, unsigned bytes) {
     static const hipError_t f32_noconv = hipFuncSetAttribute(
         reinterpret_cast<const void*>(gdn_chunk_prep_kernel<float, false>),
         hipFuncAttributeMaxDynamicSharedMemorySize, sizeof(PrepSmem<float>));
-    static const hipError_t sweep1 = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(gdn_state_sweep_lds_kernel<1>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, SweepLds<1>::kBytes);
-    static const hipError_t sweep4 = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(gdn_state_sweep_lds_kernel<4>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, SweepLds<4>::kBytes);
+    static const hipError_t sweep = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(gdn_state_sweep_lds_kernel<kSweepSW, kSweepNT>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, SweepCfg::kBytes);
     (void)kern;
     (void)bytes;
-    for (hipError_t e : {bf16_conv, bf16_noconv, f32_conv, f32_noconv, sweep1, sweep4})
+    for (hipError_t e : {bf16_conv, bf16_noconv, f32_conv, f32_noconv, sweep})
         if (e != hipSuccess) return e;
     return hipSuccess;
 }
@@ -872,12 +917,10 @@ static hipError_t launch_all(const PrefillPlan& p, hipStream_t stream, StageReco
         if (!p.io_bf16) {
             hipLaunchKernelGGL(gdn_state_sweep_f32_kernel, dim3(unit_blocks * 8), dim3(64), 0, stream,
                                p.sweep);
-        } else if (units * 8 <= kSweepOneWaveMaxWaves) {
-            hipLaunchKernelGGL(gdn_state_sweep_lds_kernel<1>, dim3(unit_blocks * 8), dim3(64),
-                               SweepLds<1>::kBytes, stream, p.sweep);
         } else {
-            hipLaunchKernelGGL(gdn_state_sweep_lds_kernel<4>, dim3(unit_blocks * 2), dim3(256),
-                               SweepLds<4>::kBytes, stream, p.sweep);
+            hipLaunchKernelGGL((gdn_state_sweep_lds_kernel<kSweepSW, kSweepNT>),
+                               dim3(unit_blocks * SweepCfg::kGroups), dim3(64 * kSweepSW),
+                               SweepCfg::kBytes, stream, p.sweep);
         }
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
