@@ -75,6 +75,43 @@ __device__ __forceinline__ float silu_f32(float x) {
 }
 __device__ __forceinline__ float rsqrt_f32(float x) { return __builtin_amdgcn_rsqf(x); }
 
+// Sum over the 16 lanes of a DPP row (lanes 16 r .. 16 r + 15); every lane of
+// the row gets the total.  Two quad swaps, then the half-row mirror and the
+// row mirror pair up the partial sums: four v_add_f32 with DPP operands
+// instead of four LDS-routed lane permutes.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl,
+                                                                 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_sum(float x) {
+    x += dpp_mov<0xB1>(x);    // quad_perm [1, 0, 3, 2]
+    x += dpp_mov<0x4E>(x);    // quad_perm [2, 3, 0, 1]
+    x += dpp_mov<0x141>(x);   // row_half_mirror: lane i <- 7 - i within 8
+    x += dpp_mov<0x140>(x);   // row_mirror: lane i <- 15 - i within 16
+    return x;
+}
+
+// Vector LDS stores of 8 consecutive / 4 consecutive elements in the math
+// type (bf16: one 16-byte / 8-byte store; fp32: two / one 16-byte stores).
+__device__ __forceinline__ void st8(bf16* p, const float* y) {
+    bf16x8 v;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = static_cast<bf16>(y[e]);
+    *reinterpret_cast<bf16x8*>(p) = v;
+}
+__device__ __forceinline__ void st8(float* p, const float* y) {
+    *reinterpret_cast<f32x4*>(p) = f32x4{y[0], y[1], y[2], y[3]};
+    *reinterpret_cast<f32x4*>(p + 4) = f32x4{y[4], y[5], y[6], y[7]};
+}
+__device__ __forceinline__ void st4(bf16* p, float a, float b, float c, float d) {
+    *reinterpret_cast<bf16x4*>(p) = bf16x4{static_cast<bf16>(a), static_cast<bf16>(b),
+                                           static_cast<bf16>(c), static_cast<bf16>(d)};
+}
+__device__ __forceinline__ void st4(float* p, float a, float b, float c, float d) {
+    *reinterpret_cast<f32x4*>(p) = f32x4{a, b, c, d};
+}
+
 // ---------------------------------------------------------------------------
 // MFMA fragment conventions (wave64, 16x16 output tiles)
 //

@@ -110,13 +110,30 @@ struct PrepSmem {
     float bg[kChunk];                      // beta * exp(G)
 };
 
-__device__ __forceinline__ float reduce16(float x) {
-    x += __shfl_xor(x, 1);
-    x += __shfl_xor(x, 2);
-    x += __shfl_xor(x, 4);
-    x += __shfl_xor(x, 8);
-    return x;
-}
+// Raw rows of 8 channels for 4 consecutive tokens and the 3 before them.
+// src is [T][heads][128]; col = head * 128 + 8 cg; chan = the conv channel
+// of the first of the 8 columns.  Rows before the sequence start come from
+// the conv state (or are zero); rows past the chunk's last valid token are
+// not read.
+// 8 raw elements as loaded (bf16 bit patterns or fp32); converted to fp32
+// only when the phase that uses them starts, so that loads can be issued one
+// phase early without holding fp32 copies in registers.
+template <class IO> struct Raw8;
+template <> struct Raw8<uint16_t> {
+    u16x8 v;
+    __device__ __forceinline__ void load(const uint16_t* p) { v = *reinterpret_cast<const u16x8*>(p); }
+    __device__ __forceinline__ void zero() { v = u16x8{0, 0, 0, 0, 0, 0, 0, 0}; }
+    __device__ __forceinline__ float at(int e) const { return bf16_bits_to_f32(v[e]); }
+};
+template <> struct Raw8<float> {
+    f32x4 a, b;
+    __device__ __forceinline__ void load(const float* p) {
+        a = *reinterpret_cast<const f32x4*>(p);
+        b = *reinterpret_cast<const f32x4*>(p + 4);
+    }
+    __device__ __forceinline__ void zero() { a = b = f32x4{0.f, 0.f, 0.f, 0.f}; }
+    __device__ __forceinline__ float at(int e) const { return e < 4 ? a[e] : b[e - 4]; }
+};
 
 // Raw rows of 8 channels for 4 consecutive tokens and the 3 before them.
 // src is [T][heads][128]; col = head * 128 + 8 cg; chan = the conv channel
@@ -125,51 +142,85 @@ __device__ __forceinline__ float reduce16(float x) {
 // not read.
 template <class IO, bool kConv>
 struct Quad {
-    float x[7][8];    // x[i]: local token tq - 3 + i
-    float w[4][8];    // w[r][e]: tap r of channel chan + e
+    Raw8<IO> xr[7];   // xr[i]: local token tq - 3 + i
+    Raw8<IO> wr[4];   // conv_w[chan .. chan + 7][0 .. 3], channel-major
+    // Chunk whose whole window lies inside the sequence (every chunk but a
+    // sequence's first and last): uniform base + 32-bit per-lane byte offsets.
+    __device__ __forceinline__ void load_inner(const IO* __restrict__ src, int heads, int col, int chan,
+                                               int t0, int tq, const IO* __restrict__ conv_w) {
+        const int first = kConv ? 0 : 3;
+        const char* base = reinterpret_cast<const char*>(src + (size_t)(t0 - 3) * heads * kD);
+        const uint32_t rs = (uint32_t)(heads * kD * sizeof(IO));
+        const uint32_t off = (uint32_t)tq * rs + (uint32_t)col * sizeof(IO);
+#pragma unroll
+        for (int i = first; i < 7; ++i) xr[i].load(reinterpret_cast<const IO*>(base + (off + i * rs)));
+    }
+    // conv weights of channels chan .. chan + 7 (small and cache resident:
+    // loaded when used rather than prefetched with the rows)
+    __device__ __forceinline__ void load_w(const IO* __restrict__ conv_w, int chan) {
+        if (kConv) {
+            const char* wb = reinterpret_cast<const char*>(conv_w);
+            const uint32_t wo = (uint32_t)chan * (kConvK * sizeof(IO));
+#pragma unroll
+            for (int h4 = 0; h4 < 4; ++h4)
+                wr[h4].load(reinterpret_cast<const IO*>(wb + (wo + 8 * h4 * sizeof(IO))));
+        }
+    }
+    // Any chunk: rows before the sequence start come from the conv state;
+    // addresses are still a uniform base + 32-bit per-lane byte offsets.
     __device__ __forceinline__ void load(const IO* __restrict__ src, int heads, int col, int chan,
                                          int t0, int tq, int len, int seq_start, int n, int Cch,
                                          const IO* __restrict__ conv_w,
                                          const IO* __restrict__ csin) {
         const int first = kConv ? 0 : 3;
+        // row t0 - 3 + r of src at base + r * rs; only rows inside the
+        // sequence (r >= 0 relative to it) are read
+        const char* base = reinterpret_cast<const char*>(src) + ((int64_t)(t0 - 3) * heads * kD) * (int64_t)sizeof(IO);
+        const uint32_t rs = (uint32_t)(heads * kD * sizeof(IO));
+        const uint32_t off = (uint32_t)tq * rs + (uint32_t)col * sizeof(IO);
+        const char* cbase = reinterpret_cast<const char*>(csin + (csin ? (size_t)n * (kConvK - 1) * Cch : 0));
 #pragma unroll
         for (int i = first; i < 7; ++i) {
             const int lt = tq - 3 + i;           // local token
             const int ts = t0 + lt;              // absolute token
-            if (lt < len && ts >= seq_start) {
-                load8(src + (size_t)ts * heads * kD + col, x[i]);
-            } else if (lt < len && csin != nullptr) {
-                load8(csin + ((size_t)n * (kConvK - 1) + (kConvK - 1 + ts - seq_start)) * Cch + chan, x[i]);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) x[i][e] = 0.f;
-            }
-        }
-        if (kConv) {
-            float raw[32];
-#pragma unroll
-            for (int h4 = 0; h4 < 4; ++h4) load8(conv_w + (size_t)chan * kConvK + 8 * h4, raw + 8 * h4);
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) w[r][e] = raw[e * 4 + r];
+            if (lt < len && ts >= seq_start)
+                xr[i].load(reinterpret_cast<const IO*>(base + (off + i * rs)));
+            else if (lt < len && csin != nullptr)
+                xr[i].load(reinterpret_cast<const IO*>(
+                    cbase + (uint32_t)(((kConvK - 1) + ts - seq_start) * Cch + chan) * sizeof(IO)));
+            else
+                xr[i].zero();
         }
     }
-    // conv + SiLU of token tq + tt (or the raw token without conv)
-    __device__ __forceinline__ void out(int tt, float* y) const {
+    // fp32 copies: x[i][e] = row i, channel e; w[r][e] = tap r of channel e
+    __device__ __forceinline__ void unpack(float (&x)[7][8], float (&w)[4][8]) const {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            if (kConv) {
-                float acc = 0.f;
+        for (int i = kConv ? 0 : 3; i < 7; ++i)
 #pragma unroll
-                for (int r = 0; r < kConvK; ++r) acc = fmaf(w[r][e], x[tt + r][e], acc);
-                y[e] = silu_f32(acc);
-            } else {
-                y[e] = x[tt + 3][e];
-            }
+            for (int e = 0; e < 8; ++e) x[i][e] = xr[i].at(e);
+        if (kConv) {
+#pragma unroll
+            for (int i = 0; i < 32; ++i) w[i & 3][i >> 2] = wr[i >> 3].at(i & 7);
         }
     }
 };
+
+// conv + SiLU of local token tq + tt from unpacked rows (or the raw token
+// without conv)
+template <bool kConv>
+__device__ __forceinline__ void conv_out(const float (&x)[7][8], const float (&w)[4][8], int tt, float* y) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        if (kConv) {
+            float acc = 0.f;
+#pragma unroll
+            for (int r = 0; r < kConvK; ++r) acc = fmaf(w[r][e], x[tt + r][e], acc);
+            y[e] = silu_f32(acc);
+        } else {
+            y[e] = x[tt + 3][e];
+        }
+    }
+}
 
 // acc = X(16x16, LDS rows ldx) * Y(16x16, LDS rows ldy) in fp32 MFMA, K split
 // as k = 4 g + s over the four 16x16x4 instructions s.
@@ -216,43 +267,60 @@ __global__ __launch_bounds__(256, 2) void gdn_chunk_prep_kernel(PrepArgs a) {
     const IO* csin = static_cast<const IO*>(a.conv_state_in);
 
     // ---- 1. q and k: conv + SiLU, L2 normalisation, scale ----
+    const int h0 = hk * group;
+    // v rows are prefetched one phase early on interior chunks (bf16 rows:
+    // the fp32 layer keeps its registers for the math instead)
+    const bool inner = sizeof(IO) == 2 && t0 - 3 >= seq_start && len == kChunk;   // uniform
+    Quad<IO, kConv> xv;        // raw v rows of the next value head
+    float gl = 0.f, bl = 0.f;  // its g and beta (wave 0, lane = token)
     {
         Quad<IO, kConv> xq, xk;
         xq.load(q, Hk, hk * kD + 8 * cg, hk * kD + 8 * cg, t0, tq, len, seq_start, n, Cch, conv_w, csin);
         xk.load(k, Hk, hk * kD + 8 * cg, Hk * kD + hk * kD + 8 * cg, t0, tq, len, seq_start, n, Cch,
                 conv_w, csin);
+        xq.load_w(conv_w, hk * kD + 8 * cg);
+        xk.load_w(conv_w, Hk * kD + hk * kD + 8 * cg);
+        // one tensor at a time (q, then k): the L2 norms are independent and
+        // only one set of fp32 rows is live
+        float xf[7][8], wf[4][8];
+        xq.unpack(xf, wf);
+        // v and gates of the first value head: in flight during phases 1 and 2
+        // (edge chunks load v when they use it)
+        if (inner) xv.load_inner(v, Hv, h0 * kD + 8 * cg, 2 * Hk * kD + h0 * kD + 8 * cg, t0, tq, conv_w);
+        if (wave == 0 && lane < len) {
+            gl = a.g[(size_t)(t0 + lane) * Hv + h0];
+            bl = a.beta[(size_t)(t0 + lane) * Hv + h0];
+        }
+        // conv + SiLU, L2 normalisation over the 128 channels of token t (the
+        // 16 lanes of a DPP row), zero for padding tokens
+        auto finish = [&](int tt, float mul, float (&y)[8]) {
+            conv_out<kConv>(xf, wf, tt, y);
+            float r = mul;
+            if (a.use_l2) {
+                float ss = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ss = fmaf(y[e], y[e], ss);
+                r *= rsqrt_f32(row16_sum(ss) + a.l2_eps);
+            }
+            if (tq + tt >= len) r = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] *= r;
+        };
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
-            const int t = tq + tt;
-            float yq[8], yk[8];
-            xq.out(tt, yq);
-            xk.out(tt, yk);
-            if (a.use_l2) {
-                float sq = 0.f, sk = 0.f;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    sq = fmaf(yq[e], yq[e], sq);
-                    sk = fmaf(yk[e], yk[e], sk);
-                }
-                sq = reduce16(sq);
-                sk = reduce16(sk);
-                const float rq = rsqrt_f32(sq + a.l2_eps), rk = rsqrt_f32(sk + a.l2_eps);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    yq[e] *= rq;
-                    yk[e] *= rk;
-                }
-            }
-            const bool valid = t < len;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                yq[e] = valid ? yq[e] * a.scale : 0.f;
-                yk[e] = valid ? yk[e] : 0.f;
-                sm.qa.q[t][8 * cg + e] = static_cast<MT>(yq[e]);
-                sm.ka.k[t][8 * cg + e] = static_cast<MT>(yk[e]);
-                sm.kt[8 * cg + e][t] = static_cast<MT>(yk[e]);
-            }
+            float y[8];
+            finish(tt, a.scale, y);
+            st8(&sm.qa.q[tq + tt][8 * cg], y);
         }
+        xk.unpack(xf, wf);
+        float yk4[4][8];   // k of the four tokens, for the transposed store
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            finish(tt, 1.0f, yk4[tt]);
+            st8(&sm.ka.k[tq + tt][8 * cg], yk4[tt]);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) st4(&sm.kt[8 * cg + e][tq], yk4[0][e], yk4[1][e], yk4[2][e], yk4[3][e]);
     }
     __syncthreads();
 
@@ -313,26 +381,39 @@ __global__ __launch_bounds__(256, 2) void gdn_chunk_prep_kernel(PrepArgs a) {
         F* VB = static_cast<F*>(a.VB) + cv * kVBUnits * 64 + lane;
         float* gates = reinterpret_cast<float*>(static_cast<F*>(a.VB) + (cv * kVBUnits + kVB_G) * 64);
 
-        // 3a. v: conv + SiLU, transposed into LDS; gates
+        // 3a. v: conv + SiLU, transposed into LDS; gates.  The next value
+        //     head's v rows and gates are loaded here, for its own 3a.
         {
-            Quad<IO, kConv> xv;
-            xv.load(v, Hv, h * kD + 8 * cg, 2 * Hk * kD + h * kD + 8 * cg, t0, tq, len, seq_start, n,
-                    Cch, conv_w, csin);
-            float gl = 0.f, bl = 0.f;
-            if (wave == 0 && lane < len) {
-                gl = a.g[(size_t)(t0 + lane) * Hv + h];
-                bl = a.beta[(size_t)(t0 + lane) * Hv + h];
+            float y[4][8];
+            {
+                if (!inner)
+                    xv.load(v, Hv, h * kD + 8 * cg, 2 * Hk * kD + h * kD + 8 * cg, t0, tq, len, seq_start,
+                            n, Cch, conv_w, csin);
+                xv.load_w(conv_w, 2 * Hk * kD + h * kD + 8 * cg);
+                float xf[7][8], wf[4][8];
+                xv.unpack(xf, wf);
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) {
+                    conv_out<kConv>(xf, wf, tt, y[tt]);
+                    const bool valid = tq + tt < len;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) y[tt][e] = valid ? y[tt][e] : 0.f;
+                }
+            }
+            const float gcur = gl, bcur = bl;
+            if (vh + 1 < group) {
+                if (inner)
+                    xv.load_inner(v, Hv, (h + 1) * kD + 8 * cg, 2 * Hk * kD + (h + 1) * kD + 8 * cg, t0,
+                                  tq, conv_w);
+                if (wave == 0 && lane < len) {
+                    gl = a.g[(size_t)(t0 + lane) * Hv + h + 1];
+                    bl = a.beta[(size_t)(t0 + lane) * Hv + h + 1];
+                }
             }
 #pragma unroll
-            for (int tt = 0; tt < 4; ++tt) {
-                float y[8];
-                xv.out(tt, y);
-                const bool valid = tq + tt < len;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) sm.vt[8 * cg + e][tq + tt] = static_cast<MT>(valid ? y[e] : 0.f);
-            }
+            for (int e = 0; e < 8; ++e) st4(&sm.vt[8 * cg + e][tq], y[0][e], y[1][e], y[2][e], y[3][e]);
             if (wave == 0) {   // G = inclusive cumsum of g over the chunk (padding: g = b = 0)
-                float G = gl;
+                float G = gcur;
 #pragma unroll
                 for (int off = 1; off < 64; off <<= 1) {
                     const float x = __shfl_up(G, off);
@@ -341,8 +422,8 @@ __global__ __launch_bounds__(256, 2) void gdn_chunk_prep_kernel(PrepArgs a) {
                 const float Gn = __shfl(G, 63);
                 const float gam = exp_f32(G);
                 sm.G[lane] = G;
-                sm.b[lane] = bl;
-                sm.bg[lane] = bl * gam;
+                sm.b[lane] = bcur;
+                sm.bg[lane] = bcur * gam;
                 gates[lane] = gam;
                 gates[64 + lane] = exp_f32(Gn - G);
             }
@@ -817,7 +898,7 @@ __global__ __launch_bounds__(256) void gdn_gated_norm_kernel(IO* __restrict__ ou
         float ss = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
-        ss = reduce16(ss);
+        ss = row16_sum(ss);   // the 16 lanes of a DPP row hold one row
         const float r = rsqrt_f32(ss * (1.0f / kD) + eps);
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[e] = x[e] * r * w[e] * silu_f32(zz[e]);
