@@ -705,53 +705,46 @@ __device__ __forceinline__ void store_o(IO* out, const f32x4 (&O)[4], int t0, in
         }
 }
 
-// Copies of chunk c's operands into an LDS buffer: three contiguous unit
-// ranges; wave w of SW issues units w, w + SW, ... of the shared ranges and
-// the 2 NT U~ units of its own tiles.  Addresses are a uniform base plus a
-// 32-bit per-lane byte offset (the scalar-base form of the copy instruction).
-template <int SW, int NT>
-__device__ __forceinline__ void sweep_issue(const SweepArgs& a, size_t ck, size_t cv, int sg,
-                                            int wave, int lane, lds_b16x8* __restrict__ buf) {
+// Copies of chunk c's operands into an LDS buffer, issued by the PW
+// producer waves of the workgroup.  LDS unit u (1 KB) receives KB unit u
+// (u < 32), VB unit u - 32 (u < 56) or U~ unit u - 56 of the workgroup's
+// tiles; producer p copies units p, p + PW, ...  Addresses are a uniform base
+// plus a 32-bit per-lane byte offset (the scalar-base form of the copy).
+template <int SW, int NT, int PW>
+__device__ __forceinline__ void sweep_issue(const SweepArgs& a, size_t ck, size_t cv, int sg, int p,
+                                            int lane, lds_b16x8* __restrict__ buf) {
+    constexpr int kUnits = SweepLds<SW, NT>::kUnits;
+    static_assert(kLdsW % PW == 0 && kLdsU % PW == 0 && kUnits % PW == 0, "unit ranges split evenly");
     const char* kb = static_cast<const char*>(a.KB) + ck * kKBUnits * 1024;
     const char* vb = static_cast<const char*>(a.VB) + cv * kVBUnits * 1024;
     const char* ub = vb + (kVB_U + 2 * SW * NT * sg) * 1024;
-    const uint32_t lo = (uint32_t)lane * 16u + (uint32_t)wave * 1024u;
+    const uint32_t lo = (uint32_t)lane * 16u + (uint32_t)p * 1024u;
 #pragma unroll
-    for (int i = 0; i < kKBUnits / SW; ++i)
-        __builtin_amdgcn_global_load_lds(kb + (lo + i * SW * 1024u), buf + (i * SW + wave) * 64, 16, 0, 0);
-#pragma unroll
-    for (int i = 0; i < kVB_U / SW; ++i)
-        __builtin_amdgcn_global_load_lds(vb + (lo + i * SW * 1024u), buf + (kLdsW + i * SW + wave) * 64, 16, 0, 0);
-    const uint32_t lu = (uint32_t)lane * 16u + (uint32_t)wave * (2048u * NT);
-#pragma unroll
-    for (int i = 0; i < 2 * NT; ++i)
-        __builtin_amdgcn_global_load_lds(ub + (lu + i * 1024u), buf + (kLdsU + 2 * NT * wave + i) * 64, 16, 0, 0);
+    for (int i = 0; i < kUnits / PW; ++i) {
+        const int u0 = i * PW;
+        const char* src = u0 < kLdsW ? kb + u0 * 1024 : u0 < kLdsU ? vb + (u0 - kLdsW) * 1024
+                                                                   : ub + (u0 - kLdsU) * 1024;
+        __builtin_amdgcn_global_load_lds(src + lo, buf + (u0 + p) * 64, 16, 0, 0);
+    }
 }
 
-// One chunk: wait for its operands, start copying the next chunk's into the
-// other buffer, compute.  cur / nxt are distinct buffers (__restrict__), so
-// the compiler adds no waits of its own; the explicit one below orders them.
-// The previous chunk's output (Oprev) is stored here, after the wait, so its
-// stores complete behind this chunk's work instead of delaying the next wait.
+// One chunk of a compute wave: wait until the producers' copies of its
+// operands have landed (their wait + the barrier), compute from cur.  The
+// previous chunk's output (Oprev) is stored after the barrier, so its stores
+// complete behind this chunk's work.
 template <int SW, int NT>
 __device__ __forceinline__ void sweep_lds_step(const SweepArgs& a, const SweepSeq& q, int j, int h,
-                                               int hk, int sg, int wave, f32x4 (&S)[NT][8],
-                                               f32x4 (&Oprev)[NT][4], lds_b16x8* __restrict__ cur,
-                                               lds_b16x8* __restrict__ nxt) {
+                                               int sg, int wave, f32x4 (&S)[NT][8],
+                                               f32x4 (&Oprev)[NT][4], const lds_b16x8* __restrict__ cur) {
     const int lane = threadIdx.x & 63, l16 = lane & 15, g4 = lane >> 4;
     const int s0 = (sg * SW + wave) * NT;   // first tile of this wave
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copies into cur have landed
-    __syncthreads();                      // every wave's have; nobody still reads nxt
+    __syncthreads();                      // chunk j's operands are in cur; nxt is free
     asm volatile("" ::: "memory");
     if (j > 0) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
             store_o(static_cast<uint16_t*>(a.out), Oprev[nt], q.seq_start + (j - 1) * kChunk, kChunk,
                     a.Hv, h, s0 + nt, l16, g4);
-    }
-    if (j + 1 < q.nch) {
-        const size_t c1 = (size_t)q.c_begin + j + 1;
-        sweep_issue<SW, NT>(a, c1 * a.Hk + hk, c1 * a.Hv + h, sg, wave, lane, nxt);
     }
     const lds_b16x8* W = cur + kLdsW * 64 + lane;
     const lds_b16x8* Q = cur + kLdsQ * 64 + lane;
@@ -776,8 +769,14 @@ __device__ __forceinline__ void sweep_lds_step(const SweepArgs& a, const SweepSe
         G[63]);
 }
 
-template <int SW, int NT>
-__global__ __launch_bounds__(64 * SW) void gdn_state_sweep_lds_kernel(SweepArgs a) {
+// Workgroup = SW compute waves (NT state tiles each) + PW producer waves.
+// Each chunk step has one barrier: producers wait for their copies into the
+// current buffer, everyone meets at the barrier, then producers copy the next
+// chunk into the other buffer while the compute waves work on this one.  The
+// compute waves never issue a copy, so copy issue never stalls the chain of
+// state updates.
+template <int SW, int NT, int PW>
+__global__ __launch_bounds__(64 * (SW + PW)) void gdn_state_sweep_lds_kernel(SweepArgs a) {
     typedef SweepLds<SW, NT> L;
     extern __shared__ __attribute__((aligned(16))) unsigned char gdn_sweep_smem[];
     lds_b16x8* buf0 = (lds_b16x8*)(gdn_sweep_smem);   // generic -> LDS address space
@@ -790,9 +789,23 @@ __global__ __launch_bounds__(64 * SW) void gdn_state_sweep_lds_kernel(SweepArgs 
     // the wave index is uniform; readfirstlane lets the compiler keep it in an SGPR
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63, l16 = lane & 15, g4 = lane >> 4;
-    const int s0 = (sg * SW + wave) * NT;
     const SweepSeq q = sweep_seq(a, n);
 
+    if (wave >= SW) {   // producer
+        const int p = wave - SW;
+        for (int j = 0; j < q.nch; ++j) {
+            const size_t c = (size_t)q.c_begin + j;
+            sweep_issue<SW, NT, PW>(a, c * a.Hk + hk, c * a.Hv + h, sg, p, lane, (j & 1) ? buf1 : buf0);
+            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): these copies have landed
+            __syncthreads();                      // consumers may read buffer j & 1
+            asm volatile("" ::: "memory");
+            // the next issue overwrites the other buffer, which the compute
+            // waves finished with before this barrier
+        }
+        return;
+    }
+
+    const int s0 = (sg * SW + wave) * NT;
     f32x4 S[NT][8];
     const size_t hrow = ((size_t)n * a.Hv + h) * kD;
 #pragma unroll
@@ -805,14 +818,11 @@ __global__ __launch_bounds__(64 * SW) void gdn_state_sweep_lds_kernel(SweepArgs 
                            : f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    if (q.nch > 0)
-        sweep_issue<SW, NT>(a, (size_t)q.c_begin * a.Hk + hk, (size_t)q.c_begin * a.Hv + h, sg, wave,
-                            lane, buf0);
     f32x4 O[NT][4];
 #pragma unroll 1
     for (int j = 0; j < q.nch; j += 2) {
-        sweep_lds_step<SW, NT>(a, q, j, h, hk, sg, wave, S, O, buf0, buf1);
-        if (j + 1 < q.nch) sweep_lds_step<SW, NT>(a, q, j + 1, h, hk, sg, wave, S, O, buf1, buf0);
+        sweep_lds_step<SW, NT>(a, q, j, h, sg, wave, S, O, buf0);
+        if (j + 1 < q.nch) sweep_lds_step<SW, NT>(a, q, j + 1, h, sg, wave, S, O, buf1);
     }
     if (q.nch > 0) {   // output of the last chunk
 #pragma unroll
@@ -945,7 +955,7 @@ __global__ __launch_bounds__(256) void gdn_conv_state_kernel(ConvStateArgs a) {
 // ===========================================================================
 // bf16 sweep: 4 waves x 2 tiles = one head per workgroup (one copy of the
 // chunk operands per head and chunk; each LDS fragment feeds two MFMAs).
-constexpr int kSweepSW = 4, kSweepNT = 1;
+constexpr int kSweepSW = 4, kSweepNT = 1, kSweepPW = 4;
 typedef SweepLds<kSweepSW, kSweepNT> SweepCfg;
 
 // Dynamic LDS above 64 KB must be allowed per kernel; done once per kernel.
@@ -963,7 +973,7 @@ static hipError_t allow_dynamic_lds(const void* kern, unsigned bytes) {
         reinterpret_cast<const void*>(gdn_chunk_prep_kernel<float, false>),
         hipFuncAttributeMaxDynamicSharedMemorySize, sizeof(PrepSmem<float>));
     static const hipError_t sweep = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(gdn_state_sweep_lds_kernel<kSweepSW, kSweepNT>),
+        reinterpret_cast<const void*>(gdn_state_sweep_lds_kernel<kSweepSW, kSweepNT, kSweepPW>),
         hipFuncAttributeMaxDynamicSharedMemorySize, SweepCfg::kBytes);
     (void)kern;
     (void)bytes;
@@ -999,8 +1009,8 @@ static hipError_t launch_all(const PrefillPlan& p, hipStream_t stream, StageReco
             hipLaunchKernelGGL(gdn_state_sweep_f32_kernel, dim3(unit_blocks * 8), dim3(64), 0, stream,
                                p.sweep);
         } else {
-            hipLaunchKernelGGL((gdn_state_sweep_lds_kernel<kSweepSW, kSweepNT>),
-                               dim3(unit_blocks * SweepCfg::kGroups), dim3(64 * kSweepSW),
+            hipLaunchKernelGGL((gdn_state_sweep_lds_kernel<kSweepSW, kSweepNT, kSweepPW>),
+                               dim3(unit_blocks * SweepCfg::kGroups), dim3(64 * (kSweepSW + kSweepPW)),
                                SweepCfg::kBytes, stream, p.sweep);
         }
         if ((e = hipGetLastError()) != hipSuccess) return e;
