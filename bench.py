@@ -120,7 +120,7 @@ def bench_prefill(args, hip):
     base = PrefillCall(x, Hk=p.Hk, Hv=p.Hv, io_bf16=True)
     sets = [base] + [clone_call(base) for _ in range(args.buffer_sets - 1)]
     stream = torch.cuda.current_stream().cuda_stream
-    nev = 7
+    nev = 2 + 2 * 48   # call brackets + begin/end of up to 48 kernels
     log(f"[bench] warmup {args.warmup} steps")
     warm_ev = [hip.event() for _ in range(nev)]
     for i in range(args.warmup):
@@ -138,13 +138,18 @@ def bench_prefill(args, hip):
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
 
-    ns = len(stage_ids)
+    # kernel i ran between ev[2 + 2i] and ev[3 + 2i] on its own stream; a
+    # stage's time is the sum over its launches (launches of different
+    # stages overlap when the call is split into chunk segments)
     stage_ms = {STAGE_NAMES[s]: 0.0 for s in stage_ids}
+    launches = {STAGE_NAMES[s]: 0 for s in stage_ids}
+    for s in stage_ids:
+        launches[STAGE_NAMES[s]] += 1
     gpu_ms = 0.0
     for ev in events:
         for j, s in enumerate(stage_ids):
-            stage_ms[STAGE_NAMES[s]] += hip.ms(ev[j], ev[j + 1]) / args.steps
-        gpu_ms += hip.ms(ev[0], ev[ns]) / args.steps
+            stage_ms[STAGE_NAMES[s]] += hip.ms(ev[2 + 2 * j], ev[3 + 2 * j]) / args.steps
+        gpu_ms += hip.ms(ev[0], ev[1]) / args.steps
     for ev in events + [warm_ev]:
         for e in ev:
             hip.destroy(e)
@@ -162,9 +167,13 @@ def bench_prefill(args, hip):
         achieved, peak, unit, bound = 3 * T * Hv * D * 2 / dom_s, HBM_PEAK, "GB/s", "hbm"
     scale = 1e12 if unit == "TFLOP/s" else 1e9
     traffic = measured_traffic(dominant)
+    nl = launches[dominant]
     roof = {"bound": bound, "achieved": round(achieved / scale, 2), "peak": peak / scale,
-            "unit": unit, "frac": round(achieved / peak, 4), "traffic": traffic,
-            "kernel": dominant, "kernel_us": round(stage_ms[dominant] * 1e3, 2)}
+            "unit": unit, "frac": round(achieved / peak, 4),
+            "traffic": traffic,   # HBM bytes per launch (counter summary average)
+            "kernel": dominant, "launches_per_step": nl,
+            "kernel_us_per_launch": round(stage_ms[dominant] * 1e3 / nl, 2),
+            "kernel_us_per_step": round(stage_ms[dominant] * 1e3, 2)}
     path = {"gpu_us_per_step": round(gpu_ms * 1e3, 2),
             "hbm_algorithmic_bytes": io_bytes,
             "hbm_frac": round(io_bytes / (gpu_ms * 1e-3) / HBM_PEAK, 4),

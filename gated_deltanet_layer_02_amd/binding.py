@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(_PKG, "libgdn.so")
 GDN_OK = 0
 GDN_F32, GDN_BF16 = 0, 1
 GDN_FLAG_L2NORM_QK = 0x1
-GDN_PREFILL_MAX_STAGES = 6
+PREFILL_MAX_KERNELS = 64   # kernels a profiled call may record (the caller's choice)
 STAGE_NAMES = {0: "chunk_table", 1: "chunk_prep", 2: "state_sweep", 3: "gated_norm",
                4: "conv_state"}
 
@@ -85,7 +85,7 @@ def lib():
         l.gdn_prefill.restype = ctypes.c_int
         l.gdn_prefill.argtypes = [dp] + [vp] * 14 + [vp, sz, vp]
         l.gdn_prefill_profiled.restype = ctypes.c_int
-        l.gdn_prefill_profiled.argtypes = [dp] + [vp] * 14 + [vp, sz, vp, vp, vp, vp]
+        l.gdn_prefill_profiled.argtypes = [dp] + [vp] * 14 + [vp, sz, vp, vp, i32, vp, vp]
         l.gdn_decode.restype = ctypes.c_int
         l.gdn_decode.argtypes = [dp] + [vp] * 11 + [i32, vp, vp]
         _lib = l
@@ -155,15 +155,20 @@ def gdn_prefill_profiled(desc: Desc, q, k, v, g, beta, *, events: Sequence[int],
                          conv_w=None, norm_w=None, cu_seqlens=None, initial_state=None,
                          conv_state_in=None, out=None, final_state=None, conv_state_out=None,
                          workspace=None, stream=None):
-    """Returns the stage ids recorded between events[i] and events[i+1]."""
-    ev = (ctypes.c_void_p * (GDN_PREFILL_MAX_STAGES + 1))(*events)
+    """events: 2 + 2 m event handles.  Returns the stage id of every kernel i,
+    which ran between events[2 + 2 i] and events[3 + 2 i]; events[0] and
+    events[1] bracket the whole call on `stream`."""
+    m = (len(events) - 2) // 2
+    if m < 1:
+        raise ValueError("need 2 + 2 m events, m >= 1")
+    ev = (ctypes.c_void_p * len(events))(*events)
     ns = ctypes.c_int32(0)
-    ids = (ctypes.c_int32 * GDN_PREFILL_MAX_STAGES)()
+    ids = (ctypes.c_int32 * m)()
     rc = lib().gdn_prefill_profiled(ctypes.byref(desc), _p(q), _p(k), _p(v), _p(g), _p(beta),
                                     _p(z), _p(conv_w), _p(norm_w), _p(cu_seqlens),
                                     _p(initial_state), _p(conv_state_in), _p(out),
                                     _p(final_state), _p(conv_state_out), _ws_ptr(workspace),
-                                    _ws_bytes(workspace), _stream(stream), ev,
+                                    _ws_bytes(workspace), _stream(stream), ev, m,
                                     ctypes.byref(ns), ids)
     if rc != GDN_OK:
         raise GdnError(rc, "gdn_prefill_profiled")

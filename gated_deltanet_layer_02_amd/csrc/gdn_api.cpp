@@ -71,8 +71,8 @@ gdn_status prefill_impl(const gdn_desc* d, const void* q, const void* k, const v
                         const void* norm_w, const int32_t* cu_seqlens, const float* initial_state,
                         const void* conv_state_in, void* out, float* final_state,
                         void* conv_state_out, void* workspace, size_t workspace_bytes,
-                        hipStream_t stream, hipEvent_t* events, int32_t* num_stages,
-                        int32_t* stage_ids) {
+                        hipStream_t stream, hipEvent_t* events, int32_t max_kernels,
+                        int32_t* num_kernels, int32_t* stage_ids) {
     gdn_status st = check_desc_common(d);
     if (st != GDN_OK) return st;
     if (d->state_dtype != GDN_F32) return GDN_ERR_BAD_DTYPE;
@@ -82,7 +82,8 @@ gdn_status prefill_impl(const gdn_desc* d, const void* q, const void* k, const v
     if (T > 0 && (z == nullptr) != (norm_w == nullptr)) return GDN_ERR_NULL_ARG;
     if (cu_seqlens == nullptr && N != 1) return GDN_ERR_NULL_ARG;
     if (workspace == nullptr && workspace_bytes > 0) return GDN_ERR_WORKSPACE;
-    if (events != nullptr && num_stages == nullptr) return GDN_ERR_NULL_ARG;
+    if (events != nullptr && (num_kernels == nullptr || stage_ids == nullptr)) return GDN_ERR_NULL_ARG;
+    if (events != nullptr && max_kernels < 1) return GDN_ERR_BAD_VALUE;
     const void* tensors[] = {q, k, v, g, beta, z, conv_w, norm_w, cu_seqlens, initial_state,
                              conv_state_in, out, final_state, conv_state_out};
     for (const void* p : tensors)
@@ -139,11 +140,12 @@ gdn_status prefill_impl(const gdn_desc* d, const void* q, const void* k, const v
     c.q = q; c.k = k; c.v = v; c.conv_state_in = conv_state_in; c.conv_state_out = conv_state_out;
     c.cu = cu_seqlens; c.T = a.T; c.N = a.N; c.Hk = a.Hk; c.Hv = a.Hv;
 
-    gdn::StageRecorder rec;
+    gdn::KernelRecorder rec;
     rec.events = events;
     rec.ids = stage_ids;
+    rec.max = max_kernels;
     const hipError_t e = gdn::launch_prefill(p, stream, rec);
-    if (num_stages) *num_stages = rec.count;
+    if (num_kernels) *num_kernels = rec.count;
     return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
@@ -184,7 +186,7 @@ gdn_status gdn_prefill(const gdn_desc* d, const void* q, const void* k, const vo
                        hipStream_t stream) {
     return prefill_impl(d, q, k, v, g, beta, z, conv_w, norm_w, cu_seqlens, initial_state,
                         conv_state_in, out, final_state, conv_state_out, workspace, workspace_bytes,
-                        stream, nullptr, nullptr, nullptr);
+                        stream, nullptr, 0, nullptr, nullptr);
 }
 
 gdn_status gdn_prefill_profiled(const gdn_desc* d, const void* q, const void* k, const void* v,
@@ -193,11 +195,11 @@ gdn_status gdn_prefill_profiled(const gdn_desc* d, const void* q, const void* k,
                                 const float* initial_state, const void* conv_state_in, void* out,
                                 float* final_state, void* conv_state_out, void* workspace,
                                 size_t workspace_bytes, hipStream_t stream, hipEvent_t* events,
-                                int32_t* num_stages, int32_t* stage_ids) {
-    if (events == nullptr || num_stages == nullptr) return GDN_ERR_NULL_ARG;
+                                int32_t max_kernels, int32_t* num_kernels, int32_t* stage_ids) {
+    if (events == nullptr || num_kernels == nullptr || stage_ids == nullptr) return GDN_ERR_NULL_ARG;
     return prefill_impl(d, q, k, v, g, beta, z, conv_w, norm_w, cu_seqlens, initial_state,
                         conv_state_in, out, final_state, conv_state_out, workspace, workspace_bytes,
-                        stream, events, num_stages, stage_ids);
+                        stream, events, max_kernels, num_kernels, stage_ids);
 }
 
 gdn_status gdn_decode(const gdn_desc* d, const void* q, const void* k, const void* v,

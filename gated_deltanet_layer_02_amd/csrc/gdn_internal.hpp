@@ -81,25 +81,28 @@ struct DecodeArgs {
     float scale, l2_eps, norm_eps;
 };
 
-// Records an event before every kernel and after the last one when the
-// caller asked for per-stage timing.
-struct StageRecorder {
+// Per-kernel timing when the caller asked for it: events[0] / events[1] on
+// the caller's stream at the start and end of the call, events[2 + 2 i] /
+// events[3 + 2 i] around kernel i on the stream it is launched on.
+struct KernelRecorder {
     hipEvent_t* events = nullptr;
     int32_t* ids = nullptr;
-    int count = 0;
+    int max = 0, count = 0;
+    hipError_t call_begin(hipStream_t s) { return events ? hipEventRecord(events[0], s) : hipSuccess; }
+    hipError_t call_end(hipStream_t s) { return events ? hipEventRecord(events[1], s) : hipSuccess; }
     hipError_t begin(int id, hipStream_t s) {
         if (!events) return hipSuccess;
-        if (count >= GDN_PREFILL_MAX_STAGES) return hipErrorInvalidValue;
+        if (count >= max) return hipErrorInvalidValue;
         if (ids) ids[count] = id;
-        return hipEventRecord(events[count++], s);
+        return hipEventRecord(events[2 + 2 * count], s);
     }
     hipError_t end(hipStream_t s) {
-        if (!events || count == 0) return hipSuccess;
-        return hipEventRecord(events[count], s);
+        if (!events) return hipSuccess;
+        return hipEventRecord(events[3 + 2 * count++], s);
     }
 };
 
-hipError_t launch_prefill(const PrefillPlan& p, hipStream_t stream, StageRecorder& rec);
+hipError_t launch_prefill(const PrefillPlan& p, hipStream_t stream, KernelRecorder& rec);
 hipError_t launch_decode(const DecodeArgs& a, bool io_bf16, bool state_bf16, bool conv,
                          hipStream_t stream);
 

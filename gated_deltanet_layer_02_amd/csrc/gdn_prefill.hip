@@ -573,12 +573,25 @@ typedef __attribute__((address_space(3))) bf16x8 lds_b16x8;
 typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
 typedef __attribute__((address_space(3))) float lds_f32;
 
-// XCD-aware mapping of blockIdx.x to (unit u = n*Hv + h, group sg): the
-// groups of one head share blockIdx.x % 8, so they run on one XCD and share
-// its L2 for the chunk operands.
-__device__ __forceinline__ void sweep_unit(int x, int groups, int& u, int& sg) {
-    u = (x / (8 * groups)) * 8 + (x & 7);
-    sg = (x >> 3) % groups;
+// XCD-aware mapping of blockIdx.x to (unit u = n*Hv + h, group sg).
+// Workgroups are dealt to the 8 XCDs round-robin (XCD = x % 8), each XCD
+// with its own L2.  Key units (n, hk) go to XCDs round-robin, and every
+// workgroup of a key unit (its R = Hv/Hk value heads x `groups` groups) to
+// that key unit's XCD, so the key head's operands (Q, K^T) and each value
+// head's are fetched into one L2 only.  Returns false past the last unit.
+__device__ __forceinline__ bool sweep_unit(int x, int groups, int N, int Hk, int Hv, int& u, int& sg) {
+    const int R = Hv / Hk, per = R * groups;
+    const int i = x >> 3;                       // slot within the XCD
+    const int ku = (i / per) * 8 + (x & 7);     // key unit n * Hk + hk
+    if (ku >= N * Hk) return false;
+    const int r = i % per;
+    sg = r % groups;
+    u = (ku / Hk) * Hv + (ku % Hk) * R + r / groups;
+    return true;
+}
+// grid size of the mapping above
+__host__ __device__ constexpr int sweep_grid(int groups, int N, int Hk, int Hv) {
+    return (N * Hk + 7) / 8 * 8 * (Hv / Hk) * groups;
 }
 
 struct SweepSeq {
@@ -783,8 +796,7 @@ __global__ __launch_bounds__(64 * (SW + PW)) void gdn_state_sweep_lds_kernel(Swe
     lds_b16x8* buf1 = buf0 + L::kUnits * 64;
 
     int u, sg;
-    sweep_unit(blockIdx.x, L::kGroups, u, sg);
-    if (u >= a.N * a.Hv) return;
+    if (!sweep_unit(blockIdx.x, L::kGroups, a.N, a.Hk, a.Hv, u, sg)) return;
     const int n = u / a.Hv, h = u % a.Hv, hk = h / (a.Hv / a.Hk);
     // the wave index is uniform; readfirstlane lets the compiler keep it in an SGPR
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -846,8 +858,7 @@ __global__ __launch_bounds__(64 * (SW + PW)) void gdn_state_sweep_lds_kernel(Swe
 __global__ __launch_bounds__(64) void gdn_state_sweep_f32_kernel(SweepArgs a) {
     typedef Frag<float> F;
     int u, sg;
-    sweep_unit(blockIdx.x, 8, u, sg);
-    if (u >= a.N * a.Hv) return;
+    if (!sweep_unit(blockIdx.x, 8, a.N, a.Hk, a.Hv, u, sg)) return;
     const int n = u / a.Hv, h = u % a.Hv, hk = h / (a.Hv / a.Hk);
     const int lane = threadIdx.x, l16 = lane & 15, g4 = lane >> 4;
     const int s = sg;
@@ -982,61 +993,109 @@ static hipError_t allow_dynamic_lds(const void* kern, unsigned bytes) {
     return hipSuccess;
 }
 
-template <class IO>
-static hipError_t launch_all(const PrefillPlan& p, hipStream_t stream, StageRecorder& rec) {
-    hipError_t e;
-    if (p.prep.cu != nullptr) {
-        if ((e = rec.begin(GDN_STAGE_CHUNK_TABLE, stream)) != hipSuccess) return e;
-        hipLaunchKernelGGL(gdn_chunk_table_kernel, dim3(1), dim3(1024), 0, stream, p.prep.cu,
-                           p.prep.N, p.prep.chunk_off);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
-    if (p.chunk_slots > 0) {
-        if ((e = rec.begin(GDN_STAGE_CHUNK_PREP, stream)) != hipSuccess) return e;
-        const dim3 grid(p.chunk_slots, p.prep.Hk);
-        typedef typename MathOf<IO>::T MT;
-        const unsigned smem = sizeof(PrepSmem<MT>);
-        auto kern = p.conv ? gdn_chunk_prep_kernel<IO, true> : gdn_chunk_prep_kernel<IO, false>;
-        if ((e = allow_dynamic_lds(reinterpret_cast<const void*>(kern), smem)) != hipSuccess) return e;
-        hipLaunchKernelGGL(kern, grid, dim3(256), smem, stream, p.prep);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
-    {
-        if ((e = rec.begin(GDN_STAGE_STATE_SWEEP, stream)) != hipSuccess) return e;
-        const int units = p.sweep.N * p.sweep.Hv;
-        const int unit_blocks = (units + 7) / 8 * 8;
-        if (!p.io_bf16) {
-            hipLaunchKernelGGL(gdn_state_sweep_f32_kernel, dim3(unit_blocks * 8), dim3(64), 0, stream,
-                               p.sweep);
-        } else {
-            hipLaunchKernelGGL((gdn_state_sweep_lds_kernel<kSweepSW, kSweepNT, kSweepPW>),
-                               dim3(unit_blocks * SweepCfg::kGroups), dim3(64 * (kSweepSW + kSweepPW)),
-                               SweepCfg::kBytes, stream, p.sweep);
-        }
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
-    if (p.gated && p.total_tokens > 0) {
-        if ((e = rec.begin(GDN_STAGE_GATED_NORM, stream)) != hipSuccess) return e;
-        const int64_t rows = p.total_tokens * p.sweep.Hv;
-        int64_t blocks = (rows + 15) / 16;
-        if (blocks > 65536) blocks = 65536;
-        hipLaunchKernelGGL(gdn_gated_norm_kernel<IO>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                           static_cast<IO*>(p.sweep.out), static_cast<const IO*>(p.z),
-                           static_cast<const IO*>(p.norm_w), rows, p.norm_eps);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
-    if (p.conv_state.conv_state_out != nullptr) {
-        if ((e = rec.begin(GDN_STAGE_CONV_STATE, stream)) != hipSuccess) return e;
-        const int Cch = 2 * p.conv_state.Hk * kD + p.conv_state.Hv * kD;
-        hipLaunchKernelGGL(gdn_conv_state_kernel<IO>, dim3((Cch + 255) / 256, p.conv_state.N),
-                           dim3(256), 0, stream, p.conv_state);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
-    return rec.end(stream);
+// ---------------------------------------------------------------------------
+// launches
+// ---------------------------------------------------------------------------
+static hipError_t launch_chunk_table(const PrefillPlan& p, hipStream_t s) {
+    hipLaunchKernelGGL(gdn_chunk_table_kernel, dim3(1), dim3(1024), 0, s, p.prep.cu, p.prep.N,
+                       p.prep.chunk_off);
+    return hipGetLastError();
 }
 
-hipError_t launch_prefill(const PrefillPlan& p, hipStream_t stream, StageRecorder& rec) {
-    return p.io_bf16 ? launch_all<uint16_t>(p, stream, rec) : launch_all<float>(p, stream, rec);
+template <class IO>
+static hipError_t launch_prep(const PrefillPlan& p, int slots, hipStream_t s) {
+    typedef typename MathOf<IO>::T MT;
+    const unsigned smem = sizeof(PrepSmem<MT>);
+    auto kern = p.conv ? gdn_chunk_prep_kernel<IO, true> : gdn_chunk_prep_kernel<IO, false>;
+    hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(kern), smem);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(slots, p.prep.Hk), dim3(256), smem, s, p.prep);
+    return hipGetLastError();
+}
+
+static int sweep_blocks(const PrefillPlan& p) {
+    const SweepArgs& a = p.sweep;
+    return sweep_grid(p.io_bf16 ? SweepCfg::kGroups : 8, a.N, a.Hk, a.Hv);
+}
+
+static hipError_t launch_sweep(const PrefillPlan& p, hipStream_t s) {
+    const SweepArgs& a = p.sweep;
+    if (!p.io_bf16) {
+        hipLaunchKernelGGL(gdn_state_sweep_f32_kernel, dim3(sweep_blocks(p)), dim3(64), 0, s, a);
+    } else {
+        hipError_t e = allow_dynamic_lds(nullptr, 0);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((gdn_state_sweep_lds_kernel<kSweepSW, kSweepNT, kSweepPW>),
+                           dim3(sweep_blocks(p)), dim3(64 * (kSweepSW + kSweepPW)), SweepCfg::kBytes, s,
+                           a);
+    }
+    return hipGetLastError();
+}
+
+// gated RMSNorm of tokens [t_lo, t_hi), all heads
+template <class IO>
+static hipError_t launch_norm(const PrefillPlan& p, int64_t t_lo, int64_t t_hi, hipStream_t s) {
+    const int64_t Hv = p.sweep.Hv;
+    const int64_t rows = (t_hi - t_lo) * Hv;
+    if (rows <= 0) return hipSuccess;
+    int64_t blocks = (rows + 15) / 16;
+    if (blocks > 65536) blocks = 65536;
+    IO* out = static_cast<IO*>(p.sweep.out) + t_lo * Hv * kD;
+    const IO* z = static_cast<const IO*>(p.z) + t_lo * Hv * kD;
+    hipLaunchKernelGGL(gdn_gated_norm_kernel<IO>, dim3((unsigned)blocks), dim3(256), 0, s, out, z,
+                       static_cast<const IO*>(p.norm_w), rows, p.norm_eps);
+    return hipGetLastError();
+}
+
+template <class IO>
+static hipError_t launch_conv_state(const PrefillPlan& p, hipStream_t s) {
+    const int Cch = 2 * p.conv_state.Hk * kD + p.conv_state.Hv * kD;
+    hipLaunchKernelGGL(gdn_conv_state_kernel<IO>, dim3((Cch + 255) / 256, p.conv_state.N), dim3(256), 0,
+                       s, p.conv_state);
+    return hipGetLastError();
+}
+
+#define GDN_TRY(x)                              \
+    do {                                        \
+        const hipError_t e_ = (x);              \
+        if (e_ != hipSuccess) return e_;        \
+    } while (0)
+
+template <class IO>
+static hipError_t run_serial(const PrefillPlan& p, hipStream_t s, KernelRecorder& rec) {
+    if (p.prep.cu != nullptr) {
+        GDN_TRY(rec.begin(GDN_STAGE_CHUNK_TABLE, s));
+        GDN_TRY(launch_chunk_table(p, s));
+        GDN_TRY(rec.end(s));
+    }
+    if (p.chunk_slots > 0) {
+        GDN_TRY(rec.begin(GDN_STAGE_CHUNK_PREP, s));
+        GDN_TRY(launch_prep<IO>(p, p.chunk_slots, s));
+        GDN_TRY(rec.end(s));
+    }
+    GDN_TRY(rec.begin(GDN_STAGE_STATE_SWEEP, s));
+    GDN_TRY(launch_sweep(p, s));
+    GDN_TRY(rec.end(s));
+    if (p.gated && p.total_tokens > 0) {
+        GDN_TRY(rec.begin(GDN_STAGE_GATED_NORM, s));
+        GDN_TRY(launch_norm<IO>(p, 0, p.total_tokens, s));
+        GDN_TRY(rec.end(s));
+    }
+    if (p.conv_state.conv_state_out != nullptr) {
+        GDN_TRY(rec.begin(GDN_STAGE_CONV_STATE, s));
+        GDN_TRY(launch_conv_state<IO>(p, s));
+        GDN_TRY(rec.end(s));
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_prefill(const PrefillPlan& p, hipStream_t stream, KernelRecorder& rec) {
+    const int n = (p.prep.cu != nullptr) + (p.chunk_slots > 0) + 1 + (p.gated && p.total_tokens > 0) +
+                  (p.conv_state.conv_state_out != nullptr);
+    if (rec.events != nullptr && n > rec.max) return hipErrorInvalidValue;
+    GDN_TRY(rec.call_begin(stream));
+    GDN_TRY(p.io_bf16 ? run_serial<uint16_t>(p, stream, rec) : run_serial<float>(p, stream, rec));
+    return rec.call_end(stream);
 }
 
 }  // namespace gdn

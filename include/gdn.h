@@ -96,8 +96,6 @@ const char* gdn_status_string(gdn_status s);
  * depends on N and T_total only through total_tokens / 64 + N chunks). */
 gdn_status gdn_prefill_workspace_size(const gdn_desc* d, size_t* bytes);
 
-/* Number of kernels gdn_prefill_profiled brackets with events (see below). */
-#define GDN_PREFILL_MAX_STAGES 6
 
 /*
  * Prefill: every token of N packed sequences.
@@ -132,11 +130,14 @@ gdn_status gdn_prefill(const gdn_desc* d,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
- * gdn_prefill with per-kernel timing: events[0..GDN_PREFILL_MAX_STAGES]
- * (caller-created hipEvent_t) are recorded on `stream` before each kernel of
- * the call and after the last one; *num_stages receives the number of kernels
- * launched (s), so events[0..s] were recorded and stage i ran between
- * events[i] and events[i+1].  stage_ids[i] (GDN_STAGE_*) names stage i.
+ * gdn_prefill with per-kernel timing.  events: 2 + 2 * max_kernels
+ * caller-created hipEvent_t.  events[0] and events[1] are recorded on
+ * `stream` at the start and at the end of the call; kernel i ran between
+ * events[2 + 2 i] and events[3 + 2 i], recorded on the stream it was
+ * launched on.  stage_ids[i] (GDN_STAGE_*, max_kernels entries) names kernel
+ * i's stage; *num_kernels receives the number of kernels.  A call that would
+ * launch more than max_kernels kernels fails with GDN_ERR_HIP before
+ * launching any.
  */
 enum {
     GDN_STAGE_CHUNK_TABLE = 0,   /* chunk offsets of the packed sequences */
@@ -153,7 +154,8 @@ gdn_status gdn_prefill_profiled(const gdn_desc* d,
                                 const float* initial_state, const void* conv_state_in,
                                 void* out, float* final_state, void* conv_state_out,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream,
-                                hipEvent_t* events, int32_t* num_stages, int32_t* stage_ids);
+                                hipEvent_t* events, int32_t max_kernels, int32_t* num_kernels,
+                                int32_t* stage_ids);
 
 /*
  * Decode: one new token for each of N sequences against cached states.

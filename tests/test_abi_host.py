@@ -118,7 +118,7 @@ def test_prefill_profiled_needs_events():
     d = B.make_desc(1, 10)
     lib = gdn.lib()
     rc = lib.gdn_prefill_profiled(ctypes.byref(d), *_ptrs(14), FAKE + 20 * STEP, 1 << 33, None,
-                                  None, None, None)
+                                  None, 8, None, None)
     assert rc == 1
 
 
