@@ -22,27 +22,34 @@ namespace gdn {
 
 // State rows are streamed once per call: nontemporal loads and stores keep
 // them from displacing anything in the caches (a read + write stream runs
-// measurably faster this way on MI355X).
-__device__ __forceinline__ void load_row8(const float* p, float* o) {
-    const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
-    const f32x4 b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p) + 1);
+// measurably faster this way on MI355X).  Lane l16 of a row's 16 lanes holds
+// 8 of its dk elements, chosen so that each load / store instruction covers
+// contiguous bytes of the row: fp32 rows (512 B) as two 256 B halves, dk =
+// 4 l16 + e and 64 + 4 l16 + e; bf16 rows (256 B) in one piece, dk = 8 l16 + e.
+__device__ __forceinline__ int row_dk(const float*, int l16, int e) {
+    return e < 4 ? 4 * l16 + e : 64 + 4 * l16 + (e - 4);
+}
+__device__ __forceinline__ int row_dk(const uint16_t*, int l16, int e) { return 8 * l16 + e; }
+__device__ __forceinline__ void load_row8(const float* row, int l16, float* o) {
+    const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row) + l16);
+    const f32x4 b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + 64) + l16);
 #pragma unroll
     for (int e = 0; e < 4; ++e) { o[e] = a[e]; o[4 + e] = b[e]; }
 }
-__device__ __forceinline__ void load_row8(const uint16_t* p, float* o) {
-    const u16x8 v = __builtin_nontemporal_load(reinterpret_cast<const u16x8*>(p));
+__device__ __forceinline__ void load_row8(const uint16_t* row, int l16, float* o) {
+    const u16x8 v = __builtin_nontemporal_load(reinterpret_cast<const u16x8*>(row) + l16);
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = bf16_bits_to_f32(v[e]);
 }
-__device__ __forceinline__ void store_row8(float* p, const float* x) {
-    __builtin_nontemporal_store(f32x4{x[0], x[1], x[2], x[3]}, reinterpret_cast<f32x4*>(p));
-    __builtin_nontemporal_store(f32x4{x[4], x[5], x[6], x[7]}, reinterpret_cast<f32x4*>(p) + 1);
+__device__ __forceinline__ void store_row8(float* row, int l16, const float* x) {
+    __builtin_nontemporal_store(f32x4{x[0], x[1], x[2], x[3]}, reinterpret_cast<f32x4*>(row) + l16);
+    __builtin_nontemporal_store(f32x4{x[4], x[5], x[6], x[7]}, reinterpret_cast<f32x4*>(row + 64) + l16);
 }
-__device__ __forceinline__ void store_row8(uint16_t* p, const float* x) {
+__device__ __forceinline__ void store_row8(uint16_t* row, int l16, const float* x) {
     u16x8 v;
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = f32_to_bf16_bits(x[e]);
-    __builtin_nontemporal_store(v, reinterpret_cast<u16x8*>(p));
+    __builtin_nontemporal_store(v, reinterpret_cast<u16x8*>(row) + l16);
 }
 
 __device__ __forceinline__ float wave_sum(float x) {
@@ -127,8 +134,9 @@ __global__ __launch_bounds__(256) void gdn_decode_kernel(DecodeArgs a) {
     float kf[8], qf[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        kf[e] = s_qk[kD + 8 * l16 + e] * rk;
-        qf[e] = s_qk[8 * l16 + e] * rq;
+        const int d = row_dk(state, l16, e);
+        kf[e] = s_qk[kD + d] * rk;
+        qf[e] = s_qk[d] * rq;
     }
     float kq = 0.f;
 #pragma unroll
@@ -150,10 +158,10 @@ __global__ __launch_bounds__(256) void gdn_decode_kernel(DecodeArgs a) {
         const float aa = exp_f32(a.g[(size_t)n * a.Hv + h]);
         const float bb = a.beta[(size_t)n * a.Hv + h];
 
-        ST* srow = state + (((size_t)slot * a.Hv + h) * kD) * kD + 8 * l16;
+        ST* srow = state + (((size_t)slot * a.Hv + h) * kD) * kD;
         float Sr[8][8];
 #pragma unroll
-        for (int p = 0; p < 8; ++p) load_row8(srow + (size_t)(rbase + 16 * p) * kD, Sr[p]);
+        for (int p = 0; p < 8; ++p) load_row8(srow + (size_t)(rbase + 16 * p) * kD, l16, Sr[p]);
         __syncthreads();   // s_v, s_zw ready
 
 #pragma unroll
@@ -171,7 +179,7 @@ __global__ __launch_bounds__(256) void gdn_decode_kernel(DecodeArgs a) {
             float nr[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) nr[e] = fmaf(aa, Sr[p][e], u * kf[e]);
-            store_row8(srow + (size_t)i * kD, nr);
+            store_row8(srow + (size_t)i * kD, l16, nr);
             if (l16 == 0) s_o[i] = fmaf(aa, dq, u * kq);
         }
         __syncthreads();   // s_o ready
