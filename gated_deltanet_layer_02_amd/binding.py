@@ -26,7 +26,7 @@ STATUS_NAMES = {0: "GDN_OK", 1: "GDN_ERR_NULL_ARG", 2: "GDN_ERR_BAD_SHAPE",
                 9: "GDN_ERR_BAD_VALUE"}
 
 EXPORTED = ["gdn_status_string", "gdn_prefill_workspace_size", "gdn_prefill",
-            "gdn_prefill_profiled", "gdn_decode"]
+            "gdn_prefill_profiled", "gdn_prefill_ex", "gdn_decode"]
 
 
 class GdnError(RuntimeError):
@@ -51,6 +51,23 @@ class Desc(ctypes.Structure):
         ("l2_eps", ctypes.c_float),
         ("norm_eps", ctypes.c_float),
         ("flags", ctypes.c_uint32),
+    ]
+
+
+class PrefillArgs(ctypes.Structure):
+    """gdn_prefill_args (pointers as integers, NULL as None)."""
+    _fields_ = [
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("g", ctypes.c_void_p), ("beta", ctypes.c_void_p),
+        ("z", ctypes.c_void_p), ("conv_w", ctypes.c_void_p), ("norm_w", ctypes.c_void_p),
+        ("cu_seqlens", ctypes.c_void_p),
+        ("initial_state", ctypes.c_void_p), ("final_state", ctypes.c_void_p),
+        ("conv_state_in", ctypes.c_void_p), ("conv_state_out", ctypes.c_void_p),
+        ("state_slots", ctypes.c_void_p), ("num_state_slots", ctypes.c_int32),
+        ("state_snapshots", ctypes.c_void_p), ("snapshot_base", ctypes.c_void_p),
+        ("snapshot_every", ctypes.c_int32), ("num_snapshot_slots", ctypes.c_int32),
+        ("out", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
     ]
 
 
@@ -86,6 +103,8 @@ def lib():
         l.gdn_prefill.argtypes = [dp] + [vp] * 14 + [vp, sz, vp]
         l.gdn_prefill_profiled.restype = ctypes.c_int
         l.gdn_prefill_profiled.argtypes = [dp] + [vp] * 14 + [vp, sz, vp, vp, i32, vp, vp]
+        l.gdn_prefill_ex.restype = ctypes.c_int
+        l.gdn_prefill_ex.argtypes = [dp, ctypes.POINTER(PrefillArgs), vp]
         l.gdn_decode.restype = ctypes.c_int
         l.gdn_decode.argtypes = [dp] + [vp] * 11 + [i32, vp, vp]
         _lib = l
@@ -148,6 +167,26 @@ def gdn_prefill(desc: Desc, q, k, v, g, beta, *, z=None, conv_w=None, norm_w=Non
                            _ws_ptr(workspace), _ws_bytes(workspace), _stream(stream))
     if check and rc != GDN_OK:
         raise GdnError(rc, "gdn_prefill")
+    return rc
+
+
+def gdn_prefill_ex(desc: Desc, q, k, v, g, beta, *, z=None, conv_w=None, norm_w=None,
+                   cu_seqlens=None, initial_state=None, final_state=None, conv_state_in=None,
+                   conv_state_out=None, state_slots=None, num_state_slots: int = 0,
+                   state_snapshots=None, snapshot_base=None, snapshot_every: int = 0,
+                   num_snapshot_slots: int = 0, out=None, workspace=None, stream=None,
+                   check: bool = True) -> int:
+    a = PrefillArgs(q=_p(q), k=_p(k), v=_p(v), g=_p(g), beta=_p(beta), z=_p(z),
+                    conv_w=_p(conv_w), norm_w=_p(norm_w), cu_seqlens=_p(cu_seqlens),
+                    initial_state=_p(initial_state), final_state=_p(final_state),
+                    conv_state_in=_p(conv_state_in), conv_state_out=_p(conv_state_out),
+                    state_slots=_p(state_slots), num_state_slots=int(num_state_slots),
+                    state_snapshots=_p(state_snapshots), snapshot_base=_p(snapshot_base),
+                    snapshot_every=int(snapshot_every), num_snapshot_slots=int(num_snapshot_slots),
+                    out=_p(out), workspace=_ws_ptr(workspace), workspace_bytes=_ws_bytes(workspace))
+    rc = lib().gdn_prefill_ex(ctypes.byref(desc), ctypes.byref(a), _stream(stream))
+    if check and rc != GDN_OK:
+        raise GdnError(rc, "gdn_prefill_ex")
     return rc
 
 

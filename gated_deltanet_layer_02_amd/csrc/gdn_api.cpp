@@ -66,64 +66,78 @@ PrefillLayout prefill_layout(const gdn_desc* d, bool varlen) {
     return L;
 }
 
-gdn_status prefill_impl(const gdn_desc* d, const void* q, const void* k, const void* v,
-                        const float* g, const float* beta, const void* z, const void* conv_w,
-                        const void* norm_w, const int32_t* cu_seqlens, const float* initial_state,
-                        const void* conv_state_in, void* out, float* final_state,
-                        void* conv_state_out, void* workspace, size_t workspace_bytes,
-                        hipStream_t stream, hipEvent_t* events, int32_t max_kernels,
-                        int32_t* num_kernels, int32_t* stage_ids) {
+gdn_status prefill_impl(const gdn_desc* d, const gdn_prefill_args& x, hipStream_t stream,
+                        hipEvent_t* events, int32_t max_kernels, int32_t* num_kernels,
+                        int32_t* stage_ids) {
     gdn_status st = check_desc_common(d);
     if (st != GDN_OK) return st;
-    if (d->state_dtype != GDN_F32) return GDN_ERR_BAD_DTYPE;
     const int64_t T = d->total_tokens;
     const int64_t N = d->num_seqs, Hk = d->num_k_heads, Hv = d->num_v_heads;
-    if (T > 0 && (!q || !k || !v || !g || !beta || !out)) return GDN_ERR_NULL_ARG;
-    if (T > 0 && (z == nullptr) != (norm_w == nullptr)) return GDN_ERR_NULL_ARG;
-    if (cu_seqlens == nullptr && N != 1) return GDN_ERR_NULL_ARG;
-    if (workspace == nullptr && workspace_bytes > 0) return GDN_ERR_WORKSPACE;
+    if (T > 0 && (!x.q || !x.k || !x.v || !x.g || !x.beta || !x.out)) return GDN_ERR_NULL_ARG;
+    if (T > 0 && (x.z == nullptr) != (x.norm_w == nullptr)) return GDN_ERR_NULL_ARG;
+    if (x.cu_seqlens == nullptr && N != 1) return GDN_ERR_NULL_ARG;
+    if (x.workspace == nullptr && x.workspace_bytes > 0) return GDN_ERR_WORKSPACE;
     if (events != nullptr && (num_kernels == nullptr || stage_ids == nullptr)) return GDN_ERR_NULL_ARG;
     if (events != nullptr && max_kernels < 1) return GDN_ERR_BAD_VALUE;
-    const void* tensors[] = {q, k, v, g, beta, z, conv_w, norm_w, cu_seqlens, initial_state,
-                             conv_state_in, out, final_state, conv_state_out};
+    const int64_t rows = x.num_state_slots == 0 ? N : x.num_state_slots;   // state pool rows
+    if (rows < 1 || (x.state_slots == nullptr && rows < N)) return GDN_ERR_BAD_SHAPE;
+    const bool snaps = x.state_snapshots != nullptr;
+    if (snaps && x.snapshot_base == nullptr) return GDN_ERR_NULL_ARG;
+    if (snaps && (x.snapshot_every < 1 || x.num_snapshot_slots < 1)) return GDN_ERR_BAD_SHAPE;
+    const void* tensors[] = {x.q, x.k, x.v, x.g, x.beta, x.z, x.conv_w, x.norm_w, x.cu_seqlens,
+                             x.initial_state, x.conv_state_in, x.out, x.final_state, x.conv_state_out,
+                             x.state_slots, x.state_snapshots, x.snapshot_base};
     for (const void* p : tensors)
         if (p && !aligned16(p)) return GDN_ERR_MISALIGNED;
-    if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255u)) return GDN_ERR_MISALIGNED;
+    if (x.workspace && (reinterpret_cast<uintptr_t>(x.workspace) & 255u)) return GDN_ERR_MISALIGNED;
 
-    const bool varlen = cu_seqlens != nullptr;
+    const bool varlen = x.cu_seqlens != nullptr;
     const PrefillLayout L = prefill_layout(d, varlen);
-    if (workspace == nullptr || workspace_bytes < L.total) return GDN_ERR_WORKSPACE;
+    if (x.workspace == nullptr || x.workspace_bytes < L.total) return GDN_ERR_WORKSPACE;
 
     // outputs must not overlap the inputs they are computed from
     const size_t es = io_size(d->io_dtype);
-    const Range rout(out, (size_t)T * Hv * gdn::kD * es);
-    const Range rin[] = {Range(q, (size_t)T * Hk * gdn::kD * es), Range(k, (size_t)T * Hk * gdn::kD * es),
-                         Range(v, (size_t)T * Hv * gdn::kD * es), Range(z, z ? (size_t)T * Hv * gdn::kD * es : 0),
-                         Range(workspace, L.total)};
+    const size_t ss = io_size(d->state_dtype);
+    const Range rout(x.out, (size_t)T * Hv * gdn::kD * es);
+    const Range rws(x.workspace, L.total);
+    const Range rin[] = {Range(x.q, (size_t)T * Hk * gdn::kD * es), Range(x.k, (size_t)T * Hk * gdn::kD * es),
+                         Range(x.v, (size_t)T * Hv * gdn::kD * es),
+                         Range(x.z, x.z ? (size_t)T * Hv * gdn::kD * es : 0), rws};
     for (const Range& r : rin)
-        if (out && rout.overlaps(r)) return GDN_ERR_ALIAS;
-    const size_t state_bytes = (size_t)N * Hv * gdn::kD * gdn::kD * sizeof(float);
-    if (final_state && Range(final_state, state_bytes).overlaps(Range(workspace, L.total))) return GDN_ERR_ALIAS;
-    if (final_state && out && Range(final_state, state_bytes).overlaps(rout)) return GDN_ERR_ALIAS;
-    if (final_state && initial_state && final_state != initial_state &&
-        Range(final_state, state_bytes).overlaps(Range(initial_state, state_bytes)))
+        if (x.out && rout.overlaps(r)) return GDN_ERR_ALIAS;
+    const size_t state_bytes = (size_t)rows * Hv * gdn::kD * gdn::kD * ss;
+    const Range rfs(x.final_state, x.final_state ? state_bytes : 0);
+    if (rfs.overlaps(rws) || rfs.overlaps(rout)) return GDN_ERR_ALIAS;
+    if (x.final_state && x.initial_state && x.final_state != x.initial_state &&
+        rfs.overlaps(Range(x.initial_state, state_bytes)))
         return GDN_ERR_ALIAS;
+    if (snaps) {
+        const Range rsn(x.state_snapshots, (size_t)x.num_snapshot_slots * Hv * gdn::kD * gdn::kD * ss);
+        const size_t cs_bytes = (size_t)rows * (gdn::kConvK - 1) * (2 * Hk + Hv) * gdn::kD * es;
+        const Range others[] = {rin[0], rin[1], rin[2], rin[3], rws, rout, rfs,
+                                Range(x.initial_state, x.initial_state ? state_bytes : 0),
+                                Range(x.conv_state_in, x.conv_state_in ? cs_bytes : 0),
+                                Range(x.conv_state_out, x.conv_state_out ? cs_bytes : 0),
+                                Range(x.g, (size_t)T * Hv * 4), Range(x.beta, (size_t)T * Hv * 4)};
+        for (const Range& r : others)
+            if (rsn.overlaps(r)) return GDN_ERR_ALIAS;
+    }
 
-    char* ws = static_cast<char*>(workspace);
+    char* ws = static_cast<char*>(x.workspace);
     gdn::PrefillPlan p{};
     p.io_bf16 = d->io_dtype == GDN_BF16;
-    p.conv = conv_w != nullptr;
-    p.gated = z != nullptr && norm_w != nullptr;
+    p.conv = x.conv_w != nullptr;
+    p.gated = x.z != nullptr && x.norm_w != nullptr;
     p.total_tokens = T;
     p.chunk_slots = (int32_t)(T > 0 ? chunk_slots(d, varlen) : 0);
-    p.z = z;
-    p.norm_w = norm_w;
+    p.z = x.z;
+    p.norm_w = x.norm_w;
     p.norm_eps = d->norm_eps;
 
     gdn::PrepArgs& a = p.prep;
-    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
-    a.conv_w = conv_w; a.conv_state_in = conv_state_in;
-    a.cu = cu_seqlens;
+    a.q = x.q; a.k = x.k; a.v = x.v; a.g = x.g; a.beta = x.beta;
+    a.conv_w = x.conv_w; a.conv_state_in = x.conv_state_in;
+    a.cu = x.cu_seqlens; a.slots = x.state_slots;
     a.chunk_off = varlen ? reinterpret_cast<int32_t*>(ws + L.chunk_off) : nullptr;
     a.KB = ws + L.KB; a.VB = ws + L.VB;
     a.T = (int32_t)T; a.N = (int32_t)N; a.Hk = (int32_t)Hk; a.Hv = (int32_t)Hv;
@@ -132,13 +146,17 @@ gdn_status prefill_impl(const gdn_desc* d, const void* q, const void* k, const v
 
     gdn::SweepArgs& s = p.sweep;
     s.KB = a.KB; s.VB = a.VB;
-    s.initial_state = initial_state; s.final_state = final_state;
-    s.out = out; s.cu = cu_seqlens; s.chunk_off = a.chunk_off;
+    s.initial_state = x.initial_state; s.final_state = x.final_state;
+    s.snapshots = x.state_snapshots; s.snap_base = x.snapshot_base;
+    s.snap_every = snaps ? x.snapshot_every : 0;
+    s.slots = x.state_slots; s.state_bf16 = d->state_dtype == GDN_BF16 ? 1 : 0;
+    s.out = x.out; s.cu = x.cu_seqlens; s.chunk_off = a.chunk_off;
     s.T = a.T; s.N = a.N; s.Hk = a.Hk; s.Hv = a.Hv;
 
     gdn::ConvStateArgs& c = p.conv_state;
-    c.q = q; c.k = k; c.v = v; c.conv_state_in = conv_state_in; c.conv_state_out = conv_state_out;
-    c.cu = cu_seqlens; c.T = a.T; c.N = a.N; c.Hk = a.Hk; c.Hv = a.Hv;
+    c.q = x.q; c.k = x.k; c.v = x.v;
+    c.conv_state_in = x.conv_state_in; c.conv_state_out = x.conv_state_out; c.slots = x.state_slots;
+    c.cu = x.cu_seqlens; c.T = a.T; c.N = a.N; c.Hk = a.Hk; c.Hv = a.Hv;
 
     gdn::KernelRecorder rec;
     rec.events = events;
@@ -147,6 +165,19 @@ gdn_status prefill_impl(const gdn_desc* d, const void* q, const void* k, const v
     const hipError_t e = gdn::launch_prefill(p, stream, rec);
     if (num_kernels) *num_kernels = rec.count;
     return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+gdn_prefill_args flat_args(const void* q, const void* k, const void* v, const float* g,
+                           const float* beta, const void* z, const void* conv_w, const void* norm_w,
+                           const int32_t* cu_seqlens, const float* initial_state,
+                           const void* conv_state_in, void* out, float* final_state,
+                           void* conv_state_out, void* workspace, size_t workspace_bytes) {
+    gdn_prefill_args x{};
+    x.q = q; x.k = k; x.v = v; x.g = g; x.beta = beta; x.z = z; x.conv_w = conv_w;
+    x.norm_w = norm_w; x.cu_seqlens = cu_seqlens; x.initial_state = initial_state;
+    x.conv_state_in = conv_state_in; x.out = out; x.final_state = final_state;
+    x.conv_state_out = conv_state_out; x.workspace = workspace; x.workspace_bytes = workspace_bytes;
+    return x;
 }
 
 }  // namespace
@@ -184,9 +215,11 @@ gdn_status gdn_prefill(const gdn_desc* d, const void* q, const void* k, const vo
                        const void* conv_state_in, void* out, float* final_state,
                        void* conv_state_out, void* workspace, size_t workspace_bytes,
                        hipStream_t stream) {
-    return prefill_impl(d, q, k, v, g, beta, z, conv_w, norm_w, cu_seqlens, initial_state,
-                        conv_state_in, out, final_state, conv_state_out, workspace, workspace_bytes,
-                        stream, nullptr, 0, nullptr, nullptr);
+    if (d != nullptr && d->state_dtype != GDN_F32) return GDN_ERR_BAD_DTYPE;
+    const gdn_prefill_args x = flat_args(q, k, v, g, beta, z, conv_w, norm_w, cu_seqlens, initial_state,
+                                         conv_state_in, out, final_state, conv_state_out, workspace,
+                                         workspace_bytes);
+    return prefill_impl(d, x, stream, nullptr, 0, nullptr, nullptr);
 }
 
 gdn_status gdn_prefill_profiled(const gdn_desc* d, const void* q, const void* k, const void* v,
@@ -197,9 +230,16 @@ gdn_status gdn_prefill_profiled(const gdn_desc* d, const void* q, const void* k,
                                 size_t workspace_bytes, hipStream_t stream, hipEvent_t* events,
                                 int32_t max_kernels, int32_t* num_kernels, int32_t* stage_ids) {
     if (events == nullptr || num_kernels == nullptr || stage_ids == nullptr) return GDN_ERR_NULL_ARG;
-    return prefill_impl(d, q, k, v, g, beta, z, conv_w, norm_w, cu_seqlens, initial_state,
-                        conv_state_in, out, final_state, conv_state_out, workspace, workspace_bytes,
-                        stream, events, max_kernels, num_kernels, stage_ids);
+    if (d != nullptr && d->state_dtype != GDN_F32) return GDN_ERR_BAD_DTYPE;
+    const gdn_prefill_args x = flat_args(q, k, v, g, beta, z, conv_w, norm_w, cu_seqlens, initial_state,
+                                         conv_state_in, out, final_state, conv_state_out, workspace,
+                                         workspace_bytes);
+    return prefill_impl(d, x, stream, events, max_kernels, num_kernels, stage_ids);
+}
+
+gdn_status gdn_prefill_ex(const gdn_desc* d, const gdn_prefill_args* args, hipStream_t stream) {
+    if (args == nullptr) return GDN_ERR_NULL_ARG;
+    return prefill_impl(d, *args, stream, nullptr, 0, nullptr, nullptr);
 }
 
 gdn_status gdn_decode(const gdn_desc* d, const void* q, const void* k, const void* v,

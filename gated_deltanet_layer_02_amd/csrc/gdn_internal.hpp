@@ -36,14 +36,21 @@ struct PrepArgs {
     const float* g; const float* beta;
     const void* conv_w; const void* conv_state_in;
     const int32_t* cu; int32_t* chunk_off;
+    const int32_t* slots;   // conv-state row of sequence n (NULL: n)
     void* KB; void* VB;
     int32_t T, N, Hk, Hv, use_l2;
     float scale, l2_eps;
 };
 
+// States are rows of a pool: sequence n uses row slots[n] (NULL: n), stored
+// fp32 or (state_bf16) bf16.  Snapshots (snap_every > 0): the state after
+// chunk boundary snap_every * j (j >= 1, before the sequence end) goes to
+// row snap_base[n] + j - 1 of `snapshots`.
 struct SweepArgs {
     const void* KB; const void* VB;
-    const float* initial_state; float* final_state;
+    const void* initial_state; void* final_state;
+    void* snapshots; const int32_t* snap_base; int32_t snap_every;
+    const int32_t* slots; int32_t state_bf16;
     void* out;
     const int32_t* cu; const int32_t* chunk_off;
     int32_t T, N, Hk, Hv;
@@ -52,7 +59,7 @@ struct SweepArgs {
 struct ConvStateArgs {
     const void* q; const void* k; const void* v;
     const void* conv_state_in; void* conv_state_out;
-    const int32_t* cu;
+    const int32_t* cu; const int32_t* slots;
     int32_t T, N, Hk, Hv;
 };
 

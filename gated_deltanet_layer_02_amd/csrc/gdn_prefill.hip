@@ -253,6 +253,7 @@ __global__ __launch_bounds__(256, 2) void gdn_chunk_prep_kernel(PrepArgs a) {
     const int c = blockIdx.x, hk = blockIdx.y;
     int n, t0, len, seq_start;
     if (!locate_chunk(a, c, n, t0, len, seq_start)) return;
+    const int crow = a.slots ? a.slots[n] : n;   // conv-state row of the sequence
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -275,8 +276,8 @@ __global__ __launch_bounds__(256, 2) void gdn_chunk_prep_kernel(PrepArgs a) {
     float gl = 0.f, bl = 0.f;  // its g and beta (wave 0, lane = token)
     {
         Quad<IO, kConv> xq, xk;
-        xq.load(q, Hk, hk * kD + 8 * cg, hk * kD + 8 * cg, t0, tq, len, seq_start, n, Cch, conv_w, csin);
-        xk.load(k, Hk, hk * kD + 8 * cg, Hk * kD + hk * kD + 8 * cg, t0, tq, len, seq_start, n, Cch,
+        xq.load(q, Hk, hk * kD + 8 * cg, hk * kD + 8 * cg, t0, tq, len, seq_start, crow, Cch, conv_w, csin);
+        xk.load(k, Hk, hk * kD + 8 * cg, Hk * kD + hk * kD + 8 * cg, t0, tq, len, seq_start, crow, Cch,
                 conv_w, csin);
         xq.load_w(conv_w, hk * kD + 8 * cg);
         xk.load_w(conv_w, Hk * kD + hk * kD + 8 * cg);
@@ -388,7 +389,7 @@ __global__ __launch_bounds__(256, 2) void gdn_chunk_prep_kernel(PrepArgs a) {
             {
                 if (!inner)
                     xv.load(v, Hv, h * kD + 8 * cg, 2 * Hk * kD + h * kD + 8 * cg, t0, tq, len, seq_start,
-                            n, Cch, conv_w, csin);
+                            crow, Cch, conv_w, csin);
                 xv.load_w(conv_w, 2 * Hk * kD + h * kD + 8 * cg);
                 float xf[7][8], wf[4][8];
                 xv.unpack(xf, wf);
@@ -592,6 +593,48 @@ __device__ __forceinline__ bool sweep_unit(int x, int groups, int N, int Hk, int
 // grid size of the mapping above
 __host__ __device__ constexpr int sweep_grid(int groups, int N, int Hk, int Hv) {
     return (N * Hk + 7) / 8 * 8 * (Hv / Hk) * groups;
+}
+
+// State rows of the sweep: 4 consecutive dk of one dv row at element offset
+// `off` of a pool stored fp32 or bf16 (RNE on store).
+__device__ __forceinline__ f32x4 state_load4(const void* base, int bf16, size_t off) {
+    if (bf16) {
+        const u16x4 x = *reinterpret_cast<const u16x4*>(static_cast<const uint16_t*>(base) + off);
+        return f32x4{bf16_bits_to_f32(x[0]), bf16_bits_to_f32(x[1]), bf16_bits_to_f32(x[2]),
+                     bf16_bits_to_f32(x[3])};
+    }
+    return *reinterpret_cast<const f32x4*>(static_cast<const float*>(base) + off);
+}
+__device__ __forceinline__ void state_store4(void* base, int bf16, size_t off, const f32x4& x) {
+    if (bf16) {
+        *reinterpret_cast<u16x4*>(static_cast<uint16_t*>(base) + off) =
+            u16x4{f32_to_bf16_bits(x[0]), f32_to_bf16_bits(x[1]), f32_to_bf16_bits(x[2]),
+                  f32_to_bf16_bits(x[3])};
+        return;
+    }
+    *reinterpret_cast<f32x4*>(static_cast<float*>(base) + off) = x;
+}
+// element offset of (pool row, head h, dv row of slice s at lane l16, dk 0)
+__device__ __forceinline__ size_t state_row(const SweepArgs& a, int row, int h, int s, int l16) {
+    return ((((size_t)row * a.Hv + h) * kD) + 16 * s + l16) * kD;
+}
+template <int NT>
+__device__ __forceinline__ void state_put(void* base, const SweepArgs& a, int row, int h, int s0,
+                                          const f32x4 (&S)[NT][8], int l16, int g4) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const size_t r = state_row(a, row, h, s0 + nt, l16);
+#pragma unroll
+        for (int m = 0; m < 8; ++m) state_store4(base, a.state_bf16, r + 16 * m + 4 * g4, S[nt][m]);
+    }
+}
+// snapshot after local chunk j when chunk j + 1 closes a boundary of the
+// snapshot grid inside the sequence
+template <int NT>
+__device__ __forceinline__ void state_snapshot(const SweepArgs& a, int n, int j, int nch, int h, int s0,
+                                               const f32x4 (&S)[NT][8], int l16, int g4) {
+    if (a.snap_every <= 0 || (j + 1) % a.snap_every != 0 || j + 1 >= nch) return;
+    state_put<NT>(a.snapshots, a, a.snap_base[n] + (j + 1) / a.snap_every - 1, h, s0, S, l16, g4);
 }
 
 struct SweepSeq {
@@ -818,23 +861,26 @@ __global__ __launch_bounds__(64 * (SW + PW)) void gdn_state_sweep_lds_kernel(Swe
     }
 
     const int s0 = (sg * SW + wave) * NT;
+    const int row = a.slots ? a.slots[n] : n;   // state pool row
     f32x4 S[NT][8];
-    const size_t hrow = ((size_t)n * a.Hv + h) * kD;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-        const size_t srow = (hrow + 16 * (s0 + nt) + l16) * kD;
+        const size_t srow = state_row(a, row, h, s0 + nt, l16);
 #pragma unroll
         for (int m = 0; m < 8; ++m)
-            S[nt][m] = a.initial_state != nullptr
-                           ? *reinterpret_cast<const f32x4*>(a.initial_state + srow + 16 * m + 4 * g4)
-                           : f32x4{0.f, 0.f, 0.f, 0.f};
+            S[nt][m] = a.initial_state != nullptr ? state_load4(a.initial_state, a.state_bf16, srow + 16 * m + 4 * g4)
+                                                  : f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
     f32x4 O[NT][4];
 #pragma unroll 1
     for (int j = 0; j < q.nch; j += 2) {
         sweep_lds_step<SW, NT>(a, q, j, h, sg, wave, S, O, buf0);
-        if (j + 1 < q.nch) sweep_lds_step<SW, NT>(a, q, j + 1, h, sg, wave, S, O, buf1);
+        state_snapshot<NT>(a, n, j, q.nch, h, s0, S, l16, g4);
+        if (j + 1 < q.nch) {
+            sweep_lds_step<SW, NT>(a, q, j + 1, h, sg, wave, S, O, buf1);
+            state_snapshot<NT>(a, n, j + 1, q.nch, h, s0, S, l16, g4);
+        }
     }
     if (q.nch > 0) {   // output of the last chunk
 #pragma unroll
@@ -842,15 +888,7 @@ __global__ __launch_bounds__(64 * (SW + PW)) void gdn_state_sweep_lds_kernel(Swe
             store_o(static_cast<uint16_t*>(a.out), O[nt], q.seq_start + (q.nch - 1) * kChunk,
                     q.L - (q.nch - 1) * kChunk, a.Hv, h, s0 + nt, l16, g4);
     }
-    if (a.final_state != nullptr) {
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            const size_t srow = (hrow + 16 * (s0 + nt) + l16) * kD;
-#pragma unroll
-            for (int m = 0; m < 8; ++m)
-                *reinterpret_cast<f32x4*>(a.final_state + srow + 16 * m + 4 * g4) = S[nt][m];
-        }
-    }
+    if (a.final_state != nullptr) state_put<NT>(a.final_state, a, row, h, s0, S, l16, g4);
 }
 
 // fp32 operands: the same sweep with operands read straight from memory
@@ -865,12 +903,12 @@ __global__ __launch_bounds__(64) void gdn_state_sweep_f32_kernel(SweepArgs a) {
     const SweepSeq q = sweep_seq(a, n);
 
     f32x4 S[1][8];
-    const size_t srow = (((size_t)n * a.Hv + h) * kD + 16 * s + l16) * kD;
+    const int row = a.slots ? a.slots[n] : n;   // state pool row
+    const size_t srow = state_row(a, row, h, s, l16);
 #pragma unroll
     for (int m = 0; m < 8; ++m)
-        S[0][m] = a.initial_state != nullptr
-                      ? *reinterpret_cast<const f32x4*>(a.initial_state + srow + 16 * m + 4 * g4)
-                      : f32x4{0.f, 0.f, 0.f, 0.f};
+        S[0][m] = a.initial_state != nullptr ? state_load4(a.initial_state, a.state_bf16, srow + 16 * m + 4 * g4)
+                                             : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 1
     for (int j = 0; j < q.nch; ++j) {
         const size_t c = (size_t)q.c_begin + j;
@@ -891,12 +929,9 @@ __global__ __launch_bounds__(64) void gdn_state_sweep_f32_kernel(SweepArgs a) {
             G[63]);
         store_o(static_cast<float*>(a.out), O[0], q.seq_start + j * kChunk,
                 min(kChunk, q.L - j * kChunk), a.Hv, h, s, l16, g4);
+        state_snapshot<1>(a, n, j, q.nch, h, s, S, l16, g4);
     }
-    if (a.final_state != nullptr) {
-#pragma unroll
-        for (int m = 0; m < 8; ++m)
-            *reinterpret_cast<f32x4*>(a.final_state + srow + 16 * m + 4 * g4) = S[0][m];
-    }
+    if (a.final_state != nullptr) state_put<1>(a.final_state, a, row, h, s, S, l16, g4);
 }
 
 // ===========================================================================
@@ -944,12 +979,13 @@ __global__ __launch_bounds__(256) void gdn_conv_state_kernel(ConvStateArgs a) {
     const int start = a.cu ? a.cu[n] : 0;
     const int L = a.cu ? a.cu[n + 1] - start : a.T;
     const int qk = a.Hk * kD;
+    const size_t crow = a.slots ? a.slots[n] : n;   // conv-state row
     IO val[kConvK - 1];
 #pragma unroll
     for (int j = 0; j < kConvK - 1; ++j) {
         const int pos = L + j;   // index into (conv state in ++ sequence)
         if (pos < kConvK - 1) {
-            val[j] = csin ? csin[((size_t)n * (kConvK - 1) + pos) * Cch + ch] : f32_to_io<IO>(0.f);
+            val[j] = csin ? csin[(crow * (kConvK - 1) + pos) * Cch + ch] : f32_to_io<IO>(0.f);
         } else {
             const size_t t = (size_t)start + pos - (kConvK - 1);
             if (ch < qk) val[j] = q[t * qk + ch];
@@ -958,7 +994,7 @@ __global__ __launch_bounds__(256) void gdn_conv_state_kernel(ConvStateArgs a) {
         }
     }
 #pragma unroll
-    for (int j = 0; j < kConvK - 1; ++j) csout[((size_t)n * (kConvK - 1) + j) * Cch + ch] = val[j];
+    for (int j = 0; j < kConvK - 1; ++j) csout[(crow * (kConvK - 1) + j) * Cch + ch] = val[j];
 }
 
 // ===========================================================================

@@ -42,7 +42,13 @@ class PrefillCall:
     def __init__(self, x: dict, *, Hk: int, Hv: int, io_bf16: bool, l2norm: bool = True,
                  scale: float = 1.0, l2_eps: float = 1e-6, norm_eps: float = 1e-6,
                  want_final_state: bool = True, want_conv_state: bool = True,
-                 pass_cu: Optional[bool] = None, device="cuda"):
+                 pass_cu: Optional[bool] = None, state_bf16: bool = False,
+                 slots: Optional[np.ndarray] = None, num_state_slots: int = 0,
+                 snapshot_every: int = 0, snapshot_base: Optional[np.ndarray] = None,
+                 num_snapshot_slots: int = 0, device="cuda"):
+        """x["state"] / x["conv_state"] hold num_state_slots rows (a pool)
+        when `slots` is given, else N rows; x["state"] is float32 or, with
+        state_bf16, uint16 bf16 bits."""
         import torch
         self.cu_host = np.asarray(x["cu_seqlens"], dtype=np.int32)
         self.N = len(self.cu_host) - 1
@@ -57,14 +63,25 @@ class PrefillCall:
         if pass_cu is None:
             pass_cu = self.N > 1
         self.cu = to_device(self.cu_host, d) if pass_cu else None
+        self.state_bf16 = state_bf16
+        self.slots = to_device(None if slots is None else np.asarray(slots, np.int32), d)
+        self.num_state_slots = int(num_state_slots)
+        rows = self.num_state_slots if self.num_state_slots > 0 else self.N
+        self.snapshot_every = int(snapshot_every)
+        self.snapshot_base = to_device(None if snapshot_base is None else np.asarray(snapshot_base, np.int32), d)
+        self.num_snapshot_slots = int(num_snapshot_slots)
+        self.extended = state_bf16 or slots is not None or self.num_state_slots > 0 or self.snapshot_every > 0
+        sdt = torch.bfloat16 if state_bf16 else torch.float32
         self.desc = B.make_desc(self.N, self.T, Hk, Hv, B.GDN_BF16 if io_bf16 else B.GDN_F32,
-                                B.GDN_F32, scale, l2_eps, norm_eps, l2norm)
+                                B.GDN_BF16 if state_bf16 else B.GDN_F32, scale, l2_eps, norm_eps, l2norm)
         self.out = empty_like_io((max(self.T, 1), Hv, 128), io_bf16, d)
-        self.final_state = (torch.empty((self.N, Hv, 128, 128), dtype=torch.float32, device=d)
+        self.final_state = (torch.empty((rows, Hv, 128, 128), dtype=sdt, device=d)
                             if want_final_state else None)
         Cch = 2 * Hk * 128 + Hv * 128
-        self.conv_state_out = (empty_like_io((self.N, 3, Cch), io_bf16, d)
+        self.conv_state_out = (empty_like_io((rows, 3, Cch), io_bf16, d)
                                if want_conv_state else None)
+        self.snapshots = (torch.empty((self.num_snapshot_slots, Hv, 128, 128), dtype=sdt, device=d)
+                          if self.snapshot_every > 0 else None)
         nbytes = B.gdn_prefill_workspace_size(self.desc)
         self.workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=d)
 
@@ -75,6 +92,13 @@ class PrefillCall:
                     conv_state_out=self.conv_state_out, workspace=self.workspace)
 
     def run(self, stream=None):
+        if self.extended:
+            B.gdn_prefill_ex(self.desc, self.q, self.k, self.v, self.g, self.beta, stream=stream,
+                             state_slots=self.slots, num_state_slots=self.num_state_slots,
+                             state_snapshots=self.snapshots, snapshot_base=self.snapshot_base,
+                             snapshot_every=self.snapshot_every,
+                             num_snapshot_slots=self.num_snapshot_slots, **self.kwargs())
+            return
         B.gdn_prefill(self.desc, self.q, self.k, self.v, self.g, self.beta, stream=stream,
                       **self.kwargs())
 

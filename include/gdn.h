@@ -82,7 +82,7 @@ typedef struct {
     int32_t head_v_dim;     /* dv: 128 */
     int32_t conv_kernel;    /* K: 4 */
     gdn_dtype io_dtype;     /* q, k, v, z, out, conv_w, norm_w, conv states */
-    gdn_dtype state_dtype;  /* recurrent state: prefill F32; decode F32 or BF16 */
+    gdn_dtype state_dtype;  /* recurrent state storage: F32 or BF16 (gdn_prefill: F32) */
     float scale;            /* multiplies q after normalisation; 1.0 leaves q as is */
     float l2_eps;           /* step 2: x / sqrt(sum x^2 + l2_eps) */
     float norm_eps;         /* step 4 */
@@ -156,6 +156,57 @@ gdn_status gdn_prefill_profiled(const gdn_desc* d,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream,
                                 hipEvent_t* events, int32_t max_kernels, int32_t* num_kernels,
                                 int32_t* stage_ids);
+
+/*
+ * Prefill with every option, arguments in one struct (fields as in
+ * gdn_prefill unless stated; unused options zero / NULL).
+ *
+ * State pool.  state_slots [N] int32 device, or NULL: the row of
+ * initial_state, final_state, conv_state_in and conv_state_out that sequence
+ * n uses (NULL: row n).  Precondition: distinct, in [0, num_state_slots).
+ * The four state tensors then have num_state_slots rows (>= N without
+ * slots); rows no sequence names are not touched.  (SGLang cookbook,
+ * Configuration Tips: the per-request state cache of --max-mamba-cache-size.)
+ *
+ * State dtype.  desc->state_dtype F32 or BF16 selects the storage of
+ * initial_state, final_state and state_snapshots: [rows, Hv, dv, dk]; the
+ * recurrence always runs on an fp32 state, bf16 is read widened and written
+ * rounded to nearest even.  (Same page: --mamba-ssm-dtype.)
+ *
+ * Snapshots.  With state_snapshots non-NULL and snapshot_every = m >= 1, the
+ * state after each chunk boundary 64 m j < L_n (j = 1, 2, ...) of sequence n
+ * is also written, to row snapshot_base[n] + j - 1 of state_snapshots
+ * [num_snapshot_slots, Hv, dv, dk] (state dtype).  snapshot_base [N] int32
+ * device; precondition: rows in [0, num_snapshot_slots), not shared between
+ * sequences.  The state after the last token is final_state, never a
+ * snapshot.  (Same page, the branching-point cache of the radix cache.)
+ *
+ * Errors as gdn_prefill; in addition GDN_ERR_BAD_SHAPE for num_state_slots <
+ * 1 (or < N without slots), snapshot_every < 1 or num_snapshot_slots < 1
+ * with snapshots, GDN_ERR_NULL_ARG for snapshots without snapshot_base, and
+ * GDN_ERR_ALIAS for a snapshot array that overlaps any other tensor.
+ */
+typedef struct {
+    const void* q; const void* k; const void* v;
+    const float* g; const float* beta;
+    const void* z; const void* conv_w; const void* norm_w;
+    const int32_t* cu_seqlens;
+    const void* initial_state;      /* state dtype */
+    void* final_state;              /* state dtype */
+    const void* conv_state_in;
+    void* conv_state_out;
+    const int32_t* state_slots;
+    int32_t num_state_slots;        /* 0: N */
+    void* state_snapshots;          /* state dtype, or NULL */
+    const int32_t* snapshot_base;
+    int32_t snapshot_every;
+    int32_t num_snapshot_slots;
+    void* out;
+    void* workspace;
+    size_t workspace_bytes;
+} gdn_prefill_args;
+
+gdn_status gdn_prefill_ex(const gdn_desc* d, const gdn_prefill_args* args, hipStream_t stream);
 
 /*
  * Decode: one new token for each of N sequences against cached states.

@@ -83,7 +83,7 @@ def test_prefill_validation_errors():
         (dict(conv_kernel=3), {}, 3),
         (dict(flags=0x8), {}, 3),
         (dict(io_dtype=5), {}, 4),
-        (dict(state_dtype=B.GDN_BF16), {}, 4),           # prefill state is fp32
+        (dict(state_dtype=B.GDN_BF16), {}, 4),           # gdn_prefill: fp32 state (gdn_prefill_ex: either)
         (dict(scale=float("nan")), {}, 9),
         (dict(l2_eps=-1.0), {}, 9),
         ({}, dict(q=None), 1),
@@ -152,3 +152,59 @@ def test_decode_validation_errors():
             setattr(d, k, v)
         rc = _decode_rc(d, ns, **pover)
         assert rc == want, (dover, pover, rc, want)
+
+
+def _ex_rc(desc, **over):
+    """gdn_prefill_ex with fake, non-overlapping device pointers."""
+    names = ["q", "k", "v", "g", "beta", "z", "conv_w", "norm_w", "cu_seqlens", "initial_state",
+             "final_state", "conv_state_in", "conv_state_out", "state_slots", "state_snapshots",
+             "snapshot_base", "out", "workspace"]
+    vals = dict(zip(names, _ptrs(len(names))))
+    vals.update(state_slots=None, state_snapshots=None, snapshot_base=None)
+    ints = dict(num_state_slots=0, snapshot_every=0, num_snapshot_slots=0, workspace_bytes=1 << 33)
+    for k, v in over.items():
+        (vals if k in vals else ints)[k] = v
+    a = B.PrefillArgs(**vals, **ints)
+    return gdn.lib().gdn_prefill_ex(ctypes.byref(desc), ctypes.byref(a), None)
+
+
+def test_prefill_ex_validation_errors():
+    snap = dict(state_snapshots=FAKE + 30 * STEP, snapshot_base=FAKE + 31 * STEP, snapshot_every=2,
+                num_snapshot_slots=8)
+    cases = [
+        ({}, dict(q=None), 1),
+        ({}, dict(num_state_slots=1), 2),                         # fewer rows than sequences
+        ({}, dict(state_slots=FAKE + 32 * STEP, num_state_slots=-1), 2),
+        ({}, dict(snap, snapshot_base=None), 1),                  # snapshots need their rows
+        ({}, dict(snap, snapshot_every=0), 2),
+        ({}, dict(snap, num_snapshot_slots=0), 2),
+        ({}, dict(snap, state_snapshots=FAKE + 16 * STEP), 8),    # snapshots alias out
+        ({}, dict(snap, state_snapshots=FAKE + 9 * STEP), 8),     # ... the initial state
+        ({}, dict(snap, state_snapshots=FAKE + 30 * STEP + 8), 5),
+        ({}, dict(state_slots=FAKE + 32 * STEP + 4), 5),
+        (dict(state_dtype=7), {}, 4),
+    ]
+    for dover, pover, want in cases:
+        dd = B.make_desc(2, 100, state_dtype=B.GDN_BF16)
+        for k, v in dover.items():
+            setattr(dd, k, v)
+        rc = _ex_rc(dd, **pover)
+        assert rc == want, (dover, pover, rc, want)
+    assert gdn.lib().gdn_prefill_ex(ctypes.byref(B.make_desc(1, 1)), None, None) == 1
+
+
+def test_prefill_args_layout_matches_the_header(tmp_path):
+    """The ctypes mirror of gdn_prefill_args has the C compiler's layout."""
+    fields = [f for f, _ in B.PrefillArgs._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text('#include "gdn.h"\n#include <stdio.h>\n#include <stddef.h>\nint main(void) {\n'
+                   '  printf("%zu", sizeof(gdn_prefill_args));\n'
+                   + "".join(f'  printf(" %zu", offsetof(gdn_prefill_args, {f}));\n' for f in fields)
+                   + "  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include",
+                    "-D__HIP_PLATFORM_AMD__", str(src), "-o", str(exe)], check=True)
+    got = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True,
+                                          check=True).stdout.split()]
+    want = [ctypes.sizeof(B.PrefillArgs)] + [getattr(B.PrefillArgs, f).offset for f in fields]
+    assert got == want
