@@ -26,7 +26,8 @@ STATUS_NAMES = {0: "GDN_OK", 1: "GDN_ERR_NULL_ARG", 2: "GDN_ERR_BAD_SHAPE",
                 9: "GDN_ERR_BAD_VALUE"}
 
 EXPORTED = ["gdn_status_string", "gdn_prefill_workspace_size", "gdn_prefill",
-            "gdn_prefill_profiled", "gdn_prefill_ex", "gdn_decode"]
+            "gdn_prefill_profiled", "gdn_prefill_ex", "gdn_decode", "gdn_decode_verify",
+            "gdn_decode_commit"]
 
 
 class GdnError(RuntimeError):
@@ -105,6 +106,10 @@ def lib():
         l.gdn_prefill_profiled.argtypes = [dp] + [vp] * 14 + [vp, sz, vp, vp, i32, vp, vp]
         l.gdn_prefill_ex.restype = ctypes.c_int
         l.gdn_prefill_ex.argtypes = [dp, ctypes.POINTER(PrefillArgs), vp]
+        l.gdn_decode_verify.restype = ctypes.c_int
+        l.gdn_decode_verify.argtypes = [dp, i32] + [vp] * 11 + [i32, vp, vp, vp, vp]
+        l.gdn_decode_commit.restype = ctypes.c_int
+        l.gdn_decode_commit.argtypes = [dp, i32] + [vp] * 6 + [i32, vp]
         l.gdn_decode.restype = ctypes.c_int
         l.gdn_decode.argtypes = [dp] + [vp] * 11 + [i32, vp, vp]
         _lib = l
@@ -224,4 +229,32 @@ def gdn_decode(desc: Desc, q, k, v, g, beta, *, state, out, z=None, conv_w=None,
                           int(num_state_slots), _p(out), _stream(stream))
     if check and rc != GDN_OK:
         raise GdnError(rc, "gdn_decode")
+    return rc
+
+
+def gdn_decode_verify(desc: Desc, num_draft: int, q, k, v, g, beta, *, state, state_ckpt, out,
+                      z=None, conv_w=None, norm_w=None, conv_state=None, conv_ckpt=None,
+                      state_slots=None, num_state_slots: Optional[int] = None, stream=None,
+                      check: bool = True) -> int:
+    if num_state_slots is None:
+        num_state_slots = desc.num_seqs
+    rc = lib().gdn_decode_verify(ctypes.byref(desc), int(num_draft), _p(q), _p(k), _p(v), _p(g),
+                                 _p(beta), _p(z), _p(conv_w), _p(norm_w), _p(state),
+                                 _p(conv_state), _p(state_slots), int(num_state_slots),
+                                 _p(state_ckpt), _p(conv_ckpt), _p(out), _stream(stream))
+    if check and rc != GDN_OK:
+        raise GdnError(rc, "gdn_decode_verify")
+    return rc
+
+
+def gdn_decode_commit(desc: Desc, num_draft: int, *, state_ckpt, accepted, state, conv_ckpt=None,
+                      conv_state=None, state_slots=None, num_state_slots: Optional[int] = None,
+                      stream=None, check: bool = True) -> int:
+    if num_state_slots is None:
+        num_state_slots = desc.num_seqs
+    rc = lib().gdn_decode_commit(ctypes.byref(desc), int(num_draft), _p(state_ckpt), _p(conv_ckpt),
+                                 _p(accepted), _p(state), _p(conv_state), _p(state_slots),
+                                 int(num_state_slots), _stream(stream))
+    if check and rc != GDN_OK:
+        raise GdnError(rc, "gdn_decode_commit")
     return rc

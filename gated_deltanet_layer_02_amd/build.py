@@ -10,7 +10,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgdn.so")
-SOURCES = ["gdn_api.cpp", "gdn_prefill.hip", "gdn_decode.hip"]
+SOURCES = ["gdn_api.cpp", "gdn_prefill.hip", "gdn_decode.hip", "gdn_verify.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -285,4 +285,79 @@ gdn_status gdn_decode(const gdn_desc* d, const void* q, const void* k, const voi
     return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
+gdn_status gdn_decode_verify(const gdn_desc* d, int32_t num_draft, const void* q, const void* k,
+                             const void* v, const float* g, const float* beta, const void* z,
+                             const void* conv_w, const void* norm_w, const void* state,
+                             const void* conv_state, const int32_t* state_slots,
+                             int32_t num_state_slots, void* state_ckpt, void* conv_ckpt, void* out,
+                             hipStream_t stream) {
+    gdn_status st = check_desc_common(d);
+    if (st != GDN_OK) return st;
+    const int64_t N = d->num_seqs, Hk = d->num_k_heads, Hv = d->num_v_heads, D = num_draft;
+    if (D < 1 || D > GDN_MAX_DRAFT || d->total_tokens != N * D) return GDN_ERR_BAD_SHAPE;
+    if (!q || !k || !v || !g || !beta || !state || !state_ckpt || !out) return GDN_ERR_NULL_ARG;
+    if ((z == nullptr) != (norm_w == nullptr)) return GDN_ERR_NULL_ARG;
+    if (num_state_slots < 1 || (state_slots == nullptr && num_state_slots < N)) return GDN_ERR_BAD_SHAPE;
+    const void* tensors[] = {q, k, v, g, beta, z, conv_w, norm_w, state, conv_state, state_slots,
+                             state_ckpt, conv_ckpt, out};
+    for (const void* p : tensors)
+        if (p && !aligned16(p)) return GDN_ERR_MISALIGNED;
+    const size_t es = io_size(d->io_dtype), ss = io_size(d->state_dtype);
+    const size_t head = (size_t)gdn::kD * gdn::kD * ss;
+    const size_t cch = (size_t)(2 * Hk + Hv) * gdn::kD;
+    const Range rin[] = {Range(q, (size_t)N * D * Hk * gdn::kD * es), Range(k, (size_t)N * D * Hk * gdn::kD * es),
+                         Range(v, (size_t)N * D * Hv * gdn::kD * es),
+                         Range(z, z ? (size_t)N * D * Hv * gdn::kD * es : 0),
+                         Range(g, (size_t)N * D * Hv * 4), Range(beta, (size_t)N * D * Hv * 4),
+                         Range(state, (size_t)num_state_slots * Hv * head),
+                         Range(conv_state, conv_state ? (size_t)num_state_slots * (gdn::kConvK - 1) * cch * es : 0)};
+    const Range routs[] = {Range(state_ckpt, (size_t)N * D * Hv * head),
+                           Range(conv_ckpt, conv_ckpt ? (size_t)N * D * (gdn::kConvK - 1) * cch * es : 0),
+                           Range(out, (size_t)N * D * Hv * gdn::kD * es)};
+    for (const Range& o : routs) {
+        for (const Range& r : rin)
+            if (o.overlaps(r)) return GDN_ERR_ALIAS;
+        for (const Range& r : routs)
+            if (&o != &r && o.overlaps(r)) return GDN_ERR_ALIAS;
+    }
+    gdn::VerifyArgs a{};
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.z = z; a.conv_w = conv_w; a.norm_w = norm_w;
+    a.state = state; a.conv_state = conv_state; a.slots = state_slots;
+    a.state_ckpt = state_ckpt; a.conv_ckpt = conv_ckpt; a.out = out;
+    a.N = (int32_t)N; a.D = (int32_t)D; a.Hk = (int32_t)Hk; a.Hv = (int32_t)Hv;
+    a.use_l2 = (d->flags & GDN_FLAG_L2NORM_QK) ? 1 : 0;
+    a.scale = d->scale; a.l2_eps = d->l2_eps; a.norm_eps = d->norm_eps;
+    const hipError_t e = gdn::launch_verify(a, d->io_dtype == GDN_BF16, d->state_dtype == GDN_BF16,
+                                            conv_w != nullptr, stream);
+    return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+gdn_status gdn_decode_commit(const gdn_desc* d, int32_t num_draft, const void* state_ckpt,
+                             const void* conv_ckpt, const int32_t* accepted, void* state,
+                             void* conv_state, const int32_t* state_slots, int32_t num_state_slots,
+                             hipStream_t stream) {
+    gdn_status st = check_desc_common(d);
+    if (st != GDN_OK) return st;
+    const int64_t N = d->num_seqs, Hk = d->num_k_heads, Hv = d->num_v_heads, D = num_draft;
+    if (D < 1 || D > GDN_MAX_DRAFT) return GDN_ERR_BAD_SHAPE;
+    if (!state_ckpt || !accepted || !state) return GDN_ERR_NULL_ARG;
+    if (num_state_slots < 1 || (state_slots == nullptr && num_state_slots < N)) return GDN_ERR_BAD_SHAPE;
+    const void* tensors[] = {state_ckpt, conv_ckpt, accepted, state, conv_state, state_slots};
+    for (const void* p : tensors)
+        if (p && !aligned16(p)) return GDN_ERR_MISALIGNED;
+    const size_t es = io_size(d->io_dtype), ss = io_size(d->state_dtype);
+    const size_t head = (size_t)gdn::kD * gdn::kD * ss;
+    const size_t cs = (size_t)(gdn::kConvK - 1) * (2 * Hk + Hv) * gdn::kD * es;
+    const Range rck(state_ckpt, (size_t)N * D * Hv * head), rcc(conv_ckpt, conv_ckpt ? N * D * cs : 0);
+    const Range rst(state, (size_t)num_state_slots * Hv * head), rcs(conv_state, conv_state ? num_state_slots * cs : 0);
+    if (rst.overlaps(rck) || rst.overlaps(rcc) || rcs.overlaps(rck) || rcs.overlaps(rcc) || rst.overlaps(rcs))
+        return GDN_ERR_ALIAS;
+    gdn::CommitArgs a{};
+    a.state_ckpt = state_ckpt; a.conv_ckpt = conv_ckpt; a.accepted = accepted;
+    a.state = state; a.conv_state = conv_state; a.slots = state_slots;
+    a.N = (int32_t)N; a.D = (int32_t)D; a.Hk = (int32_t)Hk; a.Hv = (int32_t)Hv;
+    const hipError_t e = gdn::launch_commit(a, d->io_dtype == GDN_BF16, d->state_dtype == GDN_BF16, stream);
+    return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
 }  // extern "C"

@@ -88,6 +88,22 @@ struct DecodeArgs {
     float scale, l2_eps, norm_eps;
 };
 
+// multi-token decode (verify) and commit
+struct VerifyArgs {
+    const void* q; const void* k; const void* v;
+    const float* g; const float* beta;
+    const void* z; const void* conv_w; const void* norm_w;
+    const void* state; const void* conv_state; const int32_t* slots;
+    void* state_ckpt; void* conv_ckpt; void* out;
+    int32_t N, D, Hk, Hv, use_l2;
+    float scale, l2_eps, norm_eps;
+};
+struct CommitArgs {
+    const void* state_ckpt; const void* conv_ckpt; const int32_t* accepted;
+    void* state; void* conv_state; const int32_t* slots;
+    int32_t N, D, Hk, Hv;
+};
+
 // Per-kernel timing when the caller asked for it: events[0] / events[1] on
 // the caller's stream at the start and end of the call, events[2 + 2 i] /
 // events[3 + 2 i] around kernel i on the stream it is launched on.
@@ -112,5 +128,7 @@ struct KernelRecorder {
 hipError_t launch_prefill(const PrefillPlan& p, hipStream_t stream, KernelRecorder& rec);
 hipError_t launch_decode(const DecodeArgs& a, bool io_bf16, bool state_bf16, bool conv,
                          hipStream_t stream);
+hipError_t launch_verify(const VerifyArgs& a, bool io_bf16, bool state_bf16, bool conv, hipStream_t s);
+hipError_t launch_commit(const CommitArgs& a, bool io_bf16, bool state_bf16, hipStream_t s);
 
 }  // namespace gdn

@@ -133,3 +133,47 @@ class DecodeCall:
                      out=self.out, z=self.z, conv_w=self.conv_w, norm_w=self.norm_w,
                      conv_state=self.conv_state, state_slots=self.slots,
                      num_state_slots=self.num_state_slots, stream=stream)
+
+
+class VerifyCall:
+    """Buffers of one gdn_decode_verify call: x holds the D draft tokens of each
+    of N sequences packed as a prefill of N sequences of length D (q [N*D, Hk,
+    128], ...), states [N or S, ...]."""
+
+    def __init__(self, x: dict, *, D: int, Hk: int, Hv: int, io_bf16: bool, state_bf16: bool,
+                 l2norm: bool = True, scale: float = 1.0, l2_eps: float = 1e-6,
+                 norm_eps: float = 1e-6, slots: Optional[np.ndarray] = None,
+                 num_state_slots: Optional[int] = None, want_conv_ckpt: bool = True, device="cuda"):
+        import torch
+        d = device
+        self.D = D
+        self.N = int(np.asarray(x["q"]).shape[0]) // D
+        self.q, self.k, self.v = (to_device(x[n], d) for n in ("q", "k", "v"))
+        self.g, self.beta = to_device(x["g"], d), to_device(x["beta"], d)
+        self.z, self.conv_w, self.norm_w = (to_device(x.get(n), d) for n in ("z", "conv_w", "norm_w"))
+        self.state = to_device(x["state"], d)
+        self.conv_state = to_device(x.get("conv_state"), d)
+        self.slots = to_device(None if slots is None else np.asarray(slots, np.int32), d)
+        self.num_state_slots = num_state_slots if num_state_slots is not None else self.state.shape[0]
+        self.desc = B.make_desc(self.N, self.N * D, Hk, Hv, B.GDN_BF16 if io_bf16 else B.GDN_F32,
+                                B.GDN_BF16 if state_bf16 else B.GDN_F32, scale, l2_eps, norm_eps,
+                                l2norm)
+        sdt = torch.bfloat16 if state_bf16 else torch.float32
+        self.state_ckpt = torch.empty((self.N, D, Hv, 128, 128), dtype=sdt, device=d)
+        Cch = 2 * Hk * 128 + Hv * 128
+        self.conv_ckpt = empty_like_io((self.N, D, 3, Cch), io_bf16, d) if want_conv_ckpt else None
+        self.out = empty_like_io((self.N * D, Hv, 128), io_bf16, d)
+
+    def run(self, stream=None):
+        B.gdn_decode_verify(self.desc, self.D, self.q, self.k, self.v, self.g, self.beta,
+                            state=self.state, state_ckpt=self.state_ckpt, out=self.out, z=self.z,
+                            conv_w=self.conv_w, norm_w=self.norm_w, conv_state=self.conv_state,
+                            conv_ckpt=self.conv_ckpt, state_slots=self.slots,
+                            num_state_slots=self.num_state_slots, stream=stream)
+
+    def commit(self, accepted: np.ndarray, stream=None):
+        acc = to_device(np.asarray(accepted, np.int32))
+        B.gdn_decode_commit(self.desc, self.D, state_ckpt=self.state_ckpt, accepted=acc,
+                            state=self.state, conv_ckpt=self.conv_ckpt, conv_state=self.conv_state,
+                            state_slots=self.slots, num_state_slots=self.num_state_slots,
+                            stream=stream)

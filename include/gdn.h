@@ -230,6 +230,51 @@ gdn_status gdn_decode(const gdn_desc* d,
                       const int32_t* state_slots, int32_t num_state_slots,
                       void* out, hipStream_t stream);
 
+/*
+ * Multi-token decode for speculative-decoding verify (SGLang cookbook,
+ * section 3.2: MTP / NEXTN with several draft tokens per step).  D new tokens
+ * per sequence (1 <= D <= GDN_MAX_DRAFT) run through the conv and the
+ * recurrence in order, starting from the cached state and conv state, which
+ * this call only reads.  The state and the conv window after every token are
+ * written as checkpoints, so that accepting the first j tokens is a copy of
+ * checkpoint j - 1 into the cache (gdn_decode_commit).  desc: num_seqs = N,
+ * total_tokens = N * D.
+ *   q, k           [N, D, Hk, dk] io dtype, raw
+ *   v, z           [N, D, Hv, dv] io dtype (z NULL together with norm_w)
+ *   g, beta        [N, D, Hv] fp32
+ *   conv_w, norm_w as in gdn_prefill
+ *   state          [S, Hv, dv, dk] state dtype, read only
+ *   conv_state     [S, K-1, Cch] io dtype, read only; NULL: zero history
+ *   state_slots    [N] int32 device or NULL (row n), as in gdn_decode
+ *   state_ckpt     [N, D, Hv, dv, dk] state dtype: the state after token j
+ *   conv_ckpt      [N, D, K-1, Cch] io dtype or NULL: the K-1 most recent
+ *                  raw tokens after token j (bit-exact copies of inputs)
+ *   out            [N, D, Hv, dv] io dtype
+ * Outputs must not overlap inputs (GDN_ERR_ALIAS).
+ */
+#define GDN_MAX_DRAFT 8
+gdn_status gdn_decode_verify(const gdn_desc* d, int32_t num_draft,
+                             const void* q, const void* k, const void* v,
+                             const float* g, const float* beta,
+                             const void* z, const void* conv_w, const void* norm_w,
+                             const void* state, const void* conv_state,
+                             const int32_t* state_slots, int32_t num_state_slots,
+                             void* state_ckpt, void* conv_ckpt, void* out,
+                             hipStream_t stream);
+
+/*
+ * Commit accepted draft tokens: for every sequence n with a_n = accepted[n]
+ * in 1..D, copy checkpoint a_n - 1 of state_ckpt (and of conv_ckpt, when both
+ * it and conv_state are non-NULL) into cache row state_slots[n] (NULL: n);
+ * a_n = 0 leaves the row as it is.  accepted: [N] int32 device; values
+ * outside 0..D are a precondition violation (the row is left as it is).
+ */
+gdn_status gdn_decode_commit(const gdn_desc* d, int32_t num_draft,
+                             const void* state_ckpt, const void* conv_ckpt,
+                             const int32_t* accepted, void* state, void* conv_state,
+                             const int32_t* state_slots, int32_t num_state_slots,
+                             hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

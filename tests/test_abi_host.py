@@ -208,3 +208,41 @@ def test_prefill_args_layout_matches_the_header(tmp_path):
                                           check=True).stdout.split()]
     want = [ctypes.sizeof(B.PrefillArgs)] + [getattr(B.PrefillArgs, f).offset for f in fields]
     assert got == want
+
+
+def test_verify_and_commit_validation_errors():
+    lib = gdn.lib()
+    P = _ptrs(15)
+
+    def verify(desc, D=4, **over):
+        names = ["q", "k", "v", "g", "beta", "z", "conv_w", "norm_w", "state", "cs", "slots",
+                 "ckpt", "cck", "out"]
+        vals = dict(zip(names, P))
+        vals["slots"] = None
+        vals.update(over)
+        ns = over.get("ns", desc.num_seqs)
+        return lib.gdn_decode_verify(ctypes.byref(desc), D, *[vals[n] for n in names[:11]], ns,
+                                     vals["ckpt"], vals["cck"], vals["out"], None)
+
+    d = B.make_desc(2, 8)
+    assert verify(d, D=0) == 2
+    assert verify(d, D=9) == 2
+    assert verify(B.make_desc(2, 7)) == 2                      # total_tokens != N * D
+    assert verify(d, q=None) == 1
+    assert verify(d, ckpt=None) == 1
+    assert verify(d, ns=1) == 2
+    assert verify(d, ckpt=FAKE + 8 * STEP) == 8                 # checkpoints alias the state
+    assert verify(d, out=FAKE + 11 * STEP) == 8                 # out aliases the checkpoints
+    assert verify(d, cck=FAKE + 12 * STEP + 4) == 5
+
+    def commit(desc, D=4, **over):
+        vals = dict(ckpt=P[0], cck=P[1], acc=P[2], state=P[3], cs=P[4], slots=None)
+        vals.update(over)
+        ns = over.get("ns", desc.num_seqs)
+        return lib.gdn_decode_commit(ctypes.byref(desc), D, vals["ckpt"], vals["cck"], vals["acc"],
+                                     vals["state"], vals["cs"], vals["slots"], ns, None)
+
+    assert commit(d, D=0) == 2
+    assert commit(d, acc=None) == 1
+    assert commit(d, state=P[0]) == 8                           # state pool aliases checkpoints
+    assert commit(d, ns=1) == 2
