@@ -242,6 +242,66 @@ def bench_decode(args, hip, cfg):
                          "frac": round((state_bytes + other) / t / HBM_PEAK, 4), "traffic": traffic}}
 
 
+def time_calls(hip, calls, steps, warmup):
+    """Average time of one call over `steps` rotating calls, HIP events on the stream."""
+    import torch
+    stream = torch.cuda.current_stream().cuda_stream
+    for i in range(warmup):
+        calls[i % len(calls)](stream)
+    torch.cuda.synchronize()
+    e0, e1 = hip.event(), hip.event()
+    hip.record(e0, stream)
+    for i in range(steps):
+        calls[i % len(calls)](stream)
+    hip.record(e1, stream)
+    torch.cuda.synchronize()
+    t = hip.ms(e0, e1) * 1e-3 / steps
+    hip.destroy(e0)
+    hip.destroy(e1)
+    return t
+
+
+def bench_options(args, hip, pres):
+    """C1 prefill with bf16 state storage in a state pool and a snapshot every
+    16 chunks (gdn_prefill_ex), and multi-token decode (verify) of 4 draft
+    tokens per sequence at the C4 shape, fp32 state."""
+    import numpy as np
+    import gdn_synth as gs
+    from gated_deltanet_layer_02_amd.tensors import PrefillCall, VerifyCall
+
+    p, x = pres["p"], pres["x"]
+    log("[bench] prefill with bf16 state pool and snapshots every 16 chunks")
+    xb = dict(x, state=gs.f32_to_bf16_bits(np.zeros((2, p.Hv, 128, 128), np.float32)))
+    calls = [PrefillCall(xb, Hk=p.Hk, Hv=p.Hv, io_bf16=True, state_bf16=True,
+                         slots=np.array([1], np.int32), num_state_slots=2, snapshot_every=16,
+                         snapshot_base=np.array([0], np.int32), num_snapshot_slots=3)
+             for _ in range(args.buffer_sets)]
+    t = time_calls(hip, [c.run for c in calls], args.steps, args.warmup)
+    opts = {"workload": "C1 prefill, bf16 state in a 2-row pool, snapshots every 16 chunks",
+            "us": round(t * 1e6, 2), "tokens_per_s": round(p.T / t, 1),
+            "vs_plain": round((p.T / t) / pres["tokens_per_s"], 4)}
+    del calls
+
+    D = 4
+    c4 = gs.configs()["C4"]
+    pv = gs.Problem("verify", [D] * c4.N, init_state_std=0.01, conv_state_std=0.01, seed=c4.seed)
+    log(f"[bench] verify: {c4.N} sequences x {D} draft tokens, fp32 state")
+    xv = gs.generate(pv)
+    vc = VerifyCall(xv, D=D, Hk=pv.Hk, Hv=pv.Hv, io_bf16=True, state_bf16=False)
+    t = time_calls(hip, [vc.run], max(5, args.steps // 2), 3)
+    state = pv.N * pv.Hv * 128 * 128 * 4                  # the batch's fp32 states
+    # state read once, D checkpoints written, conv window read, D conv checkpoints
+    # written, q, k, v, z, out of the D tokens
+    moved = state * (1 + D) + pv.N * 3 * pv.Cch * 2 * (1 + D) \
+        + (2 * pv.N * D * pv.Hk * 128 + 3 * pv.N * D * pv.Hv * 128) * 2
+    ver = {"workload": f"verify, {pv.N} sequences x {D} draft tokens, 16 key / 32 value heads, fp32 state",
+           "us": round(t * 1e6, 2), "tokens_per_s": round(pv.N * D / t, 1),
+           "roofline": {"bound": "hbm", "achieved": round(moved / t / 1e9, 1), "peak": HBM_PEAK / 1e9,
+                        "unit": "GB/s", "frac": round(moved / t / HBM_PEAK, 4),
+                        "bytes": moved}}
+    return {"prefill_pool_bf16_snapshots": opts, "verify": ver}
+
+
 def cpu_baseline(pres, target_s: float):
     """The fp64 oracle on the first S tokens of the same C1 inputs, all heads."""
     import numpy as np
@@ -288,6 +348,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=5.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-options", action="store_true",
+                    help="skip the prefill-options and verify legs")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a 512 MiB device-to-device copy first (counter calibration)")
     args = ap.parse_args()
@@ -315,6 +377,7 @@ def main():
     if not args.no_decode:
         dec = {"metric": "decode state GB/s", "fp32_state": bench_decode(args, hip, "C4"),
                "bf16_state": bench_decode(args, hip, "C4b")}
+    opts = None if args.no_options else bench_options(args, hip, pres)
     cpu = None if args.no_cpu_baseline else cpu_baseline(pres, args.cpu_seconds)
 
     p = pres["p"]
@@ -340,6 +403,7 @@ def main():
         "stages_us": pres["stages_us"],
         "path": pres["path"],
         "decode": dec,
+        "options": opts,
     }
     print(json.dumps(line), flush=True)
 
