@@ -183,6 +183,8 @@ def bench_prefill(args, hip):
         achieved, peak, unit, bound = FLOP_SWEEP * T * Hv / dom_s, MFMA_BF16_PEAK, "TFLOP/s", "mfma"
     elif dominant == "chunk_prep":
         achieved, peak, unit, bound = FLOP_PREP * T * Hv / dom_s, MFMA_BF16_PEAK, "TFLOP/s", "mfma"
+    elif dominant == "prep_sweep":   # prep and sweep in one launch
+        achieved, peak, unit, bound = (FLOP_PREP + FLOP_SWEEP) * T * Hv / dom_s, MFMA_BF16_PEAK, "TFLOP/s", "mfma"
     else:   # gated norm: reads o and z, writes out
         achieved, peak, unit, bound = 3 * T * Hv * D * 2 / dom_s, HBM_PEAK, "GB/s", "hbm"
     scale = 1e12 if unit == "TFLOP/s" else 1e9

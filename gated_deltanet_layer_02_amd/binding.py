@@ -18,7 +18,7 @@ GDN_F32, GDN_BF16 = 0, 1
 GDN_FLAG_L2NORM_QK = 0x1
 PREFILL_MAX_KERNELS = 64   # kernels a profiled call may record (the caller's choice)
 STAGE_NAMES = {0: "chunk_table", 1: "chunk_prep", 2: "state_sweep", 3: "gated_norm",
-               4: "conv_state"}
+               4: "conv_state", 5: "prep_sweep"}
 
 STATUS_NAMES = {0: "GDN_OK", 1: "GDN_ERR_NULL_ARG", 2: "GDN_ERR_BAD_SHAPE",
                 3: "GDN_ERR_UNSUPPORTED", 4: "GDN_ERR_BAD_DTYPE", 5: "GDN_ERR_MISALIGNED",
@@ -27,7 +27,7 @@ STATUS_NAMES = {0: "GDN_OK", 1: "GDN_ERR_NULL_ARG", 2: "GDN_ERR_BAD_SHAPE",
 
 EXPORTED = ["gdn_status_string", "gdn_prefill_workspace_size", "gdn_prefill",
             "gdn_prefill_profiled", "gdn_prefill_ex", "gdn_decode", "gdn_decode_verify",
-            "gdn_decode_commit"]
+            "gdn_decode_commit", "gdn_pipeline_timeouts"]
 
 
 class GdnError(RuntimeError):
@@ -112,6 +112,8 @@ def lib():
         l.gdn_decode_commit.argtypes = [dp, i32] + [vp] * 6 + [i32, vp]
         l.gdn_decode.restype = ctypes.c_int
         l.gdn_decode.argtypes = [dp] + [vp] * 11 + [i32, vp, vp]
+        l.gdn_pipeline_timeouts.restype = ctypes.c_int
+        l.gdn_pipeline_timeouts.argtypes = [ctypes.POINTER(ctypes.c_uint32)]
         _lib = l
     return _lib
 
@@ -121,6 +123,15 @@ def gdn_status_string(code: int) -> str:
         return lib().gdn_status_string(int(code)).decode()
     except RuntimeError:
         return STATUS_NAMES.get(int(code), f"status {code}")
+
+
+def gdn_pipeline_timeouts() -> int:
+    """Waits of pipelined prefill launches on the current device that gave up."""
+    n = ctypes.c_uint32(0)
+    rc = lib().gdn_pipeline_timeouts(ctypes.byref(n))
+    if rc != GDN_OK:
+        raise GdnError(rc, "gdn_pipeline_timeouts")
+    return int(n.value)
 
 
 def gdn_prefill_workspace_size(desc: Desc) -> int:

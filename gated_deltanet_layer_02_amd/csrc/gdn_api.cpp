@@ -4,6 +4,10 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
+#include <chrono>
+#include <random>
+
 #include <hip/hip_runtime.h>
 
 #include "../../include/gdn.h"
@@ -51,6 +55,20 @@ int64_t chunk_slots(const gdn_desc* d, bool varlen) {
     return d->total_tokens / gdn::kChunk + d->num_seqs;
 }
 
+// Epochs of pipelined launches: unique per call (a 64-bit counter from a
+// random start, never 0), so chunk flags left in a workspace by an earlier
+// call, or zeroed memory, never read as published.
+uint64_t next_epoch() {
+    static std::atomic<uint64_t> counter{[] {
+        std::random_device rd;
+        const uint64_t t = (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count();
+        return ((uint64_t)rd() << 32) ^ (uint64_t)rd() ^ (t * 0x9E3779B97F4A7C15ull);
+    }()};
+    uint64_t e;
+    do e = counter.fetch_add(1, std::memory_order_relaxed); while (e == 0);
+    return e;
+}
+
 PrefillLayout prefill_layout(const gdn_desc* d, bool varlen) {
     const size_t C = (size_t)chunk_slots(d, varlen);
     const size_t Hk = d->num_k_heads, Hv = d->num_v_heads;
@@ -62,6 +80,7 @@ PrefillLayout prefill_layout(const gdn_desc* d, bool varlen) {
     L.chunk_off = take(sizeof(int32_t) * ((size_t)d->num_seqs + 1));
     L.KB = take(C * Hk * gdn::kKBUnits * frag);
     L.VB = take(C * Hv * gdn::kVBUnits * frag);
+    L.ready = take(C * Hk * sizeof(uint64_t));
     L.total = off;
     return L;
 }
@@ -153,6 +172,9 @@ gdn_status prefill_impl(const gdn_desc* d, const gdn_prefill_args& x, hipStream_
     s.out = x.out; s.cu = x.cu_seqlens; s.chunk_off = a.chunk_off;
     s.T = a.T; s.N = a.N; s.Hk = a.Hk; s.Hv = a.Hv;
 
+    p.sync.ready = reinterpret_cast<uint64_t*>(ws + L.ready);
+    p.sync.epoch = next_epoch();
+
     gdn::ConvStateArgs& c = p.conv_state;
     c.q = x.q; c.k = x.k; c.v = x.v;
     c.conv_state_in = x.conv_state_in; c.conv_state_out = x.conv_state_out; c.slots = x.state_slots;
@@ -183,6 +205,11 @@ gdn_prefill_args flat_args(const void* q, const void* k, const void* v, const fl
 }  // namespace
 
 extern "C" {
+
+gdn_status gdn_pipeline_timeouts(uint32_t* count) {
+    if (count == nullptr) return GDN_ERR_NULL_ARG;
+    return gdn::read_pipe_timeouts(count) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
 
 const char* gdn_status_string(gdn_status s) {
     switch (s) {

@@ -56,6 +56,24 @@ struct SweepArgs {
     int32_t T, N, Hk, Hv;
 };
 
+// Prep-to-sweep hand-off of a pipelined launch (prep and sweep in one grid):
+// ready[c * Hk + hk] == epoch once prep unit (chunk slot c, key head hk) is
+// published.  ready == NULL: no pipelined launch for this call.
+struct PipeSync {
+    uint64_t* ready = nullptr;
+    uint64_t epoch = 0;
+};
+
+// Pipelined launch: workgroups [0, n_sweep) run the sweep (the sweep's own
+// grid mapping), the rest run two prep units each (prep_xcd: units are dealt
+// so that a key head's units land on the XCD of its sweep workgroups).
+struct PipeArgs {
+    PrepArgs prep;
+    SweepArgs sweep;
+    PipeSync sync;
+    int32_t n_sweep, chunk_slots, prep_xcd;
+};
+
 struct ConvStateArgs {
     const void* q; const void* k; const void* v;
     const void* conv_state_in; void* conv_state_out;
@@ -71,11 +89,12 @@ struct PrefillPlan {
     PrepArgs prep;
     SweepArgs sweep;
     ConvStateArgs conv_state;
+    PipeSync sync;                // flags of a pipelined launch (bf16 layer)
 };
 
 // Workspace carve-up of one prefill call.
 struct PrefillLayout {
-    size_t chunk_off, KB, VB, total;
+    size_t chunk_off, KB, VB, ready, total;
 };
 
 struct DecodeArgs {
@@ -126,6 +145,7 @@ struct KernelRecorder {
 };
 
 hipError_t launch_prefill(const PrefillPlan& p, hipStream_t stream, KernelRecorder& rec);
+hipError_t read_pipe_timeouts(uint32_t* count);
 hipError_t launch_decode(const DecodeArgs& a, bool io_bf16, bool state_bf16, bool conv,
                          hipStream_t stream);
 hipError_t launch_verify(const VerifyArgs& a, bool io_bf16, bool state_bf16, bool conv, hipStream_t s);

@@ -26,6 +26,9 @@
 //   gdn_conv_state_kernel       conv state out (when requested)
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <cstdlib>
+
 #include "gdn_common.hpp"
 #include "gdn_internal.hpp"
 
@@ -241,21 +244,65 @@ __device__ __forceinline__ f32x4 mm16_acc(const float* X, int ldx, const f32x4& 
     return acc;
 }
 
-template <class IO, bool kConv>
-__global__ __launch_bounds__(256, 2) void gdn_chunk_prep_kernel(PrepArgs a) {
+// Stores of the prep's results.  Coherent (kCo): agent-scope stores (sc1),
+// written through to memory and visible to every XCD once complete, so a
+// pipelined launch publishes a unit with a vmcnt wait per wave instead of
+// an L2 write-back (which flushes every dirty line of the XCD's L2 and
+// doubled the prep's time when eight waves per workgroup issued it).
+template <bool kCo> struct PrepStore;
+template <> struct PrepStore<false> {
+    template <class MT>
+    static __device__ __forceinline__ void frag(Frag<MT>* base, int lane, const Frag<MT>& f) {
+        frag_store(base + lane, f);
+    }
+    static __device__ __forceinline__ void f32(float* base, int i, float x) { base[i] = x; }
+    template <class MT>
+    static __device__ __forceinline__ void four(MT* base, int i, const f32x4& x) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) base[i + r] = static_cast<MT>(x[r]);
+    }
+};
+// Coherent form: buffer stores with the sc1 cache-policy bit on a resource
+// built from a uniform base (64 KB range; every offset used is below it).
+template <> struct PrepStore<true> {
+    static constexpr int kSc1 = 16;
+    static __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(void* base) {
+        return __builtin_amdgcn_make_buffer_rsrc(base, 0, 0x10000, 0x00020000);
+    }
+    static __device__ __forceinline__ void frag(Frag<bf16>* base, int lane, const Frag<bf16>& f) {
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f.v), rsrc(base), lane * 16, 0, kSc1);
+    }
+    static __device__ __forceinline__ void f32(float* base, int i, float x) {
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), rsrc(base), i * 4, 0, kSc1);
+    }
+    static __device__ __forceinline__ void four(bf16* base, int i, const f32x4& x) {
+        typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        const bf16x4 v = {static_cast<bf16>(x[0]), static_cast<bf16>(x[1]), static_cast<bf16>(x[2]),
+                          static_cast<bf16>(x[3])};
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), rsrc(base), i * 2, 0, kSc1);
+    }
+};
+
+// One prep unit: chunk slot c of key head hk, run by 256 threads (tid
+// 0..255, four waves) on the LDS at smem.  Returns false for slots past the
+// last chunk (nothing is written).  Every thread of the unit passes the same
+// barriers, so two units can share one workgroup.
+template <class IO, bool kConv, bool kCo = false>
+__device__ __forceinline__ bool prep_unit(const PrepArgs& a, int c, int hk, unsigned char* smem, int tid) {
     typedef typename MathOf<IO>::T MT;
     typedef Frag<MT> F;
     typedef PrepSmem<MT> Smem;
-    extern __shared__ __attribute__((aligned(16))) unsigned char gdn_prep_smem[];
-    Smem& sm = *reinterpret_cast<Smem*>(gdn_prep_smem);
+    typedef PrepStore<kCo> St;
+    Smem& sm = *reinterpret_cast<Smem*>(smem);
     constexpr int LD = Smem::kLdA;
 
-    const int c = blockIdx.x, hk = blockIdx.y;
     int n, t0, len, seq_start;
-    if (!locate_chunk(a, c, n, t0, len, seq_start)) return;
+    if (!locate_chunk(a, c, n, t0, len, seq_start)) return false;
     const int crow = a.slots ? a.slots[n] : n;   // conv-state row of the sequence
 
-    const int tid = threadIdx.x, lane = tid & 63;
+    const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, g4 = lane >> 4;
     const int cg = tid & 15, tq = 4 * (tid >> 4);     // 8 channels, 4 tokens per thread
@@ -326,7 +373,7 @@ __global__ __launch_bounds__(256, 2) void gdn_chunk_prep_kernel(PrepArgs a) {
     __syncthreads();
 
     // ---- 2. Q and K^T fragments for the sweep; K K^T and K Q^T ----
-    F* KB = static_cast<F*>(a.KB) + ((size_t)c * Hk + hk) * kKBUnits * 64 + lane;
+    F* KB = static_cast<F*>(a.KB) + ((size_t)c * Hk + hk) * kKBUnits * 64;   // unit base (uniform)
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
         const int fi = wave * 4 + f;
@@ -335,14 +382,14 @@ __global__ __launch_bounds__(256, 2) void gdn_chunk_prep_kernel(PrepArgs a) {
             F fr;
 #pragma unroll
             for (int j = 0; j < 8; ++j) fr.v[j] = sm.qa.q[row][kb + kidx(g4, j)];
-            frag_store(KB + (kKB_Q + fi) * 64, fr);
+            St::frag(KB + (kKB_Q + fi) * 64, lane, fr);
         }
         {   // K^T: rows = dk (tile fi / 2), K = token block fi % 2
             const int row = 16 * (fi >> 1) + l16, kb = 32 * (fi & 1);
             F fr;
 #pragma unroll
             for (int j = 0; j < 8; ++j) fr.v[j] = sm.kt[row][kb + kidx(g4, j)];
-            frag_store(KB + (kKB_KT + fi) * 64, fr);
+            St::frag(KB + (kKB_KT + fi) * 64, lane, fr);
         }
     }
     f32x4 KK[4], KQ[4];
@@ -379,7 +426,7 @@ __global__ __launch_bounds__(256, 2) void gdn_chunk_prep_kernel(PrepArgs a) {
     for (int vh = 0; vh < group; ++vh) {
         const int h = hk * group + vh;
         const size_t cv = (size_t)c * Hv + h;
-        F* VB = static_cast<F*>(a.VB) + cv * kVBUnits * 64 + lane;
+        F* VB = static_cast<F*>(a.VB) + cv * kVBUnits * 64;   // unit base (uniform)
         float* gates = reinterpret_cast<float*>(static_cast<F*>(a.VB) + (cv * kVBUnits + kVB_G) * 64);
 
         // 3a. v: conv + SiLU, transposed into LDS; gates.  The next value
@@ -425,8 +472,8 @@ __global__ __launch_bounds__(256, 2) void gdn_chunk_prep_kernel(PrepArgs a) {
                 sm.G[lane] = G;
                 sm.b[lane] = bcur;
                 sm.bg[lane] = bcur * gam;
-                gates[lane] = gam;
-                gates[64 + lane] = exp_f32(Gn - G);
+                St::f32(gates, lane, gam);
+                St::f32(gates, 64 + lane, exp_f32(Gn - G));
             }
         }
         __syncthreads();
@@ -452,7 +499,7 @@ __global__ __launch_bounds__(256, 2) void gdn_chunk_prep_kernel(PrepArgs a) {
                     const float x = KQ[2 * p + (j >> 2)][j & 3];
                     fr.set(j, (i <= t) ? x * exp_f32(Gt - sm.G[i]) : 0.f);
                 }
-                frag_store(VB + (kVB_P + pfrag_index(wave, p)) * 64, fr);
+                St::frag(VB + (kVB_P + pfrag_index(wave, p)) * 64, lane, fr);
             }
         }
         __syncthreads();
@@ -527,7 +574,7 @@ __global__ __launch_bounds__(256, 2) void gdn_chunk_prep_kernel(PrepArgs a) {
             }
 #pragma unroll
             for (int pk = 0; pk < 4; ++pk)   // stored negated: the sweep adds (-W) S^T to U~
-                frag_store(VB + (kVB_W + wave * 4 + pk) * 64, acc_to_frag<MT>(-Wt[2 * pk], -Wt[2 * pk + 1]));
+                St::frag(VB + (kVB_W + wave * 4 + pk) * 64, lane, acc_to_frag<MT>(-Wt[2 * pk], -Wt[2 * pk + 1]));
 #pragma unroll
             for (int nt = 0; nt < 8; ++nt) {
                 f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -540,13 +587,19 @@ __global__ __launch_bounds__(256, 2) void gdn_chunk_prep_kernel(PrepArgs a) {
                     mma(acc, au[p], bfr);
                 }
                 // lane (dv, g4) holds U~[16 wave + 4 g4 + r][16 nt + l16]
-                MT* dst = reinterpret_cast<MT*>(VB + (kVB_U + 2 * nt + (wave >> 1)) * 64) + (wave & 1) * 4;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) dst[r] = static_cast<MT>(acc[r]);
+                St::four(reinterpret_cast<MT*>(VB + (kVB_U + 2 * nt + (wave >> 1)) * 64), 8 * lane + (wave & 1) * 4,
+                         acc);
             }
         }
         __syncthreads();
     }
+    return true;
+}
+
+template <class IO, bool kConv>
+__global__ __launch_bounds__(256, 2) void gdn_chunk_prep_kernel(PrepArgs a) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char gdn_prep_smem[];
+    prep_unit<IO, kConv>(a, blockIdx.x, blockIdx.y, gdn_prep_smem, threadIdx.x);
 }
 
 // ===========================================================================
@@ -766,7 +819,7 @@ __device__ __forceinline__ void store_o(IO* out, const f32x4 (&O)[4], int t0, in
 // (u < 32), VB unit u - 32 (u < 56) or U~ unit u - 56 of the workgroup's
 // tiles; producer p copies units p, p + PW, ...  Addresses are a uniform base
 // plus a 32-bit per-lane byte offset (the scalar-base form of the copy).
-template <int SW, int NT, int PW>
+template <int SW, int NT, int PW, int kAux>
 __device__ __forceinline__ void sweep_issue(const SweepArgs& a, size_t ck, size_t cv, int sg, int p,
                                             int lane, lds_b16x8* __restrict__ buf) {
     constexpr int kUnits = SweepLds<SW, NT>::kUnits;
@@ -780,7 +833,7 @@ __device__ __forceinline__ void sweep_issue(const SweepArgs& a, size_t ck, size_
         const int u0 = i * PW;
         const char* src = u0 < kLdsW ? kb + u0 * 1024 : u0 < kLdsU ? vb + (u0 - kLdsW) * 1024
                                                                    : ub + (u0 - kLdsU) * 1024;
-        __builtin_amdgcn_global_load_lds(src + lo, buf + (u0 + p) * 64, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(src + lo, buf + (u0 + p) * 64, 16, 0, kAux);
     }
 }
 
@@ -825,21 +878,53 @@ __device__ __forceinline__ void sweep_lds_step(const SweepArgs& a, const SweepSe
         G[63]);
 }
 
+// Chunk hand-off inside a pipelined launch.  The prep unit of (chunk slot c,
+// key head hk) stores `epoch` to ready[c * Hk + hk] after its fragments are
+// visible at agent scope (every wave's release fence, then a barrier, then
+// the flag).  A sweep producer wave reads the flag with an agent-scope load
+// and then copies the fragments with agent-coherent (sc1) loads, which do not
+// hit a stale copy in any cache.  Epochs are unique per call, so the flags
+// never need clearing.  Waits are bounded: after about 2^28 ticks of the
+// 100 MHz wall clock (2.7 s) a wait gives up, counts itself in
+// gdn_pipe_timeouts and carries on (the call's result is then invalid).
+__device__ uint32_t gdn_pipe_timeouts;
+constexpr uint64_t kPipeWaitTicks = 1ull << 28;
+constexpr int kCoherentLoad = 16;   // cache-policy bits of an agent-coherent load (sc1)
+
+__device__ __forceinline__ uint64_t pipe_flag(const uint64_t* f) {
+    return __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// true once *f == epoch; false (counted) when the wait gives up
+__device__ __noinline__ bool pipe_wait(const uint64_t* f, uint64_t epoch) {
+    const uint64_t t0 = wall_clock64();
+    while (pipe_flag(f) != epoch) {
+        __builtin_amdgcn_s_sleep(2);
+        if (wall_clock64() - t0 > kPipeWaitTicks) {
+            if ((threadIdx.x & 63) == 0)
+                __hip_atomic_fetch_add(&gdn_pipe_timeouts, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return false;
+        }
+    }
+    return true;
+}
+
 // Workgroup = SW compute waves (NT state tiles each) + PW producer waves.
 // Each chunk step has one barrier: producers wait for their copies into the
 // current buffer, everyone meets at the barrier, then producers copy the next
 // chunk into the other buffer while the compute waves work on this one.  The
 // compute waves never issue a copy, so copy issue never stalls the chain of
-// state updates.
-template <int SW, int NT, int PW>
-__global__ __launch_bounds__(64 * (SW + PW)) void gdn_state_sweep_lds_kernel(SweepArgs a) {
+// state updates.  In a pipelined launch (kPipe) the producers also wait for
+// each chunk's prep unit; the flag of chunk j + 1 is read while chunk j's
+// copies are in flight, so a chunk that is already published costs no extra
+// round trip.
+template <int SW, int NT, int PW, bool kPipe>
+__device__ __forceinline__ void sweep_wg(const SweepArgs& a, int x, unsigned char* smem, const PipeSync& ps) {
     typedef SweepLds<SW, NT> L;
-    extern __shared__ __attribute__((aligned(16))) unsigned char gdn_sweep_smem[];
-    lds_b16x8* buf0 = (lds_b16x8*)(gdn_sweep_smem);   // generic -> LDS address space
+    lds_b16x8* buf0 = (lds_b16x8*)(smem);   // generic -> LDS address space
     lds_b16x8* buf1 = buf0 + L::kUnits * 64;
 
     int u, sg;
-    if (!sweep_unit(blockIdx.x, L::kGroups, a.N, a.Hk, a.Hv, u, sg)) return;
+    if (!sweep_unit(x, L::kGroups, a.N, a.Hk, a.Hv, u, sg)) return;
     const int n = u / a.Hv, h = u % a.Hv, hk = h / (a.Hv / a.Hk);
     // the wave index is uniform; readfirstlane lets the compiler keep it in an SGPR
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -848,14 +933,24 @@ __global__ __launch_bounds__(64 * (SW + PW)) void gdn_state_sweep_lds_kernel(Swe
 
     if (wave >= SW) {   // producer
         const int p = wave - SW;
+        const uint64_t* ready = kPipe ? ps.ready + hk : nullptr;   // + c * Hk
+        // after a wait gives up, the wave stops waiting (the call is invalid
+        // anyway) so that it still ends within one wait's bound
+        bool live = true;
+        if (kPipe && q.nch > 0) live = pipe_wait(ready + (size_t)q.c_begin * a.Hk, ps.epoch);
         for (int j = 0; j < q.nch; ++j) {
             const size_t c = (size_t)q.c_begin + j;
-            sweep_issue<SW, NT, PW>(a, c * a.Hk + hk, c * a.Hv + h, sg, p, lane, (j & 1) ? buf1 : buf0);
+            uint64_t ahead = 0;
+            if (kPipe && j + 1 < q.nch) ahead = pipe_flag(ready + (c + 1) * a.Hk);
+            sweep_issue<SW, NT, PW, kPipe ? kCoherentLoad : 0>(a, c * a.Hk + hk, c * a.Hv + h, sg, p, lane,
+                                                               (j & 1) ? buf1 : buf0);
             __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): these copies have landed
             __syncthreads();                      // consumers may read buffer j & 1
             asm volatile("" ::: "memory");
             // the next issue overwrites the other buffer, which the compute
             // waves finished with before this barrier
+            if (kPipe && live && j + 1 < q.nch && ahead != ps.epoch)
+                live = pipe_wait(ready + (c + 1) * a.Hk, ps.epoch);
         }
         return;
     }
@@ -889,6 +984,12 @@ __global__ __launch_bounds__(64 * (SW + PW)) void gdn_state_sweep_lds_kernel(Swe
                     q.L - (q.nch - 1) * kChunk, a.Hv, h, s0 + nt, l16, g4);
     }
     if (a.final_state != nullptr) state_put<NT>(a.final_state, a, row, h, s0, S, l16, g4);
+}
+
+template <int SW, int NT, int PW>
+__global__ __launch_bounds__(64 * (SW + PW)) void gdn_state_sweep_lds_kernel(SweepArgs a) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char gdn_sweep_smem[];
+    sweep_wg<SW, NT, PW, false>(a, blockIdx.x, gdn_sweep_smem, PipeSync{});
 }
 
 // fp32 operands: the same sweep with operands read straight from memory
@@ -998,13 +1099,76 @@ __global__ __launch_bounds__(256) void gdn_conv_state_kernel(ConvStateArgs a) {
 }
 
 // ===========================================================================
-// host-side launch sequence
+// prep and sweep in one launch
+//
+// The sweep runs on Hv * 8 / (SW * NT) workgroups per sequence, a quarter of
+// the chip for one sequence of the 32-head layer, while the prep is spread
+// over every CU.  Launched one after the other, the prep's CUs idle through
+// the whole sweep.  Here workgroups [0, n_sweep) are the sweep (they start
+// first and wait for each chunk's flag) and the rest run prep units, two per
+// workgroup (256 threads each, on separate LDS), chunk-major, so the sweep
+// trails the prep by about one unit's latency and reads fragments that were
+// written moments before.
+//
+// No deadlock: prep units never wait, and the host launches this form only
+// when the sweep workgroups (one per CU: the LDS footprint is above half a
+// CU's) take at most half of the device's CUs.
 // ===========================================================================
-// bf16 sweep: 4 waves x 2 tiles = one head per workgroup (one copy of the
-// chunk operands per head and chunk; each LDS fragment feeds two MFMAs).
+// bf16 sweep: 4 compute waves of one 16-row tile each + 4 producer waves; two
+// workgroups per head.
 constexpr int kSweepSW = 4, kSweepNT = 1, kSweepPW = 4;
 typedef SweepLds<kSweepSW, kSweepNT> SweepCfg;
+constexpr unsigned kPipePrepStride = (sizeof(PrepSmem<bf16>) + 255) / 256 * 256;
+constexpr unsigned kPipeSmem =
+    2 * kPipePrepStride > (unsigned)SweepCfg::kBytes ? 2 * kPipePrepStride : (unsigned)SweepCfg::kBytes;
+static_assert(kPipeSmem <= 160 * 1024, "fits one CU's LDS");
+static_assert(kPipeSmem > 80 * 1024, "one workgroup per CU");
 
+// Prep unit of half `half` of prep workgroup b.  With prep_xcd (Hk a multiple
+// of 8) workgroup b sits on XCD b % 8 (workgroups are dealt to the 8 XCDs
+// round-robin; n_sweep is a multiple of 8) and takes units of the key heads
+// hk = b (mod 8), which the sweep also keeps on that XCD; otherwise units go
+// chunk-major over all key heads.
+__device__ __forceinline__ void pipe_prep_unit(const PipeArgs& a, int b, int half, int& c, int& hk) {
+    const int Hk = a.prep.Hk;
+    if (a.prep_xcd) {
+        const int per = Hk >> 3;
+        const int ui = 2 * (b >> 3) + half;
+        c = ui / per;
+        hk = (b & 7) + 8 * (ui % per);
+    } else {
+        const int ui = 2 * b + half;
+        c = ui / Hk;
+        hk = ui % Hk;
+    }
+}
+
+template <bool kConv>
+__global__ __launch_bounds__(512) void gdn_prefill_pipe_kernel(PipeArgs a) {
+    static_assert(64 * (kSweepSW + kSweepPW) == 512, "a sweep workgroup fills the launch");
+    extern __shared__ __attribute__((aligned(16))) unsigned char gdn_pipe_smem[];
+    if ((int)blockIdx.x < a.n_sweep) {
+        sweep_wg<kSweepSW, kSweepNT, kSweepPW, true>(a.sweep, blockIdx.x, gdn_pipe_smem, a.sync);
+        return;
+    }
+    // uniform per wave: an SGPR, so the unit's LDS base stays scalar
+    const int half = __builtin_amdgcn_readfirstlane(threadIdx.x >> 8), tid = threadIdx.x & 255;
+    int c, hk;
+    pipe_prep_unit(a, blockIdx.x - a.n_sweep, half, c, hk);
+    if (c >= a.chunk_slots) return;
+    if (!prep_unit<uint16_t, kConv, true>(a.prep, c, hk, gdn_pipe_smem + half * kPipePrepStride, tid)) return;
+    // publish: every wave's agent-scope stores have completed (vmcnt counts
+    // stores on this architecture), then one flag
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    __syncthreads();
+    if (tid == 0)
+        __hip_atomic_store(a.sync.ready + (size_t)c * a.prep.Hk + hk, a.sync.epoch, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ===========================================================================
+// host-side launch sequence
+// ===========================================================================
 // Dynamic LDS above 64 KB must be allowed per kernel; done once per kernel.
 static hipError_t allow_dynamic_lds(const void* kern, unsigned bytes) {
     static const hipError_t bf16_conv = hipFuncSetAttribute(
@@ -1022,9 +1186,15 @@ static hipError_t allow_dynamic_lds(const void* kern, unsigned bytes) {
     static const hipError_t sweep = hipFuncSetAttribute(
         reinterpret_cast<const void*>(gdn_state_sweep_lds_kernel<kSweepSW, kSweepNT, kSweepPW>),
         hipFuncAttributeMaxDynamicSharedMemorySize, SweepCfg::kBytes);
+    static const hipError_t pipe_conv = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(gdn_prefill_pipe_kernel<true>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, kPipeSmem);
+    static const hipError_t pipe_noconv = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(gdn_prefill_pipe_kernel<false>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, kPipeSmem);
     (void)kern;
     (void)bytes;
-    for (hipError_t e : {bf16_conv, bf16_noconv, f32_conv, f32_noconv, sweep})
+    for (hipError_t e : {bf16_conv, bf16_noconv, f32_conv, f32_noconv, sweep, pipe_conv, pipe_noconv})
         if (e != hipSuccess) return e;
     return hipSuccess;
 }
@@ -1097,21 +1267,65 @@ static hipError_t launch_conv_state(const PrefillPlan& p, hipStream_t s) {
         if (e_ != hipSuccess) return e_;        \
     } while (0)
 
+// CUs of the current device (cached per device)
+static int device_cus() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0 && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+        cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+// The pipelined launch serves the bf16 layer when its sweep workgroups take
+// at most half of the CUs (so prep workgroups always find CUs) and the
+// environment does not turn it off (GDN_PREFILL_PIPELINE=0).
+static bool use_pipe(const PrefillPlan& p) {
+    if (!p.io_bf16 || p.sync.ready == nullptr || p.chunk_slots <= 0) return false;
+    const char* env = getenv("GDN_PREFILL_PIPELINE");
+    if (env != nullptr && env[0] == '0') return false;
+    return 2 * sweep_blocks(p) <= device_cus();
+}
+
+static hipError_t launch_pipe(const PrefillPlan& p, hipStream_t s) {
+    PipeArgs a;
+    a.prep = p.prep;
+    a.sweep = p.sweep;
+    a.sync = p.sync;
+    a.n_sweep = sweep_blocks(p);
+    a.chunk_slots = p.chunk_slots;
+    a.prep_xcd = p.prep.Hk % 8 == 0;
+    const int64_t units = (int64_t)p.chunk_slots * p.prep.Hk;
+    const int64_t prep_wgs = a.prep_xcd ? 8 * ((units / 8 + 1) / 2) : (units + 1) / 2;
+    GDN_TRY(allow_dynamic_lds(nullptr, 0));
+    auto kern = p.conv ? gdn_prefill_pipe_kernel<true> : gdn_prefill_pipe_kernel<false>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)(a.n_sweep + prep_wgs)), dim3(512), kPipeSmem, s, a);
+    return hipGetLastError();
+}
+
+
 template <class IO>
-static hipError_t run_serial(const PrefillPlan& p, hipStream_t s, KernelRecorder& rec) {
+static hipError_t run_serial(const PrefillPlan& p, bool pipe, hipStream_t s, KernelRecorder& rec) {
     if (p.prep.cu != nullptr) {
         GDN_TRY(rec.begin(GDN_STAGE_CHUNK_TABLE, s));
         GDN_TRY(launch_chunk_table(p, s));
         GDN_TRY(rec.end(s));
     }
-    if (p.chunk_slots > 0) {
-        GDN_TRY(rec.begin(GDN_STAGE_CHUNK_PREP, s));
-        GDN_TRY(launch_prep<IO>(p, p.chunk_slots, s));
+    if (pipe) {
+        GDN_TRY(rec.begin(GDN_STAGE_PIPELINE, s));
+        GDN_TRY(launch_pipe(p, s));
+        GDN_TRY(rec.end(s));
+    } else {
+        if (p.chunk_slots > 0) {
+            GDN_TRY(rec.begin(GDN_STAGE_CHUNK_PREP, s));
+            GDN_TRY(launch_prep<IO>(p, p.chunk_slots, s));
+            GDN_TRY(rec.end(s));
+        }
+        GDN_TRY(rec.begin(GDN_STAGE_STATE_SWEEP, s));
+        GDN_TRY(launch_sweep(p, s));
         GDN_TRY(rec.end(s));
     }
-    GDN_TRY(rec.begin(GDN_STAGE_STATE_SWEEP, s));
-    GDN_TRY(launch_sweep(p, s));
-    GDN_TRY(rec.end(s));
     if (p.gated && p.total_tokens > 0) {
         GDN_TRY(rec.begin(GDN_STAGE_GATED_NORM, s));
         GDN_TRY(launch_norm<IO>(p, 0, p.total_tokens, s));
@@ -1126,12 +1340,17 @@ static hipError_t run_serial(const PrefillPlan& p, hipStream_t s, KernelRecorder
 }
 
 hipError_t launch_prefill(const PrefillPlan& p, hipStream_t stream, KernelRecorder& rec) {
-    const int n = (p.prep.cu != nullptr) + (p.chunk_slots > 0) + 1 + (p.gated && p.total_tokens > 0) +
-                  (p.conv_state.conv_state_out != nullptr);
+    const bool pipe = use_pipe(p);
+    const int n = (p.prep.cu != nullptr) + (pipe ? 1 : (p.chunk_slots > 0) + 1) +
+                  (p.gated && p.total_tokens > 0) + (p.conv_state.conv_state_out != nullptr);
     if (rec.events != nullptr && n > rec.max) return hipErrorInvalidValue;
     GDN_TRY(rec.call_begin(stream));
-    GDN_TRY(p.io_bf16 ? run_serial<uint16_t>(p, stream, rec) : run_serial<float>(p, stream, rec));
+    GDN_TRY(p.io_bf16 ? run_serial<uint16_t>(p, pipe, stream, rec) : run_serial<float>(p, false, stream, rec));
     return rec.call_end(stream);
+}
+
+hipError_t read_pipe_timeouts(uint32_t* count) {
+    return hipMemcpyFromSymbol(count, HIP_SYMBOL(gdn_pipe_timeouts), sizeof(uint32_t), 0, hipMemcpyDeviceToHost);
 }
 
 }  // namespace gdn

@@ -92,6 +92,11 @@ typedef struct {
 /* Human-readable name of a status code (static storage). */
 const char* gdn_status_string(gdn_status s);
 
+/* Waits of pipelined prefill launches (see gdn_prefill) on the current
+ * device that gave up since the library was loaded: 0 unless work on other
+ * streams held every CU for seconds.  Synchronous (a device-to-host copy). */
+gdn_status gdn_pipeline_timeouts(uint32_t* count);
+
 /* Bytes of device workspace gdn_prefill needs for descriptor d (a bound that
  * depends on N and T_total only through total_tokens / 64 + N chunks). */
 gdn_status gdn_prefill_workspace_size(const gdn_desc* d, size_t* bytes);
@@ -119,6 +124,14 @@ gdn_status gdn_prefill_workspace_size(const gdn_desc* d, size_t* bytes);
  * Zero-length sequences pass their states through.  Any other overlap
  * between outputs and inputs is GDN_ERR_ALIAS (out against q, k, v, z) or
  * undefined.
+ *
+ * Launches: with bf16 io, when the sweep's workgroups need at most half of
+ * the device's CUs (one or a few long sequences), the chunk prep and the
+ * sweep run as one launch whose sweep workgroups wait for each chunk's prep
+ * (bounded waits; GDN_PREFILL_PIPELINE=0 in the environment selects separate
+ * launches).  Work on other streams running beside such a call must leave it
+ * CUs for its prep workgroups; a wait that gives up after about 2.7 s counts
+ * itself in gdn_pipeline_timeouts and leaves that call's result invalid.
  */
 gdn_status gdn_prefill(const gdn_desc* d,
                        const void* q, const void* k, const void* v,
@@ -144,7 +157,8 @@ enum {
     GDN_STAGE_CHUNK_PREP = 1,    /* conv, SiLU, L2, gates, K K^T, UT transform: W, U~, P */
     GDN_STAGE_STATE_SWEEP = 2,   /* sequential chunk sweep: U, O, state update */
     GDN_STAGE_GATED_NORM = 3,    /* z-gated RMSNorm of the output */
-    GDN_STAGE_CONV_STATE = 4     /* conv state out */
+    GDN_STAGE_CONV_STATE = 4,    /* conv state out */
+    GDN_STAGE_PIPELINE = 5       /* chunk prep and state sweep in one launch */
 };
 gdn_status gdn_prefill_profiled(const gdn_desc* d,
                                 const void* q, const void* k, const void* v,

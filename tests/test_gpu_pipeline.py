@@ -1,0 +1,171 @@
+"""The pipelined prefill launch (chunk prep and state sweep in one grid, with
+per-chunk flags between them) against separate launches of the same kernels
+(GDN_PREFILL_PIPELINE=0).  Both run the same arithmetic in the same order, so
+every output must match bit for bit; the pipelined result is also checked
+against the fp64 oracle.  Which form ran is read from the stage ids of a
+profiled call."""
+import ctypes
+import zlib
+
+import numpy as np
+import pytest
+
+import gdn_synth as gs
+from helpers import TOL_BF16, io_to_f64, rel_l2, say
+from oracle import oracle
+
+pytestmark = pytest.mark.gpu
+
+
+def _problem(name, lens, **kw):
+    base = dict(init_state_std=0.01, conv_state_std=0.01, seed=zlib.crc32(name.encode()) % 10000)
+    base.update(kw)
+    return gs.Problem(name, lens, **base)
+
+
+class _Events:
+    def __init__(self, n):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.ev = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            assert self.hip.hipEventCreate(ctypes.byref(e)) == 0
+            self.ev.append(e.value)
+
+    def close(self):
+        for e in self.ev:
+            self.hip.hipEventDestroy(e)
+
+
+def _stages(call):
+    import torch
+    from gated_deltanet_layer_02_amd.binding import STAGE_NAMES
+    ev = _Events(2 + 2 * 8)
+    ids = call.run_profiled(ev.ev, stream=torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    ev.close()
+    return [STAGE_NAMES[i] for i in ids]
+
+
+def _outputs(call, rows=None):
+    """Outputs of a call; of pool-shaped state outputs only `rows` (the slots:
+    the other rows of a freshly allocated pool are never written)."""
+    from gated_deltanet_layer_02_amd.tensors import to_host
+    res = {"out": to_host(call.out)[: call.T]}
+    for n in ("final_state", "conv_state_out", "snapshots"):
+        t = getattr(call, n, None)
+        if t is not None:
+            a = to_host(t)
+            res[n] = a[rows] if rows is not None and n != "snapshots" else a
+    return res
+
+
+def _run_both(p, x, monkeypatch, expect_pipe, **kw):
+    """Outputs of the pipelined and of the separate launches (two calls each,
+    on the same workspace, to cover flags left by an earlier call)."""
+    import torch
+    from gated_deltanet_layer_02_amd.tensors import PrefillCall
+    res = {}
+    for pipe in (True, False):
+        monkeypatch.setenv("GDN_PREFILL_PIPELINE", "1" if pipe else "0")
+        call = PrefillCall(x, Hk=p.Hk, Hv=p.Hv, io_bf16=True, **kw)
+        if not call.extended:
+            st = _stages(call)
+            say(f"  pipeline={int(pipe)}: stages {st}")
+            assert ("prep_sweep" in st) == (pipe and expect_pipe), st
+        rows = kw.get("slots")
+        call.run()
+        torch.cuda.synchronize()
+        first = _outputs(call, rows)
+        call.workspace.fill_(0xA5)   # garbage in the flags must not read as published
+        call.run()
+        torch.cuda.synchronize()
+        again = _outputs(call, rows)
+        for n in first:
+            assert np.array_equal(first[n], again[n]), (pipe, n)
+        res[pipe] = (first, call)
+    return res
+
+
+def _assert_same(res):
+    a, b = res[True][0], res[False][0]
+    assert a.keys() == b.keys()
+    for n in a:
+        assert np.array_equal(a[n], b[n]), f"{n} differs between pipelined and separate launches"
+
+
+CASES = [
+    # name, seq lens, heads (Hk, Hv), extra problem options, pipelined?
+    ("one-seq", [64 * 24 + 37], (16, 32), {}, True),
+    ("two-seqs", [64 * 9 + 5, 64 * 7], (16, 32), {}, True),
+    ("three-seqs", [64 * 3, 100, 64 * 2 + 1], (16, 32), {}, False),   # sweep > half the CUs
+    ("small-heads", [64 * 10 + 3], (2, 4), {}, True),                 # Hk not a multiple of 8
+    ("empty-seq", [200, 0, 130], (4, 8), {}, True),
+    ("no-conv-no-gate", [64 * 5 + 9], (2, 4), dict(conv=False, gate=False), True),
+    ("one-token", [1], (16, 32), {}, True),
+]
+
+
+@pytest.mark.parametrize("name,lens,heads,opts,expect_pipe", CASES, ids=[c[0] for c in CASES])
+def test_pipeline_matches_separate_launches(name, lens, heads, opts, expect_pipe, monkeypatch):
+    from gated_deltanet_layer_02_amd import binding as B
+    p = _problem(f"pipe-{name}", lens, Hk=heads[0], Hv=heads[1], **opts)
+    x = gs.generate(p)
+    say(f"pipeline case {name}: lens {lens} Hk={p.Hk} Hv={p.Hv} {opts}")
+    res = _run_both(p, x, monkeypatch, expect_pipe)
+    _assert_same(res)
+    # and the oracle (all heads up to 8, else a sample of 4)
+    hv = (0, p.Hv) if p.Hv <= 8 else (p.Hv - 4, p.Hv)
+    r_out, r_fs, r_cs = oracle.run_problem(p, x, heads=hv)
+    out = io_to_f64(res[True][0]["out"])
+    e_out = rel_l2(out[:, hv[0]:hv[1]], r_out) if p.T > 0 else 0.0
+    e_fs = rel_l2(res[True][0]["final_state"][:, hv[0]:hv[1]], r_fs)
+    say(f"  rel_l2 out {e_out:.2e} state {e_fs:.2e}")
+    assert e_out <= TOL_BF16 and e_fs <= TOL_BF16
+    assert np.array_equal(res[True][0]["conv_state_out"], r_cs)
+    assert B.gdn_pipeline_timeouts() == 0
+
+
+def test_pipeline_pool_bf16_state_snapshots(monkeypatch):
+    """State pool rows by slot, bf16 state storage and chunk snapshots through
+    the pipelined launch (the same shape's plain call is pipelined)."""
+    from gated_deltanet_layer_02_amd import binding as B
+    lens = [64 * 6 + 10, 64 * 4]
+    p = _problem("pipe-pool", lens, Hk=2, Hv=4)
+    x = gs.generate(p)
+    rows, slots = 5, np.array([3, 0], np.int32)
+    rng = np.random.default_rng(11)
+    x["state"] = gs.f32_to_bf16_bits((0.01 * rng.standard_normal((rows, p.Hv, 128, 128))).astype(np.float32))
+    x["conv_state"] = gs.f32_to_bf16_bits((0.01 * rng.standard_normal((rows, 3, p.Cch))).astype(np.float32))
+    every = 2
+    counts = [(L - 1) // (64 * every) for L in lens]
+    base = np.array([0, counts[0]], np.int32)
+    say(f"pipeline pool case: lens {lens}, slots {slots.tolist()}, snapshots {counts}")
+    res = _run_both(p, x, monkeypatch, True, state_bf16=True, slots=slots, num_state_slots=rows,
+                    snapshot_every=every, snapshot_base=base, num_snapshot_slots=sum(counts))
+    _assert_same(res)
+    # the same shape as a plain call takes the pipelined form
+    monkeypatch.setenv("GDN_PREFILL_PIPELINE", "1")
+    from gated_deltanet_layer_02_amd.tensors import PrefillCall
+    assert "prep_sweep" in _stages(PrefillCall(x | {"state": None, "conv_state": None}, Hk=p.Hk,
+                                               Hv=p.Hv, io_bf16=True))
+    xo = dict(x, state=x["state"][slots], conv_state=x["conv_state"][slots])
+    r_out, r_fs, r_cs = oracle.run_problem(p, xo)
+    out = io_to_f64(res[True][0]["out"])
+    fs = gs.bf16_bits_to_f32(res[True][0]["final_state"]).astype(np.float64)   # slot rows
+    assert rel_l2(out, r_out) <= TOL_BF16 and rel_l2(fs, r_fs) <= TOL_BF16
+    assert B.gdn_pipeline_timeouts() == 0
+
+
+def test_pipeline_c1_shape(monkeypatch):
+    """The 4096-token, 16 key / 32 value head layer: pipelined and separate
+    launches agree bit for bit."""
+    from gated_deltanet_layer_02_amd import binding as B
+    p = gs.configs()["C1"]
+    x = gs.generate(p)
+    say("pipeline case C1 shape")
+    res = _run_both(p, x, monkeypatch, True)
+    _assert_same(res)
+    assert B.gdn_pipeline_timeouts() == 0

@@ -47,8 +47,10 @@ def test_in_place_poisoned_side_stream():
     assert np.array_equal(to_host(call.conv_state_in), to_host(ref.conv_state_out))
 
 
-def test_profiled_brackets_every_kernel():
+@pytest.mark.parametrize("pipeline", [True, False])
+def test_profiled_brackets_every_kernel(pipeline, monkeypatch):
     import torch
+    monkeypatch.setenv("GDN_PREFILL_PIPELINE", "1" if pipeline else "0")
     from gated_deltanet_layer_02_amd.binding import STAGE_NAMES
     from gated_deltanet_layer_02_amd.tensors import PrefillCall
     T = 64 * 40
@@ -68,7 +70,8 @@ def test_profiled_brackets_every_kernel():
         events.append(e.value)
     ids = call.run_profiled(events, stream=torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
-    assert [STAGE_NAMES[i] for i in ids] == ["chunk_prep", "state_sweep", "gated_norm", "conv_state"]
+    first = ["prep_sweep"] if pipeline else ["chunk_prep", "state_sweep"]
+    assert [STAGE_NAMES[i] for i in ids] == first + ["gated_norm", "conv_state"]
 
     def ms(a, b):
         f = ctypes.c_float()
@@ -80,7 +83,7 @@ def test_profiled_brackets_every_kernel():
     # too few event slots: refused before anything is launched
     from gated_deltanet_layer_02_amd import binding as B
     with pytest.raises(B.GdnError):
-        call.run_profiled(events[:2 + 2 * 3], stream=torch.cuda.current_stream().cuda_stream)
+        call.run_profiled(events[:2 + 2 * (len(ids) - 1)], stream=torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     for e in events:
         hip.hipEventDestroy(e)
