@@ -81,6 +81,7 @@ PrefillLayout prefill_layout(const gdn_desc* d, bool varlen) {
     L.KB = take(C * Hk * gdn::kKBUnits * frag);
     L.VB = take(C * Hv * gdn::kVBUnits * frag);
     L.ready = take(C * Hk * sizeof(uint64_t));
+    L.oready = take(C * Hv * 8 * sizeof(uint64_t));
     L.total = off;
     return L;
 }
@@ -173,6 +174,7 @@ gdn_status prefill_impl(const gdn_desc* d, const gdn_prefill_args& x, hipStream_
     s.T = a.T; s.N = a.N; s.Hk = a.Hk; s.Hv = a.Hv;
 
     p.sync.ready = reinterpret_cast<uint64_t*>(ws + L.ready);
+    p.sync.oready = reinterpret_cast<uint64_t*>(ws + L.oready);
     p.sync.epoch = next_epoch();
 
     gdn::ConvStateArgs& c = p.conv_state;

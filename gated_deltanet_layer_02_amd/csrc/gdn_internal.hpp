@@ -56,11 +56,21 @@ struct SweepArgs {
     int32_t T, N, Hk, Hv;
 };
 
+struct ConvStateArgs {
+    const void* q; const void* k; const void* v;
+    const void* conv_state_in; void* conv_state_out;
+    const int32_t* cu; const int32_t* slots;
+    int32_t T, N, Hk, Hv;
+};
+
 // Prep-to-sweep hand-off of a pipelined launch (prep and sweep in one grid):
 // ready[c * Hk + hk] == epoch once prep unit (chunk slot c, key head hk) is
 // published.  ready == NULL: no pipelined launch for this call.
+// oready[(c * Hv + h) * 8 + tile] == epoch once the sweep's output of chunk
+// slot c, value head h, 16-row dv tile `tile` is stored (gated layer only).
 struct PipeSync {
     uint64_t* ready = nullptr;
+    uint64_t* oready = nullptr;
     uint64_t epoch = 0;
 };
 
@@ -70,16 +80,12 @@ struct PipeSync {
 struct PipeArgs {
     PrepArgs prep;
     SweepArgs sweep;
+    ConvStateArgs conv_state;     // conv_state_out == NULL: none
     PipeSync sync;
-    int32_t n_sweep, chunk_slots, prep_xcd;
+    const void* z; const void* norm_w; float norm_eps;   // z == NULL: no gated norm
+    int32_t n_sweep, n_prep, n_post, chunk_slots, prep_xcd;
 };
 
-struct ConvStateArgs {
-    const void* q; const void* k; const void* v;
-    const void* conv_state_in; void* conv_state_out;
-    const int32_t* cu; const int32_t* slots;
-    int32_t T, N, Hk, Hv;
-};
 
 struct PrefillPlan {
     bool io_bf16, conv, gated;
@@ -94,7 +100,7 @@ struct PrefillPlan {
 
 // Workspace carve-up of one prefill call.
 struct PrefillLayout {
-    size_t chunk_off, KB, VB, ready, total;
+    size_t chunk_off, KB, VB, ready, oready, total;
 };
 
 struct DecodeArgs {

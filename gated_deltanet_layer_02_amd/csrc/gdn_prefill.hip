@@ -26,6 +26,7 @@
 //   gdn_conv_state_kernel       conv state out (when requested)
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdlib>
 
@@ -616,14 +617,26 @@ __global__ __launch_bounds__(256, 2) void gdn_chunk_prep_kernel(PrepArgs a) {
 // LDS units of one chunk buffer: KB (Q, K^T), VB units 0..23 (W, P, gates),
 // then the U~ units of the workgroup's tiles.
 constexpr int kLdsQ = 0, kLdsKT = 16, kLdsW = 32, kLdsP = 48, kLdsG = 54, kLdsU = 56;
+// After the two operand buffers: three O staging slots.  A slot holds one
+// chunk's output of the workgroup's dv rows, dv-major ([rows][64 tokens],
+// row stride kStageLd bf16 = 136 B, so that the compute waves' 8-byte writes
+// of 16 rows spread over the banks).  Compute waves stage O of chunk j - 1
+// at step j; producer waves store it to memory two steps later (when no
+// wave writes that slot), off the chain of state updates.
 template <int SW, int NT>
 struct SweepLds {
     static constexpr int kGroups = 8 / (SW * NT);         // workgroups per head
     static constexpr int kUnits = kLdsU + 2 * SW * NT;    // 1 KB units per chunk buffer
-    static constexpr int kBytes = 2 * kUnits * 1024;      // double buffer
+    static constexpr int kOps = 2 * kUnits * 1024;        // double buffer
+    static constexpr int kRows = 16 * SW * NT;            // dv rows of the workgroup
+    static constexpr int kStageLd = 68;
+    static constexpr int kStage = kRows * kStageLd * 2;   // bytes per slot
+    static constexpr int kBytes = kOps + 3 * kStage;
 };
 
 typedef __attribute__((address_space(3))) bf16x8 lds_b16x8;
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+typedef __attribute__((address_space(3))) u16x4 lds_u16x4;
 typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
 typedef __attribute__((address_space(3))) float lds_f32;
 
@@ -814,6 +827,60 @@ __device__ __forceinline__ void store_o(IO* out, const f32x4 (&O)[4], int t0, in
         }
 }
 
+// O of a compute wave's NT tiles into a staging slot (4 tokens per 8-byte write)
+template <int SW, int NT>
+__device__ __forceinline__ void stage_o(lds_u16* slot, const f32x4 (&O)[NT][4], int wave, int l16, int g4) {
+    typedef SweepLds<SW, NT> L;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+            *reinterpret_cast<lds_u16x4*>(slot + (16 * (wave * NT + nt) + l16) * L::kStageLd + 16 * mt + 4 * g4) =
+                u16x4{f32_to_bf16_bits(O[nt][mt][0]), f32_to_bf16_bits(O[nt][mt][1]),
+                      f32_to_bf16_bits(O[nt][mt][2]), f32_to_bf16_bits(O[nt][mt][3])};
+}
+
+// Producer p's share of one staged chunk (t0, len valid tokens): 16-byte
+// pieces (token, 8 dv), 8 consecutive lanes per token row, so each token's
+// kRows * 2 bytes go out contiguous.  kCo: agent-coherent stores (sc1) for a
+// gated norm running in the same launch.
+// kFull: a whole chunk, every lane stores (the producer's wait counts on it).
+template <int SW, int NT, int PW, bool kCo, bool kFull>
+__device__ __forceinline__ void store_staged(const SweepArgs& a, const lds_u16* slot, int t0, int len, int h,
+                                             int sg, int p, int lane) {
+    typedef SweepLds<SW, NT> L;
+    constexpr int kPer = L::kRows / 8;                    // pieces per token
+    static_assert((64 * kPer) % (64 * PW) == 0, "pieces split evenly over the producers");
+    uint16_t* base = static_cast<uint16_t*>(a.out) + ((size_t)t0 * a.Hv + h) * kD + sg * L::kRows;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(base, 0, 0x7fffffff, 0x00020000);
+#pragma unroll
+    for (int k = 0; k < 64 * kPer / (64 * PW); ++k) {
+        const int piece = (k * PW + p) * 64 + lane;
+        const int t = piece / kPer, d8 = piece % kPer;
+        if (kFull || t < len) {
+            u16x8 v;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = slot[(8 * d8 + e) * L::kStageLd + t];
+            const uint32_t off = (uint32_t)t * (uint32_t)(a.Hv * kD) + 8 * d8;   // elements
+            if (kCo) {
+                typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, (int)(2 * off), 0, 16);
+            } else {
+                *reinterpret_cast<u16x8*>(base + off) = v;
+            }
+        }
+    }
+}
+
+// Output flag of the pipelined gated layer: producer p's stores of chunk c
+// have completed.  Flags (c, h, sg * PW + p): eight per chunk and head.
+__device__ __forceinline__ void publish_o(const PipeSync& ps, const SweepArgs& a, size_t c, int h, int k,
+                                          int lane) {
+    if (lane == 0)
+        __hip_atomic_store(ps.oready + (c * a.Hv + h) * 8 + k, ps.epoch, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Copies of chunk c's operands into an LDS buffer, issued by the PW
 // producer waves of the workgroup.  LDS unit u (1 KB) receives KB unit u
 // (u < 32), VB unit u - 32 (u < 56) or U~ unit u - 56 of the workgroup's
@@ -842,19 +909,13 @@ __device__ __forceinline__ void sweep_issue(const SweepArgs& a, size_t ck, size_
 // previous chunk's output (Oprev) is stored after the barrier, so its stores
 // complete behind this chunk's work.
 template <int SW, int NT>
-__device__ __forceinline__ void sweep_lds_step(const SweepArgs& a, const SweepSeq& q, int j, int h,
-                                               int sg, int wave, f32x4 (&S)[NT][8],
-                                               f32x4 (&Oprev)[NT][4], const lds_b16x8* __restrict__ cur) {
+__device__ __forceinline__ void sweep_lds_step(int j, int wave, f32x4 (&S)[NT][8], f32x4 (&Oprev)[NT][4],
+                                               const lds_b16x8* __restrict__ cur, lds_u16* stage) {
+    typedef SweepLds<SW, NT> L;
     const int lane = threadIdx.x & 63, l16 = lane & 15, g4 = lane >> 4;
-    const int s0 = (sg * SW + wave) * NT;   // first tile of this wave
     __syncthreads();                      // chunk j's operands are in cur; nxt is free
     asm volatile("" ::: "memory");
-    if (j > 0) {
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-            store_o(static_cast<uint16_t*>(a.out), Oprev[nt], q.seq_start + (j - 1) * kChunk, kChunk,
-                    a.Hv, h, s0 + nt, l16, g4);
-    }
+    if (j > 0) stage_o<SW, NT>(stage + ((j - 1) % 3) * (L::kStage / 2), Oprev, wave, l16, g4);
     const lds_b16x8* W = cur + kLdsW * 64 + lane;
     const lds_b16x8* Q = cur + kLdsQ * 64 + lane;
     const lds_b16x8* KT = cur + kLdsKT * 64 + lane;
@@ -908,20 +969,46 @@ __device__ __noinline__ bool pipe_wait(const uint64_t* f, uint64_t epoch) {
     return true;
 }
 
+// true once f[0 .. count) all equal epoch (each lane watches every 64th);
+// polls about every 0.3 us (these waits are not on the sweep's chain, and
+// fewer polls of the flag lines leave the memory channels to the sweep)
+__device__ __noinline__ bool pipe_wait_all(const uint64_t* f, int count, uint64_t epoch) {
+    const int lane = threadIdx.x & 63;
+    const uint64_t t0 = wall_clock64();
+    for (int base = 0; base < count; base += 64) {
+        const int i = base + lane;
+        while (!__all(i >= count || pipe_flag(f + i) == epoch)) {
+            __builtin_amdgcn_s_sleep(10);
+            if (wall_clock64() - t0 > kPipeWaitTicks) {
+                if (lane == 0)
+                    __hip_atomic_fetch_add(&gdn_pipe_timeouts, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                return false;
+            }
+        }
+    }
+    return true;
+}
+
 // Workgroup = SW compute waves (NT state tiles each) + PW producer waves.
 // Each chunk step has one barrier: producers wait for their copies into the
 // current buffer, everyone meets at the barrier, then producers copy the next
 // chunk into the other buffer while the compute waves work on this one.  The
 // compute waves never issue a copy, so copy issue never stalls the chain of
-// state updates.  In a pipelined launch (kPipe) the producers also wait for
-// each chunk's prep unit; the flag of chunk j + 1 is read while chunk j's
-// copies are in flight, so a chunk that is already published costs no extra
-// round trip.
+// state updates.  The producers also store the output: the compute waves
+// stage O of chunk j - 1 in LDS at step j, and producer iteration j stores
+// chunk j - 3 (16-byte stores, whole token rows), whose slot no wave writes
+// until after the next barrier; one extra barrier at the end hands over the
+// last staged chunk.  In a pipelined launch (kPipe) the producers also wait
+// for each chunk's prep unit (the flag of chunk j + 1 is read while chunk j's
+// copies are in flight, so a published chunk costs no extra round trip) and,
+// for a gated norm in the same launch, publish each chunk's output two
+// iterations after storing it.
 template <int SW, int NT, int PW, bool kPipe>
 __device__ __forceinline__ void sweep_wg(const SweepArgs& a, int x, unsigned char* smem, const PipeSync& ps) {
     typedef SweepLds<SW, NT> L;
     lds_b16x8* buf0 = (lds_b16x8*)(smem);   // generic -> LDS address space
     lds_b16x8* buf1 = buf0 + L::kUnits * 64;
+    lds_u16* stage = (lds_u16*)(smem + L::kOps);
 
     int u, sg;
     if (!sweep_unit(x, L::kGroups, a.N, a.Hk, a.Hv, u, sg)) return;
@@ -934,23 +1021,57 @@ __device__ __forceinline__ void sweep_wg(const SweepArgs& a, int x, unsigned cha
     if (wave >= SW) {   // producer
         const int p = wave - SW;
         const uint64_t* ready = kPipe ? ps.ready + hk : nullptr;   // + c * Hk
+        const bool pub = kPipe && ps.oready != nullptr;           // output flags
+        const int k = sg * PW + p;                                // this wave's output flag
+        auto slot = [&](int jj) { return stage + (jj % 3) * (L::kStage / 2); };
         // after a wait gives up, the wave stops waiting (the call is invalid
         // anyway) so that it still ends within one wait's bound
         bool live = true;
         if (kPipe && q.nch > 0) live = pipe_wait(ready + (size_t)q.c_begin * a.Hk, ps.epoch);
+        // Per iteration: copies of chunk j, then the stores of chunk j - 3,
+        // then vmcnt(kStores): loads and stores retire in order, so the copies
+        // have landed while the stores may still be in flight; they are
+        // complete after the next iteration's wait, and chunk j - 5's flag
+        // goes out here.
+        constexpr int kStores = 64 * (L::kRows / 8) / (64 * PW);   // 16-byte stores per lane and chunk
+        static_assert(kStores == 2, "the wait below allows two stores in flight");
         for (int j = 0; j < q.nch; ++j) {
             const size_t c = (size_t)q.c_begin + j;
             uint64_t ahead = 0;
             if (kPipe && j + 1 < q.nch) ahead = pipe_flag(ready + (c + 1) * a.Hk);
+            if (pub && j >= 5) publish_o(ps, a, c - 5, h, k, lane);
             sweep_issue<SW, NT, PW, kPipe ? kCoherentLoad : 0>(a, c * a.Hk + hk, c * a.Hv + h, sg, p, lane,
                                                                (j & 1) ? buf1 : buf0);
-            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): these copies have landed
-            __syncthreads();                      // consumers may read buffer j & 1
+            asm volatile("" ::: "memory");        // the stores stay behind the copies
+            // A bare barrier (no fence: a workgroup release would wait for the
+            // stores too); the waits before it cover what the consumers read.
+            if (j >= 3) {   // staged at step j - 2, complete before the last barrier
+                store_staged<SW, NT, PW, kPipe, true>(a, slot(j - 3), q.seq_start + (j - 3) * kChunk, kChunk, h,
+                                                      sg, p, lane);
+                asm volatile("" ::: "memory");
+                __builtin_amdgcn_s_waitcnt(0x0072);   // vmcnt(2) lgkmcnt(0): the copies have landed
+            } else {
+                __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+            }
+            __builtin_amdgcn_s_barrier();         // consumers may read buffer j & 1
             asm volatile("" ::: "memory");
             // the next issue overwrites the other buffer, which the compute
             // waves finished with before this barrier
             if (kPipe && live && j + 1 < q.nch && ahead != ps.epoch)
                 live = pipe_wait(ready + (c + 1) * a.Hk, ps.epoch);
+        }
+        if (q.nch > 0) {   // the last three chunks, once the compute waves staged the last one
+            __syncthreads();
+            asm volatile("" ::: "memory");
+            if (pub && q.nch >= 5) publish_o(ps, a, (size_t)q.c_begin + q.nch - 5, h, k, lane);
+            for (int jj = q.nch >= 3 ? q.nch - 3 : 0; jj < q.nch; ++jj)
+                store_staged<SW, NT, PW, kPipe, false>(a, slot(jj), q.seq_start + jj * kChunk,
+                                                       min(kChunk, q.L - jj * kChunk), h, sg, p, lane);
+            if (pub) {
+                __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+                for (int jj = q.nch >= 4 ? q.nch - 4 : 0; jj < q.nch; ++jj)
+                    publish_o(ps, a, (size_t)q.c_begin + jj, h, k, lane);
+            }
         }
         return;
     }
@@ -970,18 +1091,16 @@ __device__ __forceinline__ void sweep_wg(const SweepArgs& a, int x, unsigned cha
     f32x4 O[NT][4];
 #pragma unroll 1
     for (int j = 0; j < q.nch; j += 2) {
-        sweep_lds_step<SW, NT>(a, q, j, h, sg, wave, S, O, buf0);
+        sweep_lds_step<SW, NT>(j, wave, S, O, buf0, stage);
         state_snapshot<NT>(a, n, j, q.nch, h, s0, S, l16, g4);
         if (j + 1 < q.nch) {
-            sweep_lds_step<SW, NT>(a, q, j + 1, h, sg, wave, S, O, buf1);
+            sweep_lds_step<SW, NT>(j + 1, wave, S, O, buf1, stage);
             state_snapshot<NT>(a, n, j + 1, q.nch, h, s0, S, l16, g4);
         }
     }
-    if (q.nch > 0) {   // output of the last chunk
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-            store_o(static_cast<uint16_t*>(a.out), O[nt], q.seq_start + (q.nch - 1) * kChunk,
-                    q.L - (q.nch - 1) * kChunk, a.Hv, h, s0 + nt, l16, g4);
+    if (q.nch > 0) {   // stage the last chunk's output for the producers
+        stage_o<SW, NT>(stage + ((q.nch - 1) % 3) * (L::kStage / 2), O, wave, l16, g4);
+        __syncthreads();
     }
     if (a.final_state != nullptr) state_put<NT>(a.final_state, a, row, h, s0, S, l16, g4);
 }
@@ -1067,10 +1186,8 @@ __global__ __launch_bounds__(256) void gdn_gated_norm_kernel(IO* __restrict__ ou
 // conv state out: the K-1 most recent raw tokens of (conv state in, sequence)
 // ===========================================================================
 template <class IO>
-__global__ __launch_bounds__(256) void gdn_conv_state_kernel(ConvStateArgs a) {
+__device__ __forceinline__ void conv_state_channel(const ConvStateArgs& a, int n, int ch) {
     const int Cch = 2 * a.Hk * kD + a.Hv * kD;
-    const int ch = blockIdx.x * 256 + threadIdx.x;
-    const int n = blockIdx.y;
     if (ch >= Cch) return;
     const IO* q = static_cast<const IO*>(a.q);
     const IO* k = static_cast<const IO*>(a.k);
@@ -1096,6 +1213,11 @@ __global__ __launch_bounds__(256) void gdn_conv_state_kernel(ConvStateArgs a) {
     }
 #pragma unroll
     for (int j = 0; j < kConvK - 1; ++j) csout[(crow * (kConvK - 1) + j) * Cch + ch] = val[j];
+}
+
+template <class IO>
+__global__ __launch_bounds__(256) void gdn_conv_state_kernel(ConvStateArgs a) {
+    conv_state_channel<IO>(a, blockIdx.y, blockIdx.x * 256 + threadIdx.x);
 }
 
 // ===========================================================================
@@ -1143,12 +1265,113 @@ __device__ __forceinline__ void pipe_prep_unit(const PipeArgs& a, int b, int hal
     }
 }
 
+// Wave 0 of a post workgroup waits, the others meet it at a barrier; the
+// verdict goes through LDS word *box.
+__device__ __forceinline__ bool post_wait(const uint64_t* f, int count, uint64_t epoch, volatile int* box) {
+    if (threadIdx.x < 64) {
+        const bool ok = pipe_wait_all(f, count, epoch);
+        if (threadIdx.x == 0) *box = ok;
+    }
+    __syncthreads();
+    const bool ok = *box != 0;
+    __syncthreads();   // everyone has read the verdict before the next wait writes it
+    return ok;
+}
+
+// Gated norm, in place, of the rows of unit (chunk slot c, key head hk) once
+// the sweep has published them: out = o rsqrt(mean(o^2) + eps) w SiLU(z).
+// Rows 4 wave + g, + 32, ... (a row is 16 lanes x 8 channels; o is read with
+// coherent loads).  Returns false when the wait gave up.
+__device__ __forceinline__ bool pipe_norm_unit(const PipeArgs& a, int c, int hk, const float (&w)[8],
+                                               volatile int* box) {
+    int n, t0, len, seq_start;
+    if (!locate_chunk(a.prep, c, n, t0, len, seq_start)) return true;
+    const int Hv = a.prep.Hv, group = Hv / a.prep.Hk, h0 = hk * group;
+    if (!post_wait(a.sync.oready + ((size_t)c * Hv + h0) * 8, group * 8, a.sync.epoch, box)) return false;
+    uint16_t* out = static_cast<uint16_t*>(a.sweep.out) + (size_t)t0 * Hv * kD;
+    const uint16_t* z = static_cast<const uint16_t*>(a.z) + (size_t)t0 * Hv * kD;
+    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(out, 0, 0x7fffffff, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rz =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(z), 0, 0x7fffffff, 0x00020000);
+    const int l16 = threadIdx.x & 15;
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    constexpr int kB = 4;   // rows per lane in flight: all loads issued before any math
+    for (int r0 = threadIdx.x >> 4; r0 < len * group; r0 += 32 * kB) {
+        u32x4 ov[kB], zv[kB];
+        uint32_t e[kB];
+#pragma unroll
+        for (int b = 0; b < kB; ++b) {
+            const int r = r0 + 32 * b;
+            e[b] = (uint32_t)((r / group) * Hv + h0 + r % group) * kD + 8 * l16;   // element
+            if (r < len * group) {
+                ov[b] = __builtin_amdgcn_raw_buffer_load_b128(ro, (int)(2 * e[b]), 0, 16);   // coherent
+                zv[b] = __builtin_amdgcn_raw_buffer_load_b128(rz, (int)(2 * e[b]), 0, 0);
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < kB; ++b) {
+            if (r0 + 32 * b >= len * group) continue;
+            const u16x8 o8 = __builtin_bit_cast(u16x8, ov[b]), z8 = __builtin_bit_cast(u16x8, zv[b]);
+            float x[8];
+            float ss = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                x[i] = bf16_bits_to_f32(o8[i]);
+                ss = fmaf(x[i], x[i], ss);
+            }
+            const float rr = rsqrt_f32(row16_sum(ss) * (1.0f / kD) + a.norm_eps);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[i] = x[i] * rr * w[i] * silu_f32(bf16_bits_to_f32(z8[i]));
+            store8(out + e[b], x);
+        }
+    }
+    return true;
+}
+
+// Workgroups after the prep ones: gated norm units (chunk-major; with
+// prep_xcd, those of the key heads on this workgroup's XCD), then the conv
+// state out of sequence n once the prep units of its first chunk (the only
+// readers of conv_state_in, which it may overwrite) are published.
+__device__ void pipe_post(const PipeArgs& a, int w, volatile int* box) {
+    bool live = true;   // uniform over the workgroup
+    const int Hk = a.prep.Hk;
+    if (a.z != nullptr) {
+        float wv[8];
+        load8(static_cast<const uint16_t*>(a.norm_w) + 8 * (threadIdx.x & 15), wv);
+        if (a.prep_xcd) {
+            const int per = Hk >> 3, nw = a.n_post >> 3;
+            for (int ui = w >> 3; live && ui < a.chunk_slots * per; ui += nw)
+                live = pipe_norm_unit(a, ui / per, (w & 7) + 8 * (ui % per), wv, box);
+        } else {
+            for (int u = w; live && u < a.chunk_slots * Hk; u += a.n_post)
+                live = pipe_norm_unit(a, u / Hk, u % Hk, wv, box);
+        }
+    }
+    const ConvStateArgs& cs = a.conv_state;
+    if (cs.conv_state_out != nullptr) {
+        const int Cch = 2 * cs.Hk * kD + cs.Hv * kD, nblk = (Cch + 511) / 512;
+        for (int it = w; it < cs.N * nblk; it += a.n_post) {
+            const int n = it / nblk;
+            const int L = cs.cu ? cs.cu[n + 1] - cs.cu[n] : cs.T;
+            if (live && L > 0 && cs.conv_state_in != nullptr) {
+                const size_t c0 = cs.cu ? a.sweep.chunk_off[n] : 0;
+                live = post_wait(a.sync.ready + c0 * Hk, Hk, a.sync.epoch, box);
+            }
+            conv_state_channel<uint16_t>(cs, n, (it % nblk) * 512 + threadIdx.x);
+        }
+    }
+}
+
 template <bool kConv>
 __global__ __launch_bounds__(512) void gdn_prefill_pipe_kernel(PipeArgs a) {
     static_assert(64 * (kSweepSW + kSweepPW) == 512, "a sweep workgroup fills the launch");
     extern __shared__ __attribute__((aligned(16))) unsigned char gdn_pipe_smem[];
     if ((int)blockIdx.x < a.n_sweep) {
         sweep_wg<kSweepSW, kSweepNT, kSweepPW, true>(a.sweep, blockIdx.x, gdn_pipe_smem, a.sync);
+        return;
+    }
+    if ((int)blockIdx.x >= a.n_sweep + a.n_prep) {
+        pipe_post(a, blockIdx.x - a.n_sweep - a.n_prep, reinterpret_cast<volatile int*>(gdn_pipe_smem));
         return;
     }
     // uniform per wave: an SGPR, so the unit's LDS base stays scalar
@@ -1278,29 +1501,45 @@ static int device_cus() {
     return n;
 }
 
+// Workgroups of the gated norm and conv state in a pipelined launch: a
+// multiple of 8 (XCD round-robin), a quarter of the CUs at most.
+static int pipe_post_blocks(const PrefillPlan& p, int cus) {
+    const bool post = p.gated || p.conv_state.conv_state_out != nullptr;
+    return post ? std::max(8, std::min(64, cus / 4) / 8 * 8) : 0;
+}
+
 // The pipelined launch serves the bf16 layer when its sweep workgroups take
-// at most half of the CUs (so prep workgroups always find CUs) and the
-// environment does not turn it off (GDN_PREFILL_PIPELINE=0).
+// at most half of the CUs and, with the norm / conv-state workgroups (which
+// also wait), at most three quarters, so that prep workgroups always find
+// CUs; GDN_PREFILL_PIPELINE=0 in the environment turns it off.
 static bool use_pipe(const PrefillPlan& p) {
     if (!p.io_bf16 || p.sync.ready == nullptr || p.chunk_slots <= 0) return false;
     const char* env = getenv("GDN_PREFILL_PIPELINE");
     if (env != nullptr && env[0] == '0') return false;
-    return 2 * sweep_blocks(p) <= device_cus();
+    const int cus = device_cus(), ns = sweep_blocks(p);
+    return 2 * ns <= cus && 4 * (ns + pipe_post_blocks(p, cus)) <= 3 * cus;
 }
 
 static hipError_t launch_pipe(const PrefillPlan& p, hipStream_t s) {
     PipeArgs a;
     a.prep = p.prep;
     a.sweep = p.sweep;
+    a.conv_state = p.conv_state;
     a.sync = p.sync;
+    if (!p.gated) a.sync.oready = nullptr;
+    a.z = p.gated ? p.z : nullptr;
+    a.norm_w = p.norm_w;
+    a.norm_eps = p.norm_eps;
     a.n_sweep = sweep_blocks(p);
     a.chunk_slots = p.chunk_slots;
     a.prep_xcd = p.prep.Hk % 8 == 0;
     const int64_t units = (int64_t)p.chunk_slots * p.prep.Hk;
     const int64_t prep_wgs = a.prep_xcd ? 8 * ((units / 8 + 1) / 2) : (units + 1) / 2;
+    a.n_prep = (int32_t)((prep_wgs + 7) / 8 * 8);
+    a.n_post = pipe_post_blocks(p, device_cus());
     GDN_TRY(allow_dynamic_lds(nullptr, 0));
     auto kern = p.conv ? gdn_prefill_pipe_kernel<true> : gdn_prefill_pipe_kernel<false>;
-    hipLaunchKernelGGL(kern, dim3((unsigned)(a.n_sweep + prep_wgs)), dim3(512), kPipeSmem, s, a);
+    hipLaunchKernelGGL(kern, dim3((unsigned)(a.n_sweep + a.n_prep + a.n_post)), dim3(512), kPipeSmem, s, a);
     return hipGetLastError();
 }
 
@@ -1312,10 +1551,11 @@ static hipError_t run_serial(const PrefillPlan& p, bool pipe, hipStream_t s, Ker
         GDN_TRY(launch_chunk_table(p, s));
         GDN_TRY(rec.end(s));
     }
-    if (pipe) {
+    if (pipe) {   // prep, sweep, gated norm and conv state in one launch
         GDN_TRY(rec.begin(GDN_STAGE_PIPELINE, s));
         GDN_TRY(launch_pipe(p, s));
         GDN_TRY(rec.end(s));
+        return hipSuccess;
     } else {
         if (p.chunk_slots > 0) {
             GDN_TRY(rec.begin(GDN_STAGE_CHUNK_PREP, s));
@@ -1341,8 +1581,10 @@ static hipError_t run_serial(const PrefillPlan& p, bool pipe, hipStream_t s, Ker
 
 hipError_t launch_prefill(const PrefillPlan& p, hipStream_t stream, KernelRecorder& rec) {
     const bool pipe = use_pipe(p);
-    const int n = (p.prep.cu != nullptr) + (pipe ? 1 : (p.chunk_slots > 0) + 1) +
-                  (p.gated && p.total_tokens > 0) + (p.conv_state.conv_state_out != nullptr);
+    const int n = (p.prep.cu != nullptr) +
+                  (pipe ? 1
+                        : (p.chunk_slots > 0) + 1 + (p.gated && p.total_tokens > 0) +
+                              (p.conv_state.conv_state_out != nullptr));
     if (rec.events != nullptr && n > rec.max) return hipErrorInvalidValue;
     GDN_TRY(rec.call_begin(stream));
     GDN_TRY(p.io_bf16 ? run_serial<uint16_t>(p, pipe, stream, rec) : run_serial<float>(p, false, stream, rec));

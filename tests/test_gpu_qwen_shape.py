@@ -70,8 +70,8 @@ def test_profiled_brackets_every_kernel(pipeline, monkeypatch):
         events.append(e.value)
     ids = call.run_profiled(events, stream=torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
-    first = ["prep_sweep"] if pipeline else ["chunk_prep", "state_sweep"]
-    assert [STAGE_NAMES[i] for i in ids] == first + ["gated_norm", "conv_state"]
+    want = ["prep_sweep"] if pipeline else ["chunk_prep", "state_sweep", "gated_norm", "conv_state"]
+    assert [STAGE_NAMES[i] for i in ids] == want
 
     def ms(a, b):
         f = ctypes.c_float()
@@ -80,9 +80,10 @@ def test_profiled_brackets_every_kernel(pipeline, monkeypatch):
     total = ms(events[0], events[1])
     for j in range(len(ids)):
         assert 0.0 <= ms(events[2 + 2 * j], events[3 + 2 * j]) <= total
-    # too few event slots: refused before anything is launched
+    # too few event slots: refused before anything is launched (by the
+    # binding when that leaves none)
     from gated_deltanet_layer_02_amd import binding as B
-    with pytest.raises(B.GdnError):
+    with pytest.raises(B.GdnError if len(ids) > 1 else ValueError):
         call.run_profiled(events[:2 + 2 * (len(ids) - 1)], stream=torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     for e in events:
