@@ -31,6 +31,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK = 8.0e12          # B/s, MI355X HBM3E
 MFMA_BF16_PEAK = 2.5e15    # flop/s, dense bf16 MFMA
+FP32_PEAK = 157.3e12       # flop/s, fp32 (MFMA and vector ALUs alike)
 D = 128
 CHUNK = 64
 
@@ -38,6 +39,7 @@ CHUNK = 64
 FLOP_SWEEP = 6 * D * D + 2 * CHUNK * D           # W S^T, Q S^T, K^T U, P U
 FLOP_PREP = 2 * CHUNK * D + 2 * CHUNK * D + (2 * CHUNK * D + 2 * CHUNK * D) // 2  # W, U~, (KK^T, QK^T)/2
 FLOP_LAYER = 180224                               # whole chunked layer
+FLOP_LAYER_MIN = 139264                           # the same, triangular blocks skipped
 
 
 def log(msg):
@@ -304,6 +306,106 @@ def bench_options(args, hip, pres):
     return {"prefill_pool_bf16_snapshots": opts, "verify": ver}
 
 
+def layer_bytes(p):
+    """Once-each bytes of one prefill call: q, k, v, z, out, g, beta, weights,
+    states and conv states in and out."""
+    import gdn_synth as gs
+    es = 2 if p.io == gs.BF16 else 4
+    b = (2 * p.T * p.Hk * D + 2 * p.T * p.Hv * D) * es + 2 * p.T * p.Hv * 4
+    if p.gate:
+        b += p.T * p.Hv * D * es + D * es
+    if p.conv:
+        b += p.Cch * 4 * es + p.N * 3 * p.Cch * es * (2 if p.conv_state_std is not None else 1)
+    b += p.N * p.Hv * D * D * 4 * (2 if p.init_state_std is not None else 1)
+    return b
+
+
+def time_each(hip, calls, steps, warmup):
+    """Per-call times (s), HIP events around each call on the stream, calls rotated."""
+    import torch
+    stream = torch.cuda.current_stream().cuda_stream
+    for i in range(warmup):
+        calls[i % len(calls)](stream)
+    torch.cuda.synchronize()
+    ev = [(hip.event(), hip.event()) for _ in range(steps)]
+    for i in range(steps):
+        hip.record(ev[i][0], stream)
+        calls[i % len(calls)](stream)
+        hip.record(ev[i][1], stream)
+    torch.cuda.synchronize()
+    ts = sorted(hip.ms(a, b) * 1e-3 for a, b in ev)
+    for a, b in ev:
+        hip.destroy(a)
+        hip.destroy(b)
+    return ts
+
+
+def launch_form(hip, call):
+    """Which form the library chose for this call (from a profiled call's stages)."""
+    import torch
+    from gated_deltanet_layer_02_amd.binding import STAGE_NAMES
+    ev = [hip.event() for _ in range(2 + 2 * 8)]
+    ids = call.run_profiled(ev, stream=torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    for e in ev:
+        hip.destroy(e)
+    return "pipelined" if "prep_sweep" in [STAGE_NAMES[i] for i in ids] else "separate launches"
+
+
+def bench_configs(args, hip):
+    """Every prefill configuration: per-call median / p10 / p90, tokens/s, MFMA
+    fractions (dense-tile and triangle-aware counts) and HBM fraction; the time
+    per token of C2 against C1 (the layer is O(T)); and reference peaks
+    measured on this GPU (a device copy, and torch's bf16 GEMM)."""
+    import torch
+    import gdn_synth as gs
+    from gated_deltanet_layer_02_amd.tensors import PrefillCall
+
+    out = {}
+    per_token = {}
+    for name in ("C0", "C1", "C2", "C3"):
+        p = gs.configs()[name]
+        log(f"[bench] config {name}: {p.N} sequence(s), {p.T} tokens, io {p.io}")
+        x = gs.generate(p)
+        sets = 3 if p.T <= 8192 else 1
+        calls = [PrefillCall(x, Hk=p.Hk, Hv=p.Hv, io_bf16=p.io == gs.BF16, l2norm=p.l2norm, scale=p.scale,
+                             l2_eps=p.l2_eps, norm_eps=p.norm_eps) for _ in range(sets)]
+        form = launch_form(hip, calls[0])
+        steps = 30 if p.T <= 8192 else 10
+        ts = time_each(hip, [c.run for c in calls], steps, 5)
+        med, p10, p90 = ts[len(ts) // 2], ts[len(ts) // 10], ts[(9 * len(ts)) // 10]
+        byt = layer_bytes(p)
+        fpeak = MFMA_BF16_PEAK if p.io == gs.BF16 else FP32_PEAK   # fp32 I/O computes in fp32
+        per_token[name] = med / p.T
+        out[name] = {"tokens": p.T, "sequences": p.N, "io": p.io, "launch": form,
+                     "us_median": round(med * 1e6, 2), "us_p10": round(p10 * 1e6, 2),
+                     "us_p90": round(p90 * 1e6, 2), "tokens_per_s": round(p.T / med, 1),
+                     "flop_peak_TFLOPs": fpeak / 1e12,
+                     "flop_frac_dense_tile": round(FLOP_LAYER * p.T * p.Hv / med / fpeak, 4),
+                     "flop_frac_triangle_aware": round(FLOP_LAYER_MIN * p.T * p.Hv / med / fpeak, 4),
+                     "hbm_frac": round(byt / med / HBM_PEAK, 4), "bytes": byt}
+        del calls, x
+        torch.cuda.empty_cache()
+    out["time_per_token_C2_over_C1"] = round(per_token["C2"] / per_token["C1"], 3)
+
+    # reference peaks on this GPU (torch plumbing: a device copy and a bf16 GEMM)
+    stream = torch.cuda.current_stream().cuda_stream
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    ts = time_each(hip, [lambda s: dst.copy_(src)], 10, 3)
+    copy = 2 * src.numel() / ts[len(ts) // 2]
+    del src, dst
+    a = torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16)
+    ts = time_each(hip, [lambda s: torch.matmul(a, b)], 10, 3)
+    gemm = 2 * 8192 ** 3 / ts[len(ts) // 2]
+    del a, b
+    torch.cuda.empty_cache()
+    out["measured_peaks"] = {"device_copy_GBps": round(copy / 1e9, 1),
+                             "torch_bf16_gemm_8192_TFLOPs": round(gemm / 1e12, 1)}
+    return out
+
+
 def cpu_baseline(pres, target_s: float):
     """The fp64 oracle on the first S tokens of the same C1 inputs, all heads."""
     import numpy as np
@@ -352,6 +454,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-options", action="store_true",
                     help="skip the prefill-options and verify legs")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-configuration prefill timings (C0-C3) and reference peaks")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a 512 MiB device-to-device copy first (counter calibration)")
     args = ap.parse_args()
@@ -380,6 +484,7 @@ def main():
         dec = {"metric": "decode state GB/s", "fp32_state": bench_decode(args, hip, "C4"),
                "bf16_state": bench_decode(args, hip, "C4b")}
     opts = None if args.no_options else bench_options(args, hip, pres)
+    cfgs = None if args.no_configs else bench_configs(args, hip)
     cpu = None if args.no_cpu_baseline else cpu_baseline(pres, args.cpu_seconds)
 
     p = pres["p"]
@@ -406,6 +511,7 @@ def main():
         "path": pres["path"],
         "decode": dec,
         "options": opts,
+        "configs": cfgs,
     }
     print(json.dumps(line), flush=True)
 
