@@ -92,6 +92,25 @@ __device__ __forceinline__ float row16_sum(float x) {
     return x;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave: shifted adds within each
+// DPP row (row_shr 1, 2, 4, 8; lanes shifted in from outside the row read 0),
+// then lane 15's sum into the next row (row_bcast:15, rows 1 and 3) and lane
+// 31's into rows 2 and 3 (row_bcast:31).  Rows left out by the row mask add 0.
+template <int kCtrl, int kRows>
+__device__ __forceinline__ float dpp_rows(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl,
+                                                                 kRows, 0xF, false));
+}
+__device__ __forceinline__ float wave_incl_scan(float x) {
+    x += dpp_mov<0x111>(x);          // row_shr:1
+    x += dpp_mov<0x112>(x);          // row_shr:2
+    x += dpp_mov<0x114>(x);          // row_shr:4
+    x += dpp_mov<0x118>(x);          // row_shr:8
+    x += dpp_rows<0x142, 0xA>(x);    // row_bcast:15
+    x += dpp_rows<0x143, 0xC>(x);    // row_bcast:31
+    return x;
+}
+
 // Vector LDS stores of 8 consecutive / 4 consecutive elements in the math
 // type (bf16: one 16-byte / 8-byte store; fp32: two / one 16-byte stores).
 __device__ __forceinline__ void st8(bf16* p, const float* y) {

@@ -226,6 +226,52 @@ __device__ __forceinline__ void conv_out(const float (&x)[7][8], const float (&w
     }
 }
 
+// conv + SiLU of the quad's four tokens: y[tt][e] for local token tq + tt,
+// channel e (raw row tq + tt without conv).  bf16 rows with conv take
+// packed-pair dot products straight from the loaded bits: per channel,
+// v_perm pairs rows (i, i + 1) and each output is two bf16 dot2 ops
+// accumulating in fp32 (taps 0-1, then 2-3) against the tap pairs as they
+// sit in conv_w; no bf16 -> fp32 unpacking.  fp32 rows unpack and chain four
+// fp32 FMAs.
+template <class IO, bool kConv>
+__device__ __forceinline__ void conv_quad(const Quad<IO, kConv>& x, float (&y)[4][8]) {
+    if constexpr (sizeof(IO) == 2 && kConv) {
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+        for (int cp = 0; cp < 4; ++cp) {          // channels 2 cp, 2 cp + 1
+            uint32_t R[7];
+#pragma unroll
+            for (int i = 0; i < 7; ++i) R[i] = __builtin_bit_cast(u32x4, x.xr[i].v)[cp];
+            // conv_w rows of the two channels: (w0, w1), (w2, w3) of each.  Held
+            // as scalars: a bit cast of an element of an ext-vector value
+            // compiles to a read of element 0 with this clang.
+            const u32x4 wv = __builtin_bit_cast(u32x4, x.wr[cp].v);
+            const uint32_t w[4] = {wv[0], wv[1], wv[2], wv[3]};
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint32_t sel = h ? 0x07060302u : 0x05040100u;   // high or low halves
+                uint32_t L[6];                                         // (x_i, x_i+1) of the channel
+#pragma unroll
+                for (int i = 0; i < 6; ++i) L[i] = __builtin_amdgcn_perm(R[i + 1], R[i], sel);
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) {
+                    float acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[2 * h]),
+                                                                __builtin_bit_cast(bf16x2, L[tt]), 0.f, false);
+                    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[2 * h + 1]),
+                                                          __builtin_bit_cast(bf16x2, L[tt + 2]), acc, false);
+                    y[tt][2 * cp + h] = silu_f32(acc);
+                }
+            }
+        }
+    } else {
+        float xf[7][8], wf[4][8];
+        x.unpack(xf, wf);
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) conv_out<kConv>(xf, wf, tt, y[tt]);
+    }
+}
+
 // acc = X(16x16, LDS rows ldx) * Y(16x16, LDS rows ldy) in fp32 MFMA, K split
 // as k = 4 g + s over the four 16x16x4 instructions s.
 __device__ __forceinline__ f32x4 mm16_lds(const float* X, int ldx, const float* Y, int ldy,
@@ -330,9 +376,9 @@ __device__ __forceinline__ bool prep_unit(const PrepArgs& a, int c, int hk, unsi
         xq.load_w(conv_w, hk * kD + 8 * cg);
         xk.load_w(conv_w, Hk * kD + hk * kD + 8 * cg);
         // one tensor at a time (q, then k): the L2 norms are independent and
-        // only one set of fp32 rows is live
-        float xf[7][8], wf[4][8];
-        xq.unpack(xf, wf);
+        // only one set of conv outputs is live
+        float y4[4][8];
+        conv_quad(xq, y4);
         // v and gates of the first value head: in flight during phases 1 and 2
         // (edge chunks load v when they use it)
         if (inner) xv.load_inner(v, Hv, h0 * kD + 8 * cg, 2 * Hk * kD + h0 * kD + 8 * cg, t0, tq, conv_w);
@@ -340,10 +386,9 @@ __device__ __forceinline__ bool prep_unit(const PrepArgs& a, int c, int hk, unsi
             gl = a.g[(size_t)(t0 + lane) * Hv + h0];
             bl = a.beta[(size_t)(t0 + lane) * Hv + h0];
         }
-        // conv + SiLU, L2 normalisation over the 128 channels of token t (the
-        // 16 lanes of a DPP row), zero for padding tokens
+        // L2 normalisation over the 128 channels of token t (the 16 lanes of
+        // a DPP row), zero for padding tokens
         auto finish = [&](int tt, float mul, float (&y)[8]) {
-            conv_out<kConv>(xf, wf, tt, y);
             float r = mul;
             if (a.use_l2) {
                 float ss = 0.f;
@@ -357,19 +402,17 @@ __device__ __forceinline__ bool prep_unit(const PrepArgs& a, int c, int hk, unsi
         };
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
-            float y[8];
-            finish(tt, a.scale, y);
-            st8(&sm.qa.q[tq + tt][8 * cg], y);
+            finish(tt, a.scale, y4[tt]);
+            st8(&sm.qa.q[tq + tt][8 * cg], y4[tt]);
         }
-        xk.unpack(xf, wf);
-        float yk4[4][8];   // k of the four tokens, for the transposed store
+        conv_quad(xk, y4);   // k of the four tokens, also stored transposed
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
-            finish(tt, 1.0f, yk4[tt]);
-            st8(&sm.ka.k[tq + tt][8 * cg], yk4[tt]);
+            finish(tt, 1.0f, y4[tt]);
+            st8(&sm.ka.k[tq + tt][8 * cg], y4[tt]);
         }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) st4(&sm.kt[8 * cg + e][tq], yk4[0][e], yk4[1][e], yk4[2][e], yk4[3][e]);
+        for (int e = 0; e < 8; ++e) st4(&sm.kt[8 * cg + e][tq], y4[0][e], y4[1][e], y4[2][e], y4[3][e]);
     }
     __syncthreads();
 
@@ -439,11 +482,9 @@ __device__ __forceinline__ bool prep_unit(const PrepArgs& a, int c, int hk, unsi
                     xv.load(v, Hv, h * kD + 8 * cg, 2 * Hk * kD + h * kD + 8 * cg, t0, tq, len, seq_start,
                             crow, Cch, conv_w, csin);
                 xv.load_w(conv_w, 2 * Hk * kD + h * kD + 8 * cg);
-                float xf[7][8], wf[4][8];
-                xv.unpack(xf, wf);
+                conv_quad(xv, y);
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt) {
-                    conv_out<kConv>(xf, wf, tt, y[tt]);
                     const bool valid = tq + tt < len;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) y[tt][e] = valid ? y[tt][e] : 0.f;
@@ -462,13 +503,8 @@ __device__ __forceinline__ bool prep_unit(const PrepArgs& a, int c, int hk, unsi
 #pragma unroll
             for (int e = 0; e < 8; ++e) st4(&sm.vt[8 * cg + e][tq], y[0][e], y[1][e], y[2][e], y[3][e]);
             if (wave == 0) {   // G = inclusive cumsum of g over the chunk (padding: g = b = 0)
-                float G = gcur;
-#pragma unroll
-                for (int off = 1; off < 64; off <<= 1) {
-                    const float x = __shfl_up(G, off);
-                    if (lane >= off) G += x;
-                }
-                const float Gn = __shfl(G, 63);
+                const float G = wave_incl_scan(gcur);
+                const float Gn = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, G), 63));
                 const float gam = exp_f32(G);
                 sm.G[lane] = G;
                 sm.b[lane] = bcur;
@@ -507,6 +543,13 @@ __device__ __forceinline__ bool prep_unit(const PrepArgs& a, int c, int hk, unsi
 
         // 3c. T = (I + A)^-1, blocked by 16: diagonal blocks by forward
         //     substitution, then T_rs = -T_rr sum_{m=s}^{r-1} A_rm T_ms level by level.
+        //     Of the blocks above the diagonal only (0, 1) and (2, 3) are read
+        //     (by 3d, as the zero upper half of a 32-token block): waves 1
+        //     and 2 zero them, one 16-byte store per lane.
+        if (wave == 1 || wave == 2) {
+            const int br = 2 * (wave - 1), row = lane >> 2, col = 4 * (lane & 3);
+            *reinterpret_cast<f32x4*>(&sm.qa.t[16 * br + row][16 * (br + 1) + col]) = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
         if (wave == 0) {   // diagonal blocks: lane = (block, column)
             const int bb = lane >> 4, j = l16;
             float X[16];
@@ -519,13 +562,6 @@ __device__ __forceinline__ bool prep_unit(const PrepArgs& a, int c, int hk, unsi
             }
 #pragma unroll
             for (int r = 0; r < 16; ++r) sm.qa.t[16 * bb + r][16 * bb + j] = X[r];
-        } else {           // zero the blocks above the diagonal
-            for (int e = tid - 64; e < 6 * 256; e += 192) {
-                const int blk = e >> 8, r = (e >> 4) & 15, col = e & 15;
-                const int br = blk < 3 ? 0 : (blk < 5 ? 1 : 2);
-                const int bc = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3);
-                sm.qa.t[16 * br + r][16 * bc + col] = 0.f;
-            }
         }
         __syncthreads();
 #pragma unroll
