@@ -272,24 +272,31 @@ __device__ __forceinline__ void conv_quad(const Quad<IO, kConv>& x, float (&y)[4
     }
 }
 
-// acc = X(16x16, LDS rows ldx) * Y(16x16, LDS rows ldy) in fp32 MFMA, K split
-// as k = 4 g + s over the four 16x16x4 instructions s.
-__device__ __forceinline__ f32x4 mm16_lds(const float* X, int ldx, const float* Y, int ldy,
-                                          f32x4 acc, int l16, int g4) {
-    const f32x4 a = *reinterpret_cast<const f32x4*>(X + l16 * ldx + 4 * g4);
+// 16x16x16 products for the block substitution: A operand lane (row l16, g4)
+// holds columns 4 g4 .. 4 g4 + 3, B operand lane (column l16, g4) rows
+// 4 g4 .. 4 g4 + 3, the accumulator likewise.  bf16: one MFMA on bf16 copies;
+// fp32: four 16x16x4 MFMAs.
+template <class MT> struct Mm16;
+template <> struct Mm16<bf16> {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef s16x4 Op;
+    static __device__ __forceinline__ Op op(const f32x4& x) {
+        return s16x4{(short)f32_to_bf16_bits(x[0]), (short)f32_to_bf16_bits(x[1]), (short)f32_to_bf16_bits(x[2]),
+                     (short)f32_to_bf16_bits(x[3])};
+    }
+    static __device__ __forceinline__ f32x4 mul(const Op& a, const Op& b, const f32x4& c) {
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+    }
+};
+template <> struct Mm16<float> {
+    typedef f32x4 Op;
+    static __device__ __forceinline__ Op op(const f32x4& x) { return x; }
+    static __device__ __forceinline__ f32x4 mul(const Op& a, const Op& b, f32x4 c) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], Y[(4 * g4 + s) * ldy + l16], acc, 0, 0, 0);
-    return acc;
-}
-// acc = X(16x16, LDS) * E, E an accumulator tile (lane (n, g) holds rows 4 g + s)
-__device__ __forceinline__ f32x4 mm16_acc(const float* X, int ldx, const f32x4& E, int l16, int g4) {
-    const f32x4 a = *reinterpret_cast<const f32x4*>(X + l16 * ldx + 4 * g4);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], E[s], acc, 0, 0, 0);
-    return acc;
-}
+        for (int s = 0; s < 4; ++s) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], c, 0, 0, 0);
+        return c;
+    }
+};
 
 // Stores of the prep's results.  Coherent (kCo): agent-scope stores (sc1),
 // written through to memory and visible to every XCD once complete, so a
@@ -541,16 +548,9 @@ __device__ __forceinline__ bool prep_unit(const PrepArgs& a, int c, int hk, unsi
         }
         __syncthreads();
 
-        // 3c. T = (I + A)^-1, blocked by 16: diagonal blocks by forward
-        //     substitution, then T_rs = -T_rr sum_{m=s}^{r-1} A_rm T_ms level by level.
-        //     Of the blocks above the diagonal only (0, 1) and (2, 3) are read
-        //     (by 3d, as the zero upper half of a 32-token block): waves 1
-        //     and 2 zero them, one 16-byte store per lane.
-        if (wave == 1 || wave == 2) {
-            const int br = 2 * (wave - 1), row = lane >> 2, col = 4 * (lane & 3);
-            *reinterpret_cast<f32x4*>(&sm.qa.t[16 * br + row][16 * (br + 1) + col]) = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-        if (wave == 0) {   // diagonal blocks: lane = (block, column)
+        // 3c. Diagonal 16x16 blocks of T = (I + A)^-1 by forward substitution
+        //     (wave 0, lane = (block, column)); the rest of T is never formed.
+        if (wave == 0) {
             const int bb = lane >> 4, j = l16;
             float X[16];
 #pragma unroll
@@ -564,68 +564,59 @@ __device__ __forceinline__ bool prep_unit(const PrepArgs& a, int c, int hk, unsi
             for (int r = 0; r < 16; ++r) sm.qa.t[16 * bb + r][16 * bb + j] = X[r];
         }
         __syncthreads();
-#pragma unroll
-        for (int d = 1; d < 4; ++d) {   // blocks (r, s) with r - s = d, one per wave
-            if (wave < 4 - d) {
-                const int s = wave, r = wave + d;
-                f32x4 E = {0.f, 0.f, 0.f, 0.f};
-                for (int m = s; m < r; ++m)
-                    E = mm16_lds(&sm.ka.a[16 * r][16 * m], LD, &sm.qa.t[16 * m][16 * s], LD, E, l16, g4);
-                const f32x4 Trs = mm16_acc(&sm.qa.t[16 * r][16 * r], LD, E, l16, g4);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sm.qa.t[16 * r + 4 * g4 + i][16 * s + l16] = -Trs[i];
-            }
-            __syncthreads();
-        }
 
-        // 3d. W^T = K^T diag(b gamma) T^T (rows dk, cols = this wave's tokens):
-        //     its accumulator tiles are the sweep's A fragments of W.
-        //     U~ = T diag(b) V (rows = this wave's tokens, cols dv).
+        // 3d. W = T diag(b gamma) K and U~ = T diag(b) V by forward substitution
+        //     over the four 16-token blocks: X_r = T_rr (Y_r - sum_{m<r} A_rm X_m),
+        //     Y = diag(b gamma) K or diag(b) V.  Wave w takes the dk tiles 2w,
+        //     2w + 1 (W) and the dv tiles 2w, 2w + 1 (U~) through all four blocks,
+        //     so the chain over r never leaves the wave and every wave does the
+        //     same work.  The products are 16x16x16: an accumulator (lane (n, g)
+        //     holds rows 4g .. 4g + 3 of column n) is at once the B operand of its
+        //     tile and the A operand of its transpose, so the chain feeds itself
+        //     and W is also formed transposed, W_r^T = Z_r^T T_rr^T, in the layout
+        //     the sweep reads (rows dk, columns tokens), stored negated.
         {
-            const int t = 16 * wave + l16;
-            const int np = wave < 2 ? 1 : 2;    // token blocks with nonzero T
-            F bw[2], au[2];
+            typedef Mm16<MT> P;
+            const float* Ab = &sm.ka.a[0][0];
+            const float* Tb = &sm.qa.t[0][0];
+            typename P::Op X[3][4];   // B operands of X_0 .. X_2 per column tile
 #pragma unroll
-            for (int p = 0; p < 2; ++p) {
-                if (p >= np) continue;
+            for (int r = 0; r < 4; ++r) {
+                // T_rr: A operand (lane (row l16, g4): columns 4 g4 ..) and B operand of T_rr^T
+                const typename P::Op Top =
+                    P::op(*reinterpret_cast<const f32x4*>(Tb + (16 * r + l16) * LD + 16 * r + 4 * g4));
+                f32x4 Z[4];   // column tiles q: dk 2w, 2w + 1, dv 2w, 2w + 1
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const int i = 32 * p + kidx(g4, j);
-                    const float tv = sm.qa.t[t][i];
-                    bw[p].set(j, tv * sm.bg[i]);
-                    au[p].set(j, tv * sm.b[i]);
+                for (int q = 0; q < 4; ++q) {
+                    const int col = 16 * (2 * wave + (q & 1)) + l16;
+                    const MT* y = (q < 2 ? &sm.kt[col][0] : &sm.vt[col][0]) + 16 * r + 4 * g4;
+                    const float* sc = (q < 2 ? sm.bg : sm.b) + 16 * r + 4 * g4;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) Z[q][i] = sc[i] * static_cast<float>(y[i]);
                 }
-            }
-            f32x4 Wt[8];
 #pragma unroll
-            for (int m = 0; m < 8; ++m) {
-                Wt[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int m = 0; m < r; ++m) {
+                    const f32x4 a4 = *reinterpret_cast<const f32x4*>(Ab + (16 * r + l16) * LD + 16 * m + 4 * g4);
+                    const typename P::Op Aop = P::op(-a4);
 #pragma unroll
-                for (int p = 0; p < 2; ++p) {
-                    if (p >= np) continue;
-                    F afr;
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) afr.v[j] = sm.kt[16 * m + l16][32 * p + kidx(g4, j)];
-                    mma(Wt[m], afr, bw[p]);
+                    for (int q = 0; q < 4; ++q) Z[q] = P::mul(Aop, X[m][q], Z[q]);
                 }
-            }
+                f32x4 WT[2];
 #pragma unroll
-            for (int pk = 0; pk < 4; ++pk)   // stored negated: the sweep adds (-W) S^T to U~
-                St::frag(VB + (kVB_W + wave * 4 + pk) * 64, lane, acc_to_frag<MT>(-Wt[2 * pk], -Wt[2 * pk + 1]));
-#pragma unroll
-            for (int nt = 0; nt < 8; ++nt) {
-                f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int p = 0; p < 2; ++p) {
-                    if (p >= np) continue;
-                    F bfr;
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) bfr.v[j] = sm.vt[16 * nt + l16][32 * p + kidx(g4, j)];
-                    mma(acc, au[p], bfr);
+                for (int q = 0; q < 4; ++q) {
+                    const typename P::Op Zop = P::op(Z[q]);
+                    const f32x4 Xr = P::mul(Top, Zop, f32x4{0.f, 0.f, 0.f, 0.f});
+                    if (r < 3) X[r][q] = P::op(Xr);
+                    if (q < 2) {
+                        WT[q] = P::mul(Zop, Top, f32x4{0.f, 0.f, 0.f, 0.f});
+                    } else {   // lane (dv, g4) holds U~[16 r + 4 g4 + i][16 nt + l16]
+                        const int nt = 2 * wave + (q & 1);
+                        St::four(reinterpret_cast<MT*>(VB + (kVB_U + 2 * nt + (r >> 1)) * 64),
+                                 8 * lane + (r & 1) * 4, Xr);
+                    }
                 }
-                // lane (dv, g4) holds U~[16 wave + 4 g4 + r][16 nt + l16]
-                St::four(reinterpret_cast<MT*>(VB + (kVB_U + 2 * nt + (wave >> 1)) * 64), 8 * lane + (wave & 1) * 4,
-                         acc);
+                // stored negated: the sweep adds (-W) S^T to U~
+                St::frag(VB + (kVB_W + r * 4 + wave) * 64, lane, acc_to_frag<MT>(-WT[0], -WT[1]));
             }
         }
         __syncthreads();
