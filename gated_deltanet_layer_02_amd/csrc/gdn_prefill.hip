@@ -29,6 +29,7 @@
 #include <algorithm>
 #include <atomic>
 #include <cstdlib>
+#include <type_traits>
 
 #include "gdn_common.hpp"
 #include "gdn_internal.hpp"
@@ -443,31 +444,72 @@ __device__ __forceinline__ bool prep_unit(const PrepArgs& a, int c, int hk, unsi
             St::frag(KB + (kKB_KT + fi) * 64, lane, fr);
         }
     }
-    f32x4 KK[4], KQ[4];
+    // K K^T and K Q^T by 16x16 cells (token tile tt, tile ti), ti <= tt: the ten
+    // that A and P use, dealt five to a wave (K K^T cells for A; pairs of K Q^T
+    // cells for one P fragment (tt, p), the second absent above the diagonal):
+    //   wave 0: A (0,0) (3,3), P (0,0) (3,1)    wave 1: A (1,0) (1,1), P (1,0) (2,1)
+    //   wave 2: A (2,0..2), P (2,0)             wave 3: A (3,0..2), P (3,0)
+    // so that 3b's exponentials and these MFMAs split evenly.
+    const int nkk = wave >= 2 ? 3 : 2, npj = wave >= 2 ? 1 : 2;   // uniform
+    auto kk_tt = [&](int c) { return wave >= 2 ? wave : (wave == 0 ? 3 * c : 1); };
+    auto kk_ti = [&](int c) { return wave >= 2 ? c : (wave == 0 ? 3 * c : c); };
+    auto pj_tt = [&](int jb) { return wave >= 2 ? wave : (jb == 0 ? wave : 3 - wave); };
+    auto pj_p = [&](int jb) { return wave >= 2 ? 0 : jb; };
+    f32x4 KK[3], KQ[2][2];
     {
-        F kf[4][4], qf[4];
+        // per wave, its cells with compile-time tiles: each k / q tile it needs
+        // is read from LDS once (four fragments) and kept for its cells
+        auto cells = [&](auto wc) {
+            constexpr int W = decltype(wc)::value;
+            constexpr int kNK = W >= 2 ? 3 : 2, kNP = W >= 2 ? 1 : 2;
+            constexpr int kTT[3] = {W >= 2 ? W : (W == 0 ? 0 : 1), W >= 2 ? W : (W == 0 ? 3 : 1), W};
+            constexpr int kTI[3] = {0, W >= 2 ? 1 : (W == 0 ? 3 : 1), 2};
+            constexpr int kPT[2] = {W, W >= 2 ? W : 3 - W};
+            constexpr int kPP[2] = {0, 1};
+            // tiles used: k rows as A or B operands, q rows as B operands
+            bool kuse[4] = {false, false, false, false}, quse[4] = {false, false, false, false};
+            F kf[4][4], qf[4][4];
 #pragma unroll
-        for (int ti = 0; ti < 4; ++ti)
+            for (int c = 0; c < kNK; ++c) kuse[kTT[c]] = kuse[kTI[c]] = true;
 #pragma unroll
-            for (int p = 0; p < 4; ++p)
+            for (int jb = 0; jb < kNP; ++jb) {
+                quse[kPT[jb]] = true;
 #pragma unroll
-                for (int j = 0; j < 8; ++j) kf[ti][p].v[j] = sm.ka.k[16 * ti + l16][32 * p + kidx(g4, j)];
-#pragma unroll
-        for (int p = 0; p < 4; ++p)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) qf[p].v[j] = sm.qa.q[16 * wave + l16][32 * p + kidx(g4, j)];
-#pragma unroll
-        for (int ti = 0; ti < 4; ++ti) {
-            KK[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
-            KQ[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                F kw;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) kw.v[j] = sm.ka.k[16 * wave + l16][32 * p + kidx(g4, j)];
-                mma(KK[ti], kw, kf[ti][p]);        // rows t (tile wave), cols i (tile ti)
-                mma(KQ[ti], kf[ti][p], qf[p]);     // rows i (tile ti), cols t (tile wave)
+                for (int h = 0; h < 2; ++h)
+                    if (2 * kPP[jb] + h <= kPT[jb]) kuse[2 * kPP[jb] + h] = true;
             }
+#pragma unroll
+            for (int tile = 0; tile < 4; ++tile)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        if (kuse[tile]) kf[tile][q].v[j] = sm.ka.k[16 * tile + l16][32 * q + kidx(g4, j)];
+                        if (quse[tile]) qf[tile][q].v[j] = sm.qa.q[16 * tile + l16][32 * q + kidx(g4, j)];
+                    }
+#pragma unroll
+            for (int c = 0; c < 3; ++c) {
+                KK[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (c < kNK)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) mma(KK[c], kf[kTT[c]][q], kf[kTI[c]][q]);   // rows t, cols i
+            }
+#pragma unroll
+            for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    KQ[jb][h] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    if (jb < kNP && 2 * kPP[jb] + h <= kPT[jb])   // else above the diagonal: zero
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            mma(KQ[jb][h], kf[2 * kPP[jb] + h][q], qf[kPT[jb]][q]);   // rows i, cols t
+                }
+        };
+        switch (wave) {
+            case 0: cells(std::integral_constant<int, 0>{}); break;
+            case 1: cells(std::integral_constant<int, 1>{}); break;
+            case 2: cells(std::integral_constant<int, 2>{}); break;
+            default: cells(std::integral_constant<int, 3>{}); break;
         }
     }
     __syncthreads();   // q / k rows are dead from here on; their LDS holds A and T
@@ -522,28 +564,35 @@ __device__ __forceinline__ bool prep_unit(const PrepArgs& a, int c, int hk, unsi
         }
         __syncthreads();
 
-        // 3b. A rows of this wave's token tile; P fragments
+        // 3b. A cells and P fragments of this wave, as dealt above (cells of A
+        //     above the diagonal are never read and not written)
 #pragma unroll
-        for (int ti = 0; ti < 4; ++ti)
+        for (int c = 0; c < 3; ++c) {
+            if (c < nkk) {
+                const int tt = kk_tt(c), ti = kk_ti(c);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 16 * wave + 4 * g4 + r, i = 16 * ti + l16;
-                sm.ka.a[t][i] = (i < t) ? sm.b[t] * KK[ti][r] * exp_f32(sm.G[t] - sm.G[i]) : 0.f;
+                for (int r = 0; r < 4; ++r) {
+                    const int t = 16 * tt + 4 * g4 + r, i = 16 * ti + l16;
+                    sm.ka.a[t][i] = (i < t) ? sm.b[t] * KK[c][r] * exp_f32(sm.G[t] - sm.G[i]) : 0.f;
+                }
             }
-        {
-            const int t = 16 * wave + l16;
-            const float Gt = sm.G[t];
+        }
 #pragma unroll
-            for (int p = 0; p < 2; ++p) {
-                if (p > (wave >> 1)) continue;   // block above the diagonal: zero
+        for (int jb = 0; jb < 2; ++jb) {
+            if (jb < npj) {
+                const int tt = pj_tt(jb), p = pj_p(jb);
+                const bool hi = 2 * p + 1 <= tt;   // the block's second 16 columns are not above the diagonal
+                const int t = 16 * tt + l16;
+                const float Gt = sm.G[t];
                 F fr;
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     const int i = 32 * p + kidx(g4, j);
-                    const float x = KQ[2 * p + (j >> 2)][j & 3];
-                    fr.set(j, (i <= t) ? x * exp_f32(Gt - sm.G[i]) : 0.f);
+                    float x = 0.f;
+                    if (j < 4 || hi) x = (i <= t) ? KQ[jb][j >> 2][j & 3] * exp_f32(Gt - sm.G[i]) : 0.f;
+                    fr.set(j, x);
                 }
-                St::frag(VB + (kVB_P + pfrag_index(wave, p)) * 64, lane, fr);
+                St::frag(VB + (kVB_P + pfrag_index(tt, p)) * 64, lane, fr);
             }
         }
         __syncthreads();
