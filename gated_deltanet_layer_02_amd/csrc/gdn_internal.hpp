@@ -84,6 +84,7 @@ struct PipeArgs {
     PipeSync sync;
     const void* z; const void* norm_w; float norm_eps;   // z == NULL: no gated norm
     int32_t n_sweep, n_prep, n_post, chunk_slots, prep_xcd;
+    int32_t n_single, c_single;   // the first n_single prep workgroups: one unit each, chunks < c_single
 };
 
 

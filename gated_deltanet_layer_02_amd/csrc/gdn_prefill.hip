@@ -1322,22 +1322,34 @@ constexpr unsigned kPipeSmem =
 static_assert(kPipeSmem <= 160 * 1024, "fits one CU's LDS");
 static_assert(kPipeSmem > 80 * 1024, "one workgroup per CU");
 
-// Prep unit of half `half` of prep workgroup b.  With prep_xcd (Hk a multiple
+// Prep unit of half `half` of prep workgroup b.  The first n_single
+// workgroups run one unit each (half 1 has none) for the chunks below
+// c_single: a unit alone on its CU finishes in about two thirds of the time
+// two take together, so the sweep starts that much earlier, while the later
+// chunks, needed later, go two to a workgroup.  With prep_xcd (Hk a multiple
 // of 8) workgroup b sits on XCD b % 8 (workgroups are dealt to the 8 XCDs
-// round-robin; n_sweep is a multiple of 8) and takes units of the key heads
-// hk = b (mod 8), which the sweep also keeps on that XCD; otherwise units go
-// chunk-major over all key heads.
+// round-robin; n_sweep and n_single are multiples of 8) and takes units of the
+// key heads hk = b (mod 8), which the sweep also keeps on that XCD; otherwise
+// units go chunk-major over all key heads.  c = chunk_slots: no unit.
 __device__ __forceinline__ void pipe_prep_unit(const PipeArgs& a, int b, int half, int& c, int& hk) {
     const int Hk = a.prep.Hk;
+    const bool single = b < a.n_single;
+    const int u = single ? b : b - a.n_single;   // workgroup index within its kind
+    const int k = single ? 1 : 2;                // units per workgroup
     if (a.prep_xcd) {
         const int per = Hk >> 3;
-        const int ui = 2 * (b >> 3) + half;
+        const int ui = k * (u >> 3) + (single ? 0 : half);
         c = ui / per;
-        hk = (b & 7) + 8 * (ui % per);
+        hk = (u & 7) + 8 * (ui % per);
     } else {
-        const int ui = 2 * b + half;
+        const int ui = k * u + (single ? 0 : half);
         c = ui / Hk;
         hk = ui % Hk;
+    }
+    if (single) {
+        if (half != 0 || c >= a.c_single) c = a.chunk_slots;
+    } else {
+        c += a.c_single;
     }
 }
 
@@ -1577,11 +1589,18 @@ static int device_cus() {
     return n;
 }
 
+// Chunks whose prep units run one to a workgroup at the start of a pipelined
+// launch (the sweep's first chunks).
+constexpr int kPipeSingleChunks = 4;
+
 // Workgroups of the gated norm and conv state in a pipelined launch: a
-// multiple of 8 (XCD round-robin), a quarter of the CUs at most.
+// multiple of 8 (XCD round-robin), at most 96 and at most what the sweep
+// workgroups leave of three quarters of the CUs (at least 8).  They start
+// once every prep workgroup is dispatched; with the sweep started early by
+// the single-unit prep workgroups, 64 of them left a tail of norm work.
 static int pipe_post_blocks(const PrefillPlan& p, int cus) {
     const bool post = p.gated || p.conv_state.conv_state_out != nullptr;
-    return post ? std::max(8, std::min(64, cus / 4) / 8 * 8) : 0;
+    return post ? std::max(8, std::min(96, 3 * cus / 4 - sweep_blocks(p)) / 8 * 8) : 0;
 }
 
 // The pipelined launch serves the bf16 layer when its sweep workgroups take
@@ -1609,9 +1628,11 @@ static hipError_t launch_pipe(const PrefillPlan& p, hipStream_t s) {
     a.n_sweep = sweep_blocks(p);
     a.chunk_slots = p.chunk_slots;
     a.prep_xcd = p.prep.Hk % 8 == 0;
-    const int64_t units = (int64_t)p.chunk_slots * p.prep.Hk;
+    a.c_single = std::min(p.chunk_slots, kPipeSingleChunks);
+    a.n_single = (a.c_single * p.prep.Hk + 7) / 8 * 8;
+    const int64_t units = (int64_t)(p.chunk_slots - a.c_single) * p.prep.Hk;   // two per workgroup
     const int64_t prep_wgs = a.prep_xcd ? 8 * ((units / 8 + 1) / 2) : (units + 1) / 2;
-    a.n_prep = (int32_t)((prep_wgs + 7) / 8 * 8);
+    a.n_prep = a.n_single + (int32_t)((prep_wgs + 7) / 8 * 8);
     a.n_post = pipe_post_blocks(p, device_cus());
     GDN_TRY(allow_dynamic_lds(nullptr, 0));
     auto kern = p.conv ? gdn_prefill_pipe_kernel<true> : gdn_prefill_pipe_kernel<false>;
