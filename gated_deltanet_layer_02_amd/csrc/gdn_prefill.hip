@@ -95,6 +95,13 @@ __device__ __forceinline__ bool locate_chunk(const PrepArgs& a, int c, int& n, i
 // lanes on 16 rows, same column) spread over the banks.  The q / k row tiles
 // are only needed until K K^T and K Q^T are formed; their space is then
 // reused for A and T (fp32).
+// kt / vt are written and read in groups of 4 tokens (8 bytes of bf16): row
+// `row`'s group g sits at group g ^ ((row >> 3) & 15), so that the transposed
+// stores (rows 8 cg + e of 16 lanes) spread over the banks instead of four
+// lanes sharing each, while the fragment and substitution reads stay
+// conflict-free.  Element offset of token group `g` in row `row`:
+__device__ __forceinline__ int tsw(int row, int g) { return 4 * (g ^ ((row >> 3) & 15)); }
+
 template <class MT>
 struct PrepSmem {
     static constexpr int kRowPad = sizeof(MT) == 2 ? 16 : 8;   // elements
@@ -108,8 +115,8 @@ struct PrepSmem {
         MT k[kChunk][kD + kRowPad];        // normalised k rows
         float a[kChunk][kLdA];             // A
     } ka;
-    MT kt[kD][kChunk + kColPad];           // normalised k, transposed (token contiguous)
-    MT vt[kD][kChunk + kColPad];           // conv'd v of one value head, transposed
+    MT kt[kD][kChunk + kColPad];           // normalised k, transposed (token contiguous, swizzled)
+    MT vt[kD][kChunk + kColPad];           // conv'd v of one value head, transposed (swizzled)
     float G[kChunk];                       // inclusive cumsum of g
     float b[kChunk];                       // beta
     float bg[kChunk];                      // beta * exp(G)
@@ -420,7 +427,8 @@ __device__ __forceinline__ bool prep_unit(const PrepArgs& a, int c, int hk, unsi
             st8(&sm.ka.k[tq + tt][8 * cg], y4[tt]);
         }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) st4(&sm.kt[8 * cg + e][tq], y4[0][e], y4[1][e], y4[2][e], y4[3][e]);
+        for (int e = 0; e < 8; ++e)
+            st4(&sm.kt[8 * cg + e][tsw(8 * cg + e, tq >> 2)], y4[0][e], y4[1][e], y4[2][e], y4[3][e]);
     }
     __syncthreads();
 
@@ -440,7 +448,10 @@ __device__ __forceinline__ bool prep_unit(const PrepArgs& a, int c, int hk, unsi
             const int row = 16 * (fi >> 1) + l16, kb = 32 * (fi & 1);
             F fr;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) fr.v[j] = sm.kt[row][kb + kidx(g4, j)];
+            for (int j = 0; j < 8; ++j) {
+                const int t = kb + kidx(g4, j);
+                fr.v[j] = sm.kt[row][tsw(row, t >> 2) + (t & 3)];
+            }
             St::frag(KB + (kKB_KT + fi) * 64, lane, fr);
         }
     }
@@ -550,7 +561,8 @@ __device__ __forceinline__ bool prep_unit(const PrepArgs& a, int c, int hk, unsi
                 }
             }
 #pragma unroll
-            for (int e = 0; e < 8; ++e) st4(&sm.vt[8 * cg + e][tq], y[0][e], y[1][e], y[2][e], y[3][e]);
+            for (int e = 0; e < 8; ++e)
+                st4(&sm.vt[8 * cg + e][tsw(8 * cg + e, tq >> 2)], y[0][e], y[1][e], y[2][e], y[3][e]);
             if (wave == 0) {   // G = inclusive cumsum of g over the chunk (padding: g = b = 0)
                 const float G = wave_incl_scan(gcur);
                 const float Gn = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, G), 63));
@@ -638,7 +650,7 @@ __device__ __forceinline__ bool prep_unit(const PrepArgs& a, int c, int hk, unsi
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int col = 16 * (2 * wave + (q & 1)) + l16;
-                    const MT* y = (q < 2 ? &sm.kt[col][0] : &sm.vt[col][0]) + 16 * r + 4 * g4;
+                    const MT* y = (q < 2 ? &sm.kt[col][0] : &sm.vt[col][0]) + tsw(col, 4 * r + g4);
                     const float* sc = (q < 2 ? sm.bg : sm.b) + 16 * r + 4 * g4;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) Z[q][i] = sc[i] * static_cast<float>(y[i]);
