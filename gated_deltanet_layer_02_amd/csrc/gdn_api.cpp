@@ -55,17 +55,18 @@ int64_t chunk_slots(const gdn_desc* d, bool varlen) {
     return d->total_tokens / gdn::kChunk + d->num_seqs;
 }
 
-// Epochs of pipelined launches: unique per call (a 64-bit counter from a
-// random start, never 0), so chunk flags left in a workspace by an earlier
-// call, or zeroed memory, never read as published.
+// Epochs of pipelined launches: unique per call and even (a 64-bit counter
+// from a random start, stepped by 2, never 0), so chunk flags left in a
+// workspace by an earlier call (epoch or epoch + 1), or zeroed memory, never
+// read as published.
 uint64_t next_epoch() {
     static std::atomic<uint64_t> counter{[] {
         std::random_device rd;
         const uint64_t t = (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count();
-        return ((uint64_t)rd() << 32) ^ (uint64_t)rd() ^ (t * 0x9E3779B97F4A7C15ull);
+        return (((uint64_t)rd() << 32) ^ (uint64_t)rd() ^ (t * 0x9E3779B97F4A7C15ull)) & ~1ull;
     }()};
     uint64_t e;
-    do e = counter.fetch_add(1, std::memory_order_relaxed); while (e == 0);
+    do e = counter.fetch_add(2, std::memory_order_relaxed); while (e == 0);
     return e;
 }
 
@@ -82,6 +83,7 @@ PrefillLayout prefill_layout(const gdn_desc* d, bool varlen) {
     L.VB = take(C * Hv * gdn::kVBUnits * frag);
     L.ready = take(C * Hk * sizeof(uint64_t));
     L.oready = take(C * Hv * 8 * sizeof(uint64_t));
+    L.xcc = take((size_t)d->num_seqs * Hv * (gdn::kD / 16) * sizeof(uint64_t));   // <= one per 16 dv rows
     L.total = off;
     return L;
 }
@@ -175,6 +177,7 @@ gdn_status prefill_impl(const gdn_desc* d, const gdn_prefill_args& x, hipStream_
 
     p.sync.ready = reinterpret_cast<uint64_t*>(ws + L.ready);
     p.sync.oready = reinterpret_cast<uint64_t*>(ws + L.oready);
+    p.sync.xcc = reinterpret_cast<uint64_t*>(ws + L.xcc);
     p.sync.epoch = next_epoch();
 
     gdn::ConvStateArgs& c = p.conv_state;

@@ -63,14 +63,22 @@ struct ConvStateArgs {
     int32_t T, N, Hk, Hv;
 };
 
-// Prep-to-sweep hand-off of a pipelined launch (prep and sweep in one grid):
-// ready[c * Hk + hk] == epoch once prep unit (chunk slot c, key head hk) is
-// published.  ready == NULL: no pipelined launch for this call.
+// Prep-to-sweep hand-off of a pipelined launch (prep and sweep in one grid).
+// Epochs are even.  ready[c * Hk + hk] == epoch or epoch + 1 once prep unit
+// (chunk slot c, key head hk) is published: epoch + 1 when its fragments are
+// in the L2 of the XCD that every sweep workgroup of the key head runs on
+// (their coherent loads go through that L2), epoch when they were written
+// back to memory first.  ready == NULL: no pipelined launch.
 // oready[(c * Hv + h) * 8 + tile] == epoch once the sweep's output of chunk
 // slot c, value head h, 16-row dv tile `tile` is stored (gated layer only).
+// xcc[(n * Hk + hk) * xcc_per + r] == epoch ^ ((id + 1) << 56) once sweep
+// workgroup r of key unit (n, hk) has recorded the id of its XCD; xcc == NULL:
+// prep units always write their fragments back to memory.
 struct PipeSync {
     uint64_t* ready = nullptr;
     uint64_t* oready = nullptr;
+    uint64_t* xcc = nullptr;
+    int32_t xcc_per = 0;          // sweep workgroups per key unit
     uint64_t epoch = 0;
 };
 
@@ -101,7 +109,7 @@ struct PrefillPlan {
 
 // Workspace carve-up of one prefill call.
 struct PrefillLayout {
-    size_t chunk_off, KB, VB, ready, oready, total;
+    size_t chunk_off, KB, VB, ready, oready, xcc, total;
 };
 
 struct DecodeArgs {

@@ -306,11 +306,19 @@ template <> struct Mm16<float> {
     }
 };
 
-// Stores of the prep's results.  Coherent (kCo): agent-scope stores (sc1),
-// written through to memory and visible to every XCD once complete, so a
-// pipelined launch publishes a unit with a vmcnt wait per wave instead of
-// an L2 write-back (which flushes every dirty line of the XCD's L2 and
-// doubled the prep's time when eight waves per workgroup issued it).
+// Id of the XCD this wave runs on (hardware register XCC_ID, bits 3:0) and
+// its tag for one call: tags of different calls never coincide (epochs of
+// different calls differ below bit 56).
+__device__ __forceinline__ int xcd_id() { return __builtin_amdgcn_s_getreg(20 | (3 << 11)); }
+__device__ __forceinline__ uint64_t xcd_tag(uint64_t epoch, int id) { return epoch ^ ((uint64_t)(id + 1) << 56); }
+// A pipelined-launch flag holds this call's (even) epoch, or epoch + 1.
+__device__ __forceinline__ bool same_epoch(uint64_t v, uint64_t epoch) { return (v | 1) == (epoch | 1); }
+
+// Stores of the prep's results.  kCo (pipelined launch): buffer stores with
+// no cache-policy bits, complete once in this XCD's L2, the coherence point
+// of its CUs.  A unit whose readers all run on this XCD publishes them as
+// they are; any other writes the L2 back to memory first (one agent-scope
+// release), so that copies on every XCD see them.
 template <bool kCo> struct PrepStore;
 template <> struct PrepStore<false> {
     template <class MT>
@@ -324,35 +332,37 @@ template <> struct PrepStore<false> {
         for (int r = 0; r < 4; ++r) base[i + r] = static_cast<MT>(x[r]);
     }
 };
-// Coherent form: buffer stores with the sc1 cache-policy bit on a resource
-// built from a uniform base (64 KB range; every offset used is below it).
+// A resource built from a uniform base (64 KB range; every offset used is below it).
 template <> struct PrepStore<true> {
-    static constexpr int kSc1 = 16;
     static __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(void* base) {
         return __builtin_amdgcn_make_buffer_rsrc(base, 0, 0x10000, 0x00020000);
     }
     static __device__ __forceinline__ void frag(Frag<bf16>* base, int lane, const Frag<bf16>& f) {
         typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f.v), rsrc(base), lane * 16, 0, kSc1);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f.v), rsrc(base), lane * 16, 0, 0);
     }
     static __device__ __forceinline__ void f32(float* base, int i, float x) {
-        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), rsrc(base), i * 4, 0, kSc1);
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), rsrc(base), i * 4, 0, 0);
     }
     static __device__ __forceinline__ void four(bf16* base, int i, const f32x4& x) {
         typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
         typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
         const bf16x4 v = {static_cast<bf16>(x[0]), static_cast<bf16>(x[1]), static_cast<bf16>(x[2]),
                           static_cast<bf16>(x[3])};
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), rsrc(base), i * 2, 0, kSc1);
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), rsrc(base), i * 2, 0, 0);
     }
 };
 
 // One prep unit: chunk slot c of key head hk, run by 256 threads (tid
 // 0..255, four waves) on the LDS at smem.  Returns false for slots past the
 // last chunk (nothing is written).  Every thread of the unit passes the same
-// barriers, so two units can share one workgroup.
+// barriers, so two units can share one workgroup.  In a pipelined launch
+// (kCo, ps), `local` (valid in wave 0) tells whether every sweep workgroup of
+// the unit's key unit recorded this XCD in ps->xcc (read after phase 1, when
+// the sweep workgroups, dispatched first, have long recorded theirs).
 template <class IO, bool kConv, bool kCo = false>
-__device__ __forceinline__ bool prep_unit(const PrepArgs& a, int c, int hk, unsigned char* smem, int tid) {
+__device__ __forceinline__ bool prep_unit(const PrepArgs& a, int c, int hk, unsigned char* smem, int tid,
+                                          const PipeSync* ps = nullptr, bool* local = nullptr) {
     typedef typename MathOf<IO>::T MT;
     typedef Frag<MT> F;
     typedef PrepSmem<MT> Smem;
@@ -369,6 +379,7 @@ __device__ __forceinline__ bool prep_unit(const PrepArgs& a, int c, int hk, unsi
     const int l16 = lane & 15, g4 = lane >> 4;
     const int cg = tid & 15, tq = 4 * (tid >> 4);     // 8 channels, 4 tokens per thread
     const int Hk = a.Hk, Hv = a.Hv, group = Hv / Hk;
+
     const int Cch = 2 * Hk * kD + Hv * kD;
     const IO* q = static_cast<const IO*>(a.q);
     const IO* k = static_cast<const IO*>(a.k);
@@ -431,6 +442,11 @@ __device__ __forceinline__ bool prep_unit(const PrepArgs& a, int c, int hk, unsi
             st4(&sm.kt[8 * cg + e][tsw(8 * cg + e, tq >> 2)], y4[0][e], y4[1][e], y4[2][e], y4[3][e]);
     }
     __syncthreads();
+    const bool probe = kCo && ps != nullptr && ps->xcc != nullptr;   // uniform
+    uint64_t tag = 0;   // lane r < xcc_per: the XCD tag of sweep workgroup r of this key unit
+    if (probe && wave == 0 && lane < ps->xcc_per)
+        tag = __hip_atomic_load(ps->xcc + ((size_t)n * Hk + hk) * ps->xcc_per + lane, __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_AGENT);
 
     // ---- 2. Q and K^T fragments for the sweep; K K^T and K Q^T ----
     F* KB = static_cast<F*>(a.KB) + ((size_t)c * Hk + hk) * kKBUnits * 64;   // unit base (uniform)
@@ -682,6 +698,8 @@ __device__ __forceinline__ bool prep_unit(const PrepArgs& a, int c, int hk, unsi
         }
         __syncthreads();
     }
+    if (kCo && wave == 0 && local != nullptr)
+        *local = probe && __all(lane >= ps->xcc_per || tag == xcd_tag(ps->epoch, xcd_id()));
     return true;
 }
 
@@ -1027,15 +1045,20 @@ __device__ __forceinline__ void sweep_lds_step(int j, int wave, f32x4 (&S)[NT][8
         G[63]);
 }
 
-// Chunk hand-off inside a pipelined launch.  The prep unit of (chunk slot c,
-// key head hk) stores `epoch` to ready[c * Hk + hk] after its fragments are
-// visible at agent scope (every wave's release fence, then a barrier, then
-// the flag).  A sweep producer wave reads the flag with an agent-scope load
-// and then copies the fragments with agent-coherent (sc1) loads, which do not
-// hit a stale copy in any cache.  Epochs are unique per call, so the flags
-// never need clearing.  Waits are bounded: after about 2^28 ticks of the
-// 100 MHz wall clock (2.7 s) a wait gives up, counts itself in
-// gdn_pipe_timeouts and carries on (the call's result is then invalid).
+// Chunk hand-off inside a pipelined launch.  A prep unit's fragments are
+// plain stores, complete once in its XCD's L2.  When every sweep workgroup of
+// its key unit recorded the same XCD (ps.xcc), the unit publishes at once and
+// its flag is epoch + 1: the readers' agent-coherent (sc1) loads go through
+// that same L2, which holds the lines (dirty, or written back when evicted).
+// Otherwise an agent-scope release first writes the L2 back to memory and the
+// flag is `epoch`.  The flag is one store to ready[c * Hk + hk] after every
+// wave of the unit has waited for its stores and a barrier.  A sweep producer
+// wave reads the flag with an agent-scope load and copies the fragments with
+// agent-coherent loads, which do not hit a stale copy in any cache.  Epochs
+// are unique per call, so the flags never need clearing.  Waits are bounded:
+// after about 2^28 ticks of the 100 MHz wall clock (2.7 s) a wait gives up,
+// counts itself in gdn_pipe_timeouts and carries on (the call's result is then
+// invalid).
 __device__ uint32_t gdn_pipe_timeouts;
 constexpr uint64_t kPipeWaitTicks = 1ull << 28;
 constexpr int kCoherentLoad = 16;   // cache-policy bits of an agent-coherent load (sc1)
@@ -1043,21 +1066,23 @@ constexpr int kCoherentLoad = 16;   // cache-policy bits of an agent-coherent lo
 __device__ __forceinline__ uint64_t pipe_flag(const uint64_t* f) {
     return __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// true once *f == epoch; false (counted) when the wait gives up
-__device__ __noinline__ bool pipe_wait(const uint64_t* f, uint64_t epoch) {
+// The value of *f once it holds epoch or epoch + 1 (never 0); 0 (counted)
+// when the wait gives up.  A call: its loads are complete when it returns.
+__device__ __noinline__ uint64_t pipe_wait(const uint64_t* f, uint64_t epoch) {
     const uint64_t t0 = wall_clock64();
-    while (pipe_flag(f) != epoch) {
+    uint64_t v;
+    while (!same_epoch(v = pipe_flag(f), epoch)) {
         __builtin_amdgcn_s_sleep(2);
         if (wall_clock64() - t0 > kPipeWaitTicks) {
             if ((threadIdx.x & 63) == 0)
                 __hip_atomic_fetch_add(&gdn_pipe_timeouts, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            return false;
+            return 0;
         }
     }
-    return true;
+    return v;
 }
 
-// true once f[0 .. count) all equal epoch (each lane watches every 64th);
+// true once f[0 .. count) all hold epoch (or epoch + 1; each lane watches every 64th);
 // polls about every 0.3 us (these waits are not on the sweep's chain, and
 // fewer polls of the flag lines leave the memory channels to the sweep)
 __device__ __noinline__ bool pipe_wait_all(const uint64_t* f, int count, uint64_t epoch) {
@@ -1065,7 +1090,7 @@ __device__ __noinline__ bool pipe_wait_all(const uint64_t* f, int count, uint64_
     const uint64_t t0 = wall_clock64();
     for (int base = 0; base < count; base += 64) {
         const int i = base + lane;
-        while (!__all(i >= count || pipe_flag(f + i) == epoch)) {
+        while (!__all(i >= count || same_epoch(pipe_flag(f + i), epoch))) {
             __builtin_amdgcn_s_sleep(10);
             if (wall_clock64() - t0 > kPipeWaitTicks) {
                 if (lane == 0)
@@ -1112,10 +1137,16 @@ __device__ __forceinline__ void sweep_wg(const SweepArgs& a, int x, unsigned cha
         const bool pub = kPipe && ps.oready != nullptr;           // output flags
         const int k = sg * PW + p;                                // this wave's output flag
         auto slot = [&](int jj) { return stage + (jj % 3) * (L::kStage / 2); };
+        // this workgroup's XCD, for the key unit's prep units to compare with theirs
+        if (kPipe && ps.xcc != nullptr && p == 0 && lane == 0) {
+            const int r = (h - hk * (a.Hv / a.Hk)) * L::kGroups + sg;
+            __hip_atomic_store(ps.xcc + ((size_t)n * a.Hk + hk) * ps.xcc_per + r, xcd_tag(ps.epoch, xcd_id()),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
         // after a wait gives up, the wave stops waiting (the call is invalid
         // anyway) so that it still ends within one wait's bound
         bool live = true;
-        if (kPipe && q.nch > 0) live = pipe_wait(ready + (size_t)q.c_begin * a.Hk, ps.epoch);
+        if (kPipe && q.nch > 0) live = pipe_wait(ready + (size_t)q.c_begin * a.Hk, ps.epoch) != 0;
         // Per iteration: copies of chunk j, then the stores of chunk j - 3,
         // then vmcnt(kStores): loads and stores retire in order, so the copies
         // have landed while the stores may still be in flight; they are
@@ -1145,8 +1176,8 @@ __device__ __forceinline__ void sweep_wg(const SweepArgs& a, int x, unsigned cha
             asm volatile("" ::: "memory");
             // the next issue overwrites the other buffer, which the compute
             // waves finished with before this barrier
-            if (kPipe && live && j + 1 < q.nch && ahead != ps.epoch)
-                live = pipe_wait(ready + (c + 1) * a.Hk, ps.epoch);
+            if (kPipe && live && j + 1 < q.nch && !same_epoch(ahead, ps.epoch))
+                live = pipe_wait(ready + (c + 1) * a.Hk, ps.epoch) != 0;
         }
         if (q.nch > 0) {   // the last three chunks, once the compute waves staged the last one
             __syncthreads();
@@ -1479,14 +1510,20 @@ __global__ __launch_bounds__(512) void gdn_prefill_pipe_kernel(PipeArgs a) {
     int c, hk;
     pipe_prep_unit(a, blockIdx.x - a.n_sweep, half, c, hk);
     if (c >= a.chunk_slots) return;
-    if (!prep_unit<uint16_t, kConv, true>(a.prep, c, hk, gdn_pipe_smem + half * kPipePrepStride, tid)) return;
-    // publish: every wave's agent-scope stores have completed (vmcnt counts
-    // stores on this architecture), then one flag
+    bool local = false;
+    if (!prep_unit<uint16_t, kConv, true>(a.prep, c, hk, gdn_pipe_smem + half * kPipePrepStride, tid, &a.sync,
+                                          &local))
+        return;
+    // publish: every wave's stores are complete in this XCD's L2 (vmcnt counts
+    // stores on this architecture), then one flag: epoch + 1 for readers on
+    // this XCD, else epoch after an agent-scope release (L2 written back)
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     __syncthreads();
-    if (tid == 0)
-        __hip_atomic_store(a.sync.ready + (size_t)c * a.prep.Hk + hk, a.sync.epoch, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) {
+        if (!local) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        __hip_atomic_store(a.sync.ready + (size_t)c * a.prep.Hk + hk, a.sync.epoch + (local ? 1 : 0),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 }
 
 // ===========================================================================
@@ -1646,6 +1683,13 @@ static hipError_t launch_pipe(const PrefillPlan& p, hipStream_t s) {
     const int64_t prep_wgs = a.prep_xcd ? 8 * ((units / 8 + 1) / 2) : (units + 1) / 2;
     a.n_prep = a.n_single + (int32_t)((prep_wgs + 7) / 8 * 8);
     a.n_post = pipe_post_blocks(p, device_cus());
+    // prep units leave their fragments in the L2 of an XCD they share with
+    // all of their key unit's sweep workgroups; GDN_PIPE_L2=0 in the
+    // environment has them write the L2 back to memory always
+    a.sync.xcc_per = (p.prep.Hv / p.prep.Hk) * SweepLds<kSweepSW, kSweepNT>::kGroups;
+    const char* l2 = getenv("GDN_PIPE_L2");
+    if ((l2 != nullptr && l2[0] == '0') || a.sync.xcc_per > 64 || SweepLds<kSweepSW, kSweepNT>::kGroups > kD / 16)
+        a.sync.xcc = nullptr;
     GDN_TRY(allow_dynamic_lds(nullptr, 0));
     auto kern = p.conv ? gdn_prefill_pipe_kernel<true> : gdn_prefill_pipe_kernel<false>;
     hipLaunchKernelGGL(kern, dim3((unsigned)(a.n_sweep + a.n_prep + a.n_post)), dim3(512), kPipeSmem, s, a);

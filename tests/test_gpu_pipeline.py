@@ -169,3 +169,42 @@ def test_pipeline_c1_shape(monkeypatch):
     res = _run_both(p, x, monkeypatch, True)
     _assert_same(res)
     assert B.gdn_pipeline_timeouts() == 0
+
+
+def _kept_units(call):
+    """Prep units of the last call whose fragments stayed in an XCD's L2: their
+    ready flag is the call's epoch + 1.  The epoch is the most common non-zero
+    word of the workspace (every output flag holds it)."""
+    import torch
+    w = call.workspace.view(torch.int64).cpu().numpy().view(np.uint64)
+    vals, counts = np.unique(w[w != 0], return_counts=True)
+    epoch = vals[np.argmax(counts)]
+    assert epoch % 2 == 0 and counts.max() >= call.T // 64 * 8, "no epoch found"
+    return int(np.count_nonzero(w == epoch + np.uint64(1)))
+
+
+def test_pipeline_l2_hand_off_matches_write_through(monkeypatch):
+    """Prep fragments left in the L2 of the sweep's XCD and fragments written
+    through to memory (GDN_PIPE_L2=0) give the same bits, in either order on
+    one workspace (the flags of the other form's call are stale)."""
+    import torch
+    from gated_deltanet_layer_02_amd import binding as B
+    from gated_deltanet_layer_02_amd.tensors import PrefillCall
+    p = gs.configs()["C1"]
+    x = gs.generate(p)
+    monkeypatch.setenv("GDN_PREFILL_PIPELINE", "1")
+    call = PrefillCall(x, Hk=p.Hk, Hv=p.Hv, io_bf16=True)
+    call.workspace.zero_()
+    res, kept = [], []
+    for mode in ("1", "0", "1"):
+        monkeypatch.setenv("GDN_PIPE_L2", mode)
+        call.run()
+        torch.cuda.synchronize()
+        res.append(_outputs(call))
+        kept.append(_kept_units(call))
+    say(f"pipeline L2 hand-off, C1 shape: units kept in L2 per call {kept} of {p.T // 64 * p.Hk}")
+    assert kept[1] == 0
+    for r in res[1:]:
+        for n in res[0]:
+            assert np.array_equal(res[0][n], r[n]), n
+    assert B.gdn_pipeline_timeouts() == 0
