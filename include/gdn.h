@@ -129,7 +129,11 @@ gdn_status gdn_prefill_workspace_size(const gdn_desc* d, size_t* bytes);
  * the device's CUs (one or a few long sequences), the chunk prep and the
  * sweep run as one launch whose sweep workgroups wait for each chunk's prep
  * (bounded waits; GDN_PREFILL_PIPELINE=0 in the environment selects separate
- * launches).  Work on other streams running beside such a call must leave it
+ * launches).  In that launch a chunk's prep results stay in the L2 of the XCD
+ * that all of their readers run on, where each sweep workgroup records its
+ * XCD; units whose readers are elsewhere write them back to memory first
+ * (GDN_PIPE_L2=0 in the environment: every unit does).  Both give the same
+ * bits.  Work on other streams running beside such a call must leave it
  * CUs for its prep workgroups; a wait that gives up after about 2.7 s counts
  * itself in gdn_pipeline_timeouts and leaves that call's result invalid.
  */
