@@ -83,8 +83,10 @@ struct PipeSync {
 };
 
 // Pipelined launch: workgroups [0, n_sweep) run the sweep (the sweep's own
-// grid mapping), the rest run two prep units each (prep_xcd: units are dealt
-// so that a key head's units land on the XCD of its sweep workgroups).
+// grid mapping), then n_prep prep workgroups (one or two units each; prep_xcd:
+// units are dealt so that a key head's units land on the XCD of its sweep
+// workgroups) and n_post gated-norm / conv-state workgroups, the post ones
+// before the prep ones when post_first.
 struct PipeArgs {
     PrepArgs prep;
     SweepArgs sweep;
@@ -93,6 +95,7 @@ struct PipeArgs {
     const void* z; const void* norm_w; float norm_eps;   // z == NULL: no gated norm
     int32_t n_sweep, n_prep, n_post, chunk_slots, prep_xcd;
     int32_t n_single, c_single;   // the first n_single prep workgroups: one unit each, chunks < c_single
+    int32_t post_first;           // grid order sweep | post | prep (long sequences) instead of sweep | prep | post
 };
 
 

@@ -1371,7 +1371,7 @@ static_assert(kPipeSmem > 80 * 1024, "one workgroup per CU");
 // two take together, so the sweep starts that much earlier, while the later
 // chunks, needed later, go two to a workgroup.  With prep_xcd (Hk a multiple
 // of 8) workgroup b sits on XCD b % 8 (workgroups are dealt to the 8 XCDs
-// round-robin; n_sweep and n_single are multiples of 8) and takes units of the
+// round-robin; n_sweep, n_single and n_post are multiples of 8) and takes units of the
 // key heads hk = b (mod 8), which the sweep also keeps on that XCD; otherwise
 // units go chunk-major over all key heads.  c = chunk_slots: no unit.
 __device__ __forceinline__ void pipe_prep_unit(const PipeArgs& a, int b, int half, int& c, int& hk) {
@@ -1501,14 +1501,16 @@ __global__ __launch_bounds__(512) void gdn_prefill_pipe_kernel(PipeArgs a) {
         sweep_wg<kSweepSW, kSweepNT, kSweepPW, true>(a.sweep, blockIdx.x, gdn_pipe_smem, a.sync);
         return;
     }
-    if ((int)blockIdx.x >= a.n_sweep + a.n_prep) {
-        pipe_post(a, blockIdx.x - a.n_sweep - a.n_prep, reinterpret_cast<volatile int*>(gdn_pipe_smem));
+    const int r = (int)blockIdx.x - a.n_sweep;   // index past the sweep workgroups
+    const int post = a.post_first ? r : r - a.n_prep;
+    if (post >= 0 && post < a.n_post) {
+        pipe_post(a, post, reinterpret_cast<volatile int*>(gdn_pipe_smem));
         return;
     }
     // uniform per wave: an SGPR, so the unit's LDS base stays scalar
     const int half = __builtin_amdgcn_readfirstlane(threadIdx.x >> 8), tid = threadIdx.x & 255;
     int c, hk;
-    pipe_prep_unit(a, blockIdx.x - a.n_sweep, half, c, hk);
+    pipe_prep_unit(a, a.post_first ? r - a.n_post : r, half, c, hk);
     if (c >= a.chunk_slots) return;
     bool local = false;
     if (!prep_unit<uint16_t, kConv, true>(a.prep, c, hk, gdn_pipe_smem + half * kPipePrepStride, tid, &a.sync,
@@ -1642,14 +1644,26 @@ static int device_cus() {
 // launch (the sweep's first chunks).
 constexpr int kPipeSingleChunks = 4;
 
-// Workgroups of the gated norm and conv state in a pipelined launch: a
-// multiple of 8 (XCD round-robin), at most 96 and at most what the sweep
-// workgroups leave of three quarters of the CUs (at least 8).  They start
-// once every prep workgroup is dispatched; with the sweep started early by
-// the single-unit prep workgroups, 64 of them left a tail of norm work.
+// Long sequences (at least kPipePostFirstChunks chunk slots) put the gated
+// norm / conv-state workgroups before the prep ones in the grid, so that they
+// start with the sweep: placed after them, they start only once every prep
+// workgroup is dispatched, and the norm of a long sequence piles up until the
+// prep ends (65,536 tokens: 2.18 ms last, 1.93 ms first).  Shorter sequences
+// keep them last, since the prep needs the CUs at the start (4,096 tokens:
+// 141 us last, 158 us first; the two orders cross near 16,384 tokens).
+constexpr int kPipePostFirstChunks = 256;
+static bool pipe_post_first(const PrefillPlan& p) { return p.chunk_slots >= kPipePostFirstChunks; }
+
+// Their number: a multiple of 8 (XCD round-robin), at most what the sweep
+// workgroups leave of three quarters of the CUs (at least 8), and at most 96
+// placed last (with the sweep started early by the single-unit prep
+// workgroups, 64 of them left a tail of norm work) or a quarter of the CUs
+// placed first (more left the prep too few CUs: 72 or 80 of 256 made the
+// 65,536-token call 2.39 ms).
 static int pipe_post_blocks(const PrefillPlan& p, int cus) {
     const bool post = p.gated || p.conv_state.conv_state_out != nullptr;
-    return post ? std::max(8, std::min(96, 3 * cus / 4 - sweep_blocks(p)) / 8 * 8) : 0;
+    const int cap = pipe_post_first(p) ? cus / 4 : 96;
+    return post ? std::max(8, std::min(cap, 3 * cus / 4 - sweep_blocks(p)) / 8 * 8) : 0;
 }
 
 // The pipelined launch serves the bf16 layer when its sweep workgroups take
@@ -1683,6 +1697,7 @@ static hipError_t launch_pipe(const PrefillPlan& p, hipStream_t s) {
     const int64_t prep_wgs = a.prep_xcd ? 8 * ((units / 8 + 1) / 2) : (units + 1) / 2;
     a.n_prep = a.n_single + (int32_t)((prep_wgs + 7) / 8 * 8);
     a.n_post = pipe_post_blocks(p, device_cus());
+    a.post_first = pipe_post_first(p) ? 1 : 0;
     // prep units leave their fragments in the L2 of an XCD they share with
     // all of their key unit's sweep workgroups; GDN_PIPE_L2=0 in the
     // environment has them write the L2 back to memory always

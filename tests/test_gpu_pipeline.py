@@ -105,6 +105,7 @@ CASES = [
     ("empty-seq", [200, 0, 130], (4, 8), {}, True),
     ("no-conv-no-gate", [64 * 5 + 9], (2, 4), dict(conv=False, gate=False), True),
     ("one-token", [1], (16, 32), {}, True),
+    ("post-first", [64 * 256 + 37], (16, 32), {}, True),             # norm workgroups ahead of the prep
 ]
 
 
