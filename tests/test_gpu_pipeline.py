@@ -173,15 +173,24 @@ def test_pipeline_c1_shape(monkeypatch):
 
 
 def _kept_units(call):
-    """Prep units of the last call whose fragments stayed in an XCD's L2: their
-    ready flag is the call's epoch + 1.  The epoch is the most common non-zero
-    word of the workspace (every output flag holds it)."""
+    """Prep units of the last (bf16) call whose fragments stayed in an XCD's L2:
+    their ready flag is the call's epoch + 1.  Reads the flags where the
+    workspace keeps them: after the chunk offsets, KB (32 units of 1 KB per
+    chunk slot and key head) and VB (40 per chunk slot and value head), each
+    region rounded up to 256 bytes; chunk slots = T / 64 + N with cu_seqlens,
+    ceil(T / 64) without.  The output flags that follow all hold the epoch."""
     import torch
     w = call.workspace.view(torch.int64).cpu().numpy().view(np.uint64)
-    vals, counts = np.unique(w[w != 0], return_counts=True)
-    epoch = vals[np.argmax(counts)]
-    assert epoch % 2 == 0 and counts.max() >= call.T // 64 * 8, "no epoch found"
-    return int(np.count_nonzero(w == epoch + np.uint64(1)))
+    C = call.T // 64 + call.N if call.cu is not None else -(-call.T // 64)
+    r256 = lambda n: (n + 255) // 256 * 256
+    off = r256(4 * (call.N + 1)) + r256(C * call.Hk * 32 * 1024) + r256(C * call.Hv * 40 * 1024)
+    ready = w[off // 8: off // 8 + C * call.Hk]
+    off += r256(C * call.Hk * 8)
+    published = -(-call.T // 64) * call.Hv * 8
+    oready = w[off // 8: off // 8 + published]
+    epoch = oready[0]
+    assert epoch != 0 and epoch % 2 == 0 and np.all(oready == epoch), "workspace layout"
+    return int(np.count_nonzero(ready == epoch + np.uint64(1)))
 
 
 def test_pipeline_l2_hand_off_matches_write_through(monkeypatch):
@@ -208,4 +217,33 @@ def test_pipeline_l2_hand_off_matches_write_through(monkeypatch):
     for r in res[1:]:
         for n in res[0]:
             assert np.array_equal(res[0][n], r[n]), n
+    assert B.gdn_pipeline_timeouts() == 0
+
+
+def test_pipeline_write_back_fallback(monkeypatch):
+    """Two key heads: prep units are dealt chunk-major over every XCD while the
+    sweep of a key head sits on one, so most units find a reader elsewhere and
+    write their L2 back before publishing; the result equals the all-write-back
+    form bit for bit."""
+    import torch
+    from gated_deltanet_layer_02_amd import binding as B
+    from gated_deltanet_layer_02_amd.tensors import PrefillCall
+    p = _problem("pipe-fallback", [64 * 20 + 11], Hk=2, Hv=4)
+    x = gs.generate(p)
+    monkeypatch.setenv("GDN_PREFILL_PIPELINE", "1")
+    call = PrefillCall(x, Hk=p.Hk, Hv=p.Hv, io_bf16=True)
+    assert "prep_sweep" in _stages(call)
+    res, kept = [], []
+    for mode in ("1", "0"):
+        monkeypatch.setenv("GDN_PIPE_L2", mode)
+        call.workspace.zero_()
+        call.run()
+        torch.cuda.synchronize()
+        res.append(_outputs(call))
+        kept.append(_kept_units(call))
+    units = -(-p.T // 64) * p.Hk
+    say(f"pipeline write-back fallback, Hk=2: units kept in L2 {kept} of {units}")
+    assert 0 < kept[0] < units and kept[1] == 0
+    for n in res[0]:
+        assert np.array_equal(res[0][n], res[1][n]), n
     assert B.gdn_pipeline_timeouts() == 0
