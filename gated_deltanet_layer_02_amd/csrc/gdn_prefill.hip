@@ -1655,14 +1655,14 @@ constexpr int kPipePostFirstChunks = 256;
 static bool pipe_post_first(const PrefillPlan& p) { return p.chunk_slots >= kPipePostFirstChunks; }
 
 // Their number: a multiple of 8 (XCD round-robin), at most what the sweep
-// workgroups leave of three quarters of the CUs (at least 8), and at most 96
-// placed last (with the sweep started early by the single-unit prep
-// workgroups, 64 of them left a tail of norm work) or a quarter of the CUs
-// placed first (more left the prep too few CUs: 72 or 80 of 256 made the
-// 65,536-token call 2.39 ms).
+// workgroups leave of three quarters of the CUs (at least 8), and at most
+// half of the CUs placed last (dispatched late, they work through a backlog
+// of norm units: at 4,096 tokens 64 of them left a tail of norm work, 96 took
+// 139.6 us per call and 128 138.2) or a quarter placed first (more left the
+// prep too few CUs: 72 or 80 of 256 made the 65,536-token call 2.39 ms).
 static int pipe_post_blocks(const PrefillPlan& p, int cus) {
     const bool post = p.gated || p.conv_state.conv_state_out != nullptr;
-    const int cap = pipe_post_first(p) ? cus / 4 : 96;
+    const int cap = pipe_post_first(p) ? cus / 4 : cus / 2;
     return post ? std::max(8, std::min(cap, 3 * cus / 4 - sweep_blocks(p)) / 8 * 8) : 0;
 }
 
