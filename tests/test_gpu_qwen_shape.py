@@ -17,12 +17,14 @@ def _qwen_shape(name, T, seed):
                       seed=seed)
 
 
-def test_in_place_poisoned_side_stream():
+@pytest.mark.parametrize("T", [64 * 26 + 33, 64 * 256 + 33], ids=["norm-last", "norm-first"])
+def test_in_place_poisoned_side_stream(T):
     """Every output written, results equal to a fresh call, and work queued
-    on the caller's stream afterwards sees them."""
+    on the caller's stream afterwards sees them.  At 257 chunks the norm /
+    conv-state workgroups run ahead of the prep ones and overwrite the conv
+    state in place early: only after the first chunk's prep units read it."""
     import torch
     from gated_deltanet_layer_02_amd.tensors import PrefillCall, to_host
-    T = 64 * 26 + 33
     p = _qwen_shape("qwen-inplace", T, seed=5)
     x = gs.generate(p)
     say(f"Qwen shape in place on a side stream: T={T}")
