@@ -1669,7 +1669,9 @@ static int pipe_post_blocks(const PrefillPlan& p, int cus) {
 // The pipelined launch serves the bf16 layer when its sweep workgroups take
 // at most half of the CUs and, with the norm / conv-state workgroups (which
 // also wait), at most three quarters, so that prep workgroups always find
-// CUs; GDN_PREFILL_PIPELINE=0 in the environment turns it off.
+// CUs.  Workgroup x is dispatched to XCD x % 8 from that XCD's own share; the
+// sweep and post counts are multiples of 8, so the bound holds on every XCD.
+// GDN_PREFILL_PIPELINE=0 in the environment turns it off.
 static bool use_pipe(const PrefillPlan& p) {
     if (!p.io_bf16 || p.sync.ready == nullptr || p.chunk_slots <= 0) return false;
     const char* env = getenv("GDN_PREFILL_PIPELINE");
