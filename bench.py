@@ -181,12 +181,17 @@ def bench_prefill(args, hip):
         + p.Cch * 4 * 2 + D * 2 + N * Hv * D * D * 4 + N * 3 * p.Cch * 2
     dominant = max(stage_ms, key=stage_ms.get)
     dom_s = stage_ms[dominant] * 1e-3
+    # algorithmic flop per (token, value head) of the dominant kernel's share,
+    # dense 64x64 tile count; the pipelined kernel runs the whole layer
+    count = None
     if dominant == "state_sweep":
-        achieved, peak, unit, bound = FLOP_SWEEP * T * Hv / dom_s, MFMA_BF16_PEAK, "TFLOP/s", "mfma"
+        count = ("sweep: W S^T, Q S^T, K^T U (6 d^2) + P U (2 C d)", FLOP_SWEEP)
     elif dominant == "chunk_prep":
-        achieved, peak, unit, bound = FLOP_PREP * T * Hv / dom_s, MFMA_BF16_PEAK, "TFLOP/s", "mfma"
-    elif dominant == "prep_sweep":   # prep and sweep in one launch
-        achieved, peak, unit, bound = (FLOP_PREP + FLOP_SWEEP) * T * Hv / dom_s, MFMA_BF16_PEAK, "TFLOP/s", "mfma"
+        count = ("prep: T [b V | b gamma K] (4 C d) + half of K K^T and Q K^T", FLOP_PREP)
+    elif dominant == "prep_sweep":
+        count = ("whole layer: K K^T, Q K^T, T [b V | b gamma K], P U (10 C d) + 6 d^2", FLOP_LAYER)
+    if count is not None:
+        achieved, peak, unit, bound = count[1] * T * Hv / dom_s, MFMA_BF16_PEAK, "TFLOP/s", "mfma"
     else:   # gated norm: reads o and z, writes out
         achieved, peak, unit, bound = 3 * T * Hv * D * 2 / dom_s, HBM_PEAK, "GB/s", "hbm"
     scale = 1e12 if unit == "TFLOP/s" else 1e9
@@ -195,6 +200,9 @@ def bench_prefill(args, hip):
     roof = {"bound": bound, "achieved": round(achieved / scale, 2), "peak": peak / scale,
             "unit": unit, "frac": round(achieved / peak, 4),
             "traffic": traffic,   # HBM bytes per launch (counter summary average)
+            "flop_per_token_head": count[1] if count else None,
+            "flop_count": count[0] if count else None,
+            "flop_per_launch": count[1] * T * Hv if count else None,
             "kernel": dominant, "launches_per_step": nl,
             "kernel_us_per_launch": round(stage_ms[dominant] * 1e3 / nl, 2),
             "kernel_us_per_step": round(stage_ms[dominant] * 1e3, 2)}
@@ -406,6 +414,77 @@ def bench_configs(args, hip):
     return out
 
 
+def _host_cpu():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _prefix(x, S):
+    """The first S tokens of a single-sequence problem's inputs."""
+    import numpy as np
+    xs = {n: (a[:S] if n in ("q", "k", "v", "z", "g", "beta") else a) for n, a in x.items()}
+    xs["cu_seqlens"] = np.array([0, S], dtype=np.int32)
+    return xs
+
+
+def cpu_baseline_configs(per_run_s: float = 1.0):
+    """The fp64 oracle on every configuration, with one host thread and with
+    all of them: tokens/s on a bounded sample of each (about per_run_s of
+    single-thread work), the sample stated."""
+    import dataclasses
+    import numpy as np
+    import gdn_synth as gs
+    from oracle import oracle
+    allthreads = oracle.max_threads()
+    res = {"host_cpu": _host_cpu(), "host_logical_cpus": os.cpu_count(), "threads_all": allthreads}
+    for name in ("C0", "C1", "C2", "C3", "C4", "C4b"):
+        p = gs.configs()[name]
+        x = gs.generate(p)
+        if p.decode:
+            sample, xs, ps, tokens = f"all {p.N} sequences, one token each", x, p, p.N
+        elif p.N == 1 and p.T <= 512:
+            sample, xs, ps, tokens = f"all {p.T} tokens", x, p, p.T
+        else:
+            # the first S tokens of the first sequence, S sized for about
+            # per_run_s of single-thread work on all value heads
+            L0 = p.seq_lens[0]
+            x0 = {n: a for n, a in x.items()}
+            if p.N > 1:
+                t1 = int(x["cu_seqlens"][1])
+                x0 = {n: (a[:t1] if n in ("q", "k", "v", "z", "g", "beta") else a) for n, a in x.items()}
+                x0["state"] = None if x["state"] is None else x["state"][:1]
+                x0["conv_state"] = None if x["conv_state"] is None else x["conv_state"][:1]
+            S = min(L0, 64)
+            t = _time_oracle(oracle, dataclasses.replace(p, seq_lens=[S]), _prefix(x0, S), 1)
+            S = int(min(L0, max(64, S * per_run_s / max(t, 1e-3))))
+            ps, xs, tokens = dataclasses.replace(p, seq_lens=[S]), _prefix(x0, S), S
+            sample = f"first {S} tokens of sequence 0 ({L0} tokens), all {p.Hv} value heads"
+        entry = {"sample": sample}
+        for label, th in (("one_thread", 1), ("all_threads", allthreads)):
+            reps, t = 0, 0.0
+            while reps < 20 and (t < per_run_s or reps < 2):
+                t += _time_oracle(oracle, ps, xs, th)
+                reps += 1
+            used = min(th, ps.N * ps.Hv)
+            entry[label] = {"tokens_per_s": round(reps * tokens / t, 2), "threads": used,
+                            "runs": reps, "seconds": round(t, 2)}
+        res[name] = entry
+        log(f"[bench] cpu oracle {name}: {entry['one_thread']['tokens_per_s']} tok/s (1 thread), "
+            f"{entry['all_threads']['tokens_per_s']} tok/s ({entry['all_threads']['threads']} threads)")
+    return res
+
+
+def _time_oracle(oracle, p, xs, threads):
+    t0 = time.perf_counter()
+    oracle.run_problem(p, xs, threads=threads)
+    return time.perf_counter() - t0
+
+
 def cpu_baseline(pres, target_s: float):
     """The fp64 oracle on the first S tokens of the same C1 inputs, all heads."""
     import numpy as np
@@ -413,8 +492,7 @@ def cpu_baseline(pres, target_s: float):
     p, x = pres["p"], pres["x"]
 
     def run(S):
-        xs = {n: (a[:S] if n in ("q", "k", "v", "z", "g", "beta") else a) for n, a in x.items()}
-        xs["cu_seqlens"] = np.array([0, S], dtype=np.int32)
+        xs = _prefix(x, S)
         t0 = time.perf_counter()
         oracle.run_problem(p, xs)
         return time.perf_counter() - t0
@@ -429,14 +507,7 @@ def cpu_baseline(pres, target_s: float):
         t += run(S)
         reps += 1
     threads = min(oracle.max_threads(), p.N * p.Hv)
-    cpu = "unknown"
-    try:
-        for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                cpu = line.split(":", 1)[1].strip()
-                break
-    except OSError:
-        pass
+    cpu = _host_cpu()
     return {"value": round(reps * S / t, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"first {S} of {p.T} tokens of the same workload, all {p.Hv} value heads, "
                       f"fp64, OpenMP over heads, {reps} runs in {t:.1f} s wall",
@@ -486,6 +557,7 @@ def main():
     opts = None if args.no_options else bench_options(args, hip, pres)
     cfgs = None if args.no_configs else bench_configs(args, hip)
     cpu = None if args.no_cpu_baseline else cpu_baseline(pres, args.cpu_seconds)
+    cpu_cfg = None if args.no_cpu_baseline else cpu_baseline_configs()
 
     p = pres["p"]
     line = {
@@ -507,6 +579,7 @@ def main():
                    "io": "bf16", "state": "fp32", "buffer_sets": pres["buffer_sets"]},
         "roofline": pres["roofline"],
         "cpu_baseline": cpu,
+        "cpu_baseline_configs": cpu_cfg,
         "stages_us": pres["stages_us"],
         "path": pres["path"],
         "decode": dec,

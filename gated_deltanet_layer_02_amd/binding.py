@@ -16,6 +16,9 @@ LIB_PATH = os.path.join(_PKG, "libgdn.so")
 GDN_OK = 0
 GDN_F32, GDN_BF16 = 0, 1
 GDN_FLAG_L2NORM_QK = 0x1
+GDN_FLAG_SEPARATE_LAUNCHES = 0x2
+GDN_FLAG_PREP_WRITE_BACK = 0x4
+GDN_FLAG_TEST_WAITS_GIVE_UP = 0x8
 PREFILL_MAX_KERNELS = 64   # kernels a profiled call may record (the caller's choice)
 STAGE_NAMES = {0: "chunk_table", 1: "chunk_prep", 2: "state_sweep", 3: "gated_norm",
                4: "conv_state", 5: "prep_sweep"}
@@ -27,7 +30,7 @@ STATUS_NAMES = {0: "GDN_OK", 1: "GDN_ERR_NULL_ARG", 2: "GDN_ERR_BAD_SHAPE",
 
 EXPORTED = ["gdn_status_string", "gdn_prefill_workspace_size", "gdn_prefill",
             "gdn_prefill_profiled", "gdn_prefill_ex", "gdn_decode", "gdn_decode_verify",
-            "gdn_decode_commit", "gdn_pipeline_timeouts"]
+            "gdn_decode_commit", "gdn_prefill_wait_status"]
 
 
 class GdnError(RuntimeError):
@@ -75,12 +78,14 @@ class PrefillArgs(ctypes.Structure):
 def make_desc(num_seqs: int, total_tokens: int, num_k_heads: int = 16, num_v_heads: int = 32,
               io_dtype: int = GDN_BF16, state_dtype: int = GDN_F32, scale: float = 1.0,
               l2_eps: float = 1e-6, norm_eps: float = 1e-6, l2norm: bool = True,
-              head_dim: int = 128, conv_kernel: int = 4) -> Desc:
+              head_dim: int = 128, conv_kernel: int = 4, separate_launches: bool = False,
+              prep_write_back: bool = False, flags: int = 0) -> Desc:
+    f = (GDN_FLAG_L2NORM_QK if l2norm else 0) | (GDN_FLAG_SEPARATE_LAUNCHES if separate_launches else 0) \
+        | (GDN_FLAG_PREP_WRITE_BACK if prep_write_back else 0) | int(flags)
     return Desc(num_seqs=num_seqs, total_tokens=total_tokens, num_k_heads=num_k_heads,
                 num_v_heads=num_v_heads, head_k_dim=head_dim, head_v_dim=head_dim,
                 conv_kernel=conv_kernel, io_dtype=io_dtype, state_dtype=state_dtype,
-                scale=scale, l2_eps=l2_eps, norm_eps=norm_eps,
-                flags=GDN_FLAG_L2NORM_QK if l2norm else 0)
+                scale=scale, l2_eps=l2_eps, norm_eps=norm_eps, flags=f)
 
 
 _lib = None
@@ -112,8 +117,8 @@ def lib():
         l.gdn_decode_commit.argtypes = [dp, i32] + [vp] * 6 + [i32, vp]
         l.gdn_decode.restype = ctypes.c_int
         l.gdn_decode.argtypes = [dp] + [vp] * 11 + [i32, vp, vp]
-        l.gdn_pipeline_timeouts.restype = ctypes.c_int
-        l.gdn_pipeline_timeouts.argtypes = [ctypes.POINTER(ctypes.c_uint32)]
+        l.gdn_prefill_wait_status.restype = ctypes.c_int
+        l.gdn_prefill_wait_status.argtypes = [vp, sz, vp, ctypes.POINTER(i32)]
         _lib = l
     return _lib
 
@@ -125,13 +130,15 @@ def gdn_status_string(code: int) -> str:
         return STATUS_NAMES.get(int(code), f"status {code}")
 
 
-def gdn_pipeline_timeouts() -> int:
-    """Waits of pipelined prefill launches on the current device that gave up."""
-    n = ctypes.c_uint32(0)
-    rc = lib().gdn_pipeline_timeouts(ctypes.byref(n))
+def gdn_prefill_wait_status(workspace, stream=None) -> int:
+    """1 if a wait of the last prefill call on `workspace` gave up (its outputs
+    are invalid), else 0.  Synchronises `stream`."""
+    f = ctypes.c_int32(-1)
+    rc = lib().gdn_prefill_wait_status(_ws_ptr(workspace), _ws_bytes(workspace), _stream(stream),
+                                       ctypes.byref(f))
     if rc != GDN_OK:
-        raise GdnError(rc, "gdn_pipeline_timeouts")
-    return int(n.value)
+        raise GdnError(rc, "gdn_prefill_wait_status")
+    return int(f.value)
 
 
 def gdn_prefill_workspace_size(desc: Desc) -> int:

@@ -41,7 +41,9 @@ gdn_status check_desc_common(const gdn_desc* d) {
     if (d->num_k_heads > 4096 || d->num_v_heads > 4096) return GDN_ERR_BAD_SHAPE;
     if (d->head_k_dim != gdn::kD || d->head_v_dim != gdn::kD) return GDN_ERR_UNSUPPORTED;
     if (d->conv_kernel != gdn::kConvK) return GDN_ERR_UNSUPPORTED;
-    if (d->flags & ~GDN_FLAG_L2NORM_QK) return GDN_ERR_UNSUPPORTED;
+    if (d->flags & ~(GDN_FLAG_L2NORM_QK | GDN_FLAG_SEPARATE_LAUNCHES | GDN_FLAG_PREP_WRITE_BACK |
+                     GDN_FLAG_TEST_WAITS_GIVE_UP))
+        return GDN_ERR_UNSUPPORTED;
     if (d->io_dtype != GDN_F32 && d->io_dtype != GDN_BF16) return GDN_ERR_BAD_DTYPE;
     if (d->state_dtype != GDN_F32 && d->state_dtype != GDN_BF16) return GDN_ERR_BAD_DTYPE;
     if (!isfinite(d->scale) || !isfinite(d->l2_eps) || !isfinite(d->norm_eps)) return GDN_ERR_BAD_VALUE;
@@ -78,6 +80,7 @@ PrefillLayout prefill_layout(const gdn_desc* d, bool varlen) {
     PrefillLayout L{};
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t at = off; off = round_up(off + bytes, 256); return at; };
+    L.status = take(gdn::kStatusBytes);   // offset 0, whatever the descriptor
     L.chunk_off = take(sizeof(int32_t) * ((size_t)d->num_seqs + 1));
     L.KB = take(C * Hk * gdn::kKBUnits * frag);
     L.VB = take(C * Hv * gdn::kVBUnits * frag);
@@ -148,6 +151,8 @@ gdn_status prefill_impl(const gdn_desc* d, const gdn_prefill_args& x, hipStream_
     char* ws = static_cast<char*>(x.workspace);
     gdn::PrefillPlan p{};
     p.io_bf16 = d->io_dtype == GDN_BF16;
+    p.allow_pipe = (d->flags & GDN_FLAG_SEPARATE_LAUNCHES) == 0;
+    p.l2_handoff = (d->flags & GDN_FLAG_PREP_WRITE_BACK) == 0;
     p.conv = x.conv_w != nullptr;
     p.gated = x.z != nullptr && x.norm_w != nullptr;
     p.total_tokens = T;
@@ -167,6 +172,8 @@ gdn_status prefill_impl(const gdn_desc* d, const gdn_prefill_args& x, hipStream_
     a.scale = d->scale; a.l2_eps = d->l2_eps;
 
     gdn::SweepArgs& s = p.sweep;
+    s.status = reinterpret_cast<uint64_t*>(ws + L.status);
+    s.epoch = next_epoch();
     s.KB = a.KB; s.VB = a.VB;
     s.initial_state = x.initial_state; s.final_state = x.final_state;
     s.snapshots = x.state_snapshots; s.snap_base = x.snapshot_base;
@@ -178,7 +185,9 @@ gdn_status prefill_impl(const gdn_desc* d, const gdn_prefill_args& x, hipStream_
     p.sync.ready = reinterpret_cast<uint64_t*>(ws + L.ready);
     p.sync.oready = reinterpret_cast<uint64_t*>(ws + L.oready);
     p.sync.xcc = reinterpret_cast<uint64_t*>(ws + L.xcc);
-    p.sync.epoch = next_epoch();
+    p.sync.epoch = s.epoch;
+    // about 2.7 s of the 100 MHz wall clock; none with the test flag
+    p.sync.wait_ticks = (d->flags & GDN_FLAG_TEST_WAITS_GIVE_UP) ? 0 : gdn::kPipeWaitTicks;
 
     gdn::ConvStateArgs& c = p.conv_state;
     c.q = x.q; c.k = x.k; c.v = x.v;
@@ -211,9 +220,18 @@ gdn_prefill_args flat_args(const void* q, const void* k, const void* v, const fl
 
 extern "C" {
 
-gdn_status gdn_pipeline_timeouts(uint32_t* count) {
-    if (count == nullptr) return GDN_ERR_NULL_ARG;
-    return gdn::read_pipe_timeouts(count) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+gdn_status gdn_prefill_wait_status(const void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                   int32_t* failed) {
+    if (failed == nullptr) return GDN_ERR_NULL_ARG;
+    if (workspace == nullptr || workspace_bytes < gdn::kStatusBytes) return GDN_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u) return GDN_ERR_MISALIGNED;
+    uint64_t w[2] = {0, 0};
+    if (hipStreamSynchronize(stream) != hipSuccess) return GDN_ERR_HIP;
+    if (hipMemcpy(w, workspace, sizeof(w), hipMemcpyDeviceToHost) != hipSuccess) return GDN_ERR_HIP;
+    // status[0]: the epoch of the last call on this workspace (even, never 0);
+    // status[1]: that epoch too iff one of its waits gave up
+    *failed = (w[0] != 0 && (w[0] & 1) == 0 && w[1] == w[0]) ? 1 : 0;
+    return GDN_OK;
 }
 
 const char* gdn_status_string(gdn_status s) {

@@ -47,6 +47,11 @@ struct PrepArgs {
 // chunk boundary snap_every * j (j >= 1, before the sequence end) goes to
 // row snap_base[n] + j - 1 of `snapshots`.
 struct SweepArgs {
+    // Call status words at the start of the workspace: status[0] receives the
+    // call's epoch from workgroup 0 of the sweep (every form launches one),
+    // status[1] the same epoch from any bounded wait that gives up.  The call
+    // failed iff both hold its epoch.
+    uint64_t* status; uint64_t epoch;
     const void* KB; const void* VB;
     const void* initial_state; void* final_state;
     void* snapshots; const int32_t* snap_base; int32_t snap_every;
@@ -80,7 +85,9 @@ struct PipeSync {
     uint64_t* xcc = nullptr;
     int32_t xcc_per = 0;          // sweep workgroups per key unit
     uint64_t epoch = 0;
+    uint64_t wait_ticks = 0;      // bound of every wait, in ticks of the 100 MHz wall clock
 };
+constexpr uint64_t kPipeWaitTicks = 1ull << 28;   // wait_ticks of a normal call: about 2.7 s
 
 // Pipelined launch: workgroups [0, n_sweep) run the sweep (the sweep's own
 // grid mapping), then n_prep prep workgroups (one or two units each; prep_xcd:
@@ -101,6 +108,8 @@ struct PipeArgs {
 
 struct PrefillPlan {
     bool io_bf16, conv, gated;
+    bool allow_pipe;              // the pipelined launch may serve this call
+    bool l2_handoff;              // pipelined prep units may leave their results in L2
     int64_t total_tokens;
     int32_t chunk_slots;          // grid rows of the prep kernel
     const void* z; const void* norm_w; float norm_eps;
@@ -111,9 +120,12 @@ struct PrefillPlan {
 };
 
 // Workspace carve-up of one prefill call.
+// The first 256 bytes hold the call status words (SweepArgs::status), at the
+// same offset for every descriptor so that gdn_prefill_wait_status finds them.
 struct PrefillLayout {
-    size_t chunk_off, KB, VB, ready, oready, xcc, total;
+    size_t status, chunk_off, KB, VB, ready, oready, xcc, total;
 };
+constexpr size_t kStatusBytes = 256;
 
 struct DecodeArgs {
     const void* q; const void* k; const void* v;
@@ -163,7 +175,6 @@ struct KernelRecorder {
 };
 
 hipError_t launch_prefill(const PrefillPlan& p, hipStream_t stream, KernelRecorder& rec);
-hipError_t read_pipe_timeouts(uint32_t* count);
 hipError_t launch_decode(const DecodeArgs& a, bool io_bf16, bool state_bf16, bool conv,
                          hipStream_t stream);
 hipError_t launch_verify(const VerifyArgs& a, bool io_bf16, bool state_bf16, bool conv, hipStream_t s);

@@ -28,7 +28,6 @@
 
 #include <algorithm>
 #include <atomic>
-#include <cstdlib>
 #include <type_traits>
 
 #include "gdn_common.hpp"
@@ -812,6 +811,14 @@ __device__ __forceinline__ void state_snapshot(const SweepArgs& a, int n, int j,
 struct SweepSeq {
     int seq_start, L, c_begin, nch;
 };
+
+// Sweep workgroup 0 records the call's epoch in status[0] (every launch form
+// runs a sweep), so that the status words tell this call's failures from an
+// earlier call's.
+__device__ __forceinline__ void mark_call(const SweepArgs& a, int x) {
+    if (x == 0 && threadIdx.x == 0 && a.status != nullptr)
+        __hip_atomic_store(a.status, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ __forceinline__ SweepSeq sweep_seq(const SweepArgs& a, int n) {
     SweepSeq q;
     if (a.cu == nullptr) {
@@ -1057,25 +1064,31 @@ __device__ __forceinline__ void sweep_lds_step(int j, int wave, f32x4 (&S)[NT][8
 // agent-coherent loads, which do not hit a stale copy in any cache.  Epochs
 // are unique per call, so the flags never need clearing.  Waits are bounded:
 // after about 2^28 ticks of the 100 MHz wall clock (2.7 s) a wait gives up,
-// counts itself in gdn_pipe_timeouts and carries on (the call's result is then
-// invalid).
-__device__ uint32_t gdn_pipe_timeouts;
-constexpr uint64_t kPipeWaitTicks = 1ull << 28;
+// marks the call as failed (status[1] = epoch, beside status[0] = epoch that
+// sweep workgroup 0 stores at its start) and carries on: the call's result is
+// then invalid, and the caller learns it from the workspace.
 constexpr int kCoherentLoad = 16;   // cache-policy bits of an agent-coherent load (sc1)
 
 __device__ __forceinline__ uint64_t pipe_flag(const uint64_t* f) {
     return __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// The value of *f once it holds epoch or epoch + 1 (never 0); 0 (counted)
-// when the wait gives up.  A call: its loads are complete when it returns.
-__device__ __noinline__ uint64_t pipe_wait(const uint64_t* f, uint64_t epoch) {
+// A wait that gave up: the call's failure word receives its epoch.
+__device__ __forceinline__ void pipe_fail(uint64_t* status, uint64_t epoch) {
+    if ((threadIdx.x & 63) == 0 && status != nullptr)
+        __hip_atomic_store(status + 1, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The value of *f once it holds epoch or epoch + 1 (never 0); 0 (the call
+// marked failed) when the wait gives up.  A call: its loads are complete when
+// it returns.
+__device__ __noinline__ uint64_t pipe_wait(const uint64_t* f, uint64_t epoch, uint64_t* status,
+                                           uint64_t ticks) {
     const uint64_t t0 = wall_clock64();
     uint64_t v;
     while (!same_epoch(v = pipe_flag(f), epoch)) {
         __builtin_amdgcn_s_sleep(2);
-        if (wall_clock64() - t0 > kPipeWaitTicks) {
-            if ((threadIdx.x & 63) == 0)
-                __hip_atomic_fetch_add(&gdn_pipe_timeouts, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (wall_clock64() - t0 > ticks) {
+            pipe_fail(status, epoch);
             return 0;
         }
     }
@@ -1085,16 +1098,16 @@ __device__ __noinline__ uint64_t pipe_wait(const uint64_t* f, uint64_t epoch) {
 // true once f[0 .. count) all hold epoch (or epoch + 1; each lane watches every 64th);
 // polls about every 0.3 us (these waits are not on the sweep's chain, and
 // fewer polls of the flag lines leave the memory channels to the sweep)
-__device__ __noinline__ bool pipe_wait_all(const uint64_t* f, int count, uint64_t epoch) {
+__device__ __noinline__ bool pipe_wait_all(const uint64_t* f, int count, uint64_t epoch, uint64_t* status,
+                                           uint64_t ticks) {
     const int lane = threadIdx.x & 63;
     const uint64_t t0 = wall_clock64();
     for (int base = 0; base < count; base += 64) {
         const int i = base + lane;
         while (!__all(i >= count || same_epoch(pipe_flag(f + i), epoch))) {
             __builtin_amdgcn_s_sleep(10);
-            if (wall_clock64() - t0 > kPipeWaitTicks) {
-                if (lane == 0)
-                    __hip_atomic_fetch_add(&gdn_pipe_timeouts, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (wall_clock64() - t0 > ticks) {
+                pipe_fail(status, epoch);
                 return false;
             }
         }
@@ -1123,6 +1136,7 @@ __device__ __forceinline__ void sweep_wg(const SweepArgs& a, int x, unsigned cha
     lds_b16x8* buf1 = buf0 + L::kUnits * 64;
     lds_u16* stage = (lds_u16*)(smem + L::kOps);
 
+    mark_call(a, x);
     int u, sg;
     if (!sweep_unit(x, L::kGroups, a.N, a.Hk, a.Hv, u, sg)) return;
     const int n = u / a.Hv, h = u % a.Hv, hk = h / (a.Hv / a.Hk);
@@ -1146,7 +1160,8 @@ __device__ __forceinline__ void sweep_wg(const SweepArgs& a, int x, unsigned cha
         // after a wait gives up, the wave stops waiting (the call is invalid
         // anyway) so that it still ends within one wait's bound
         bool live = true;
-        if (kPipe && q.nch > 0) live = pipe_wait(ready + (size_t)q.c_begin * a.Hk, ps.epoch) != 0;
+        if (kPipe && q.nch > 0)
+            live = pipe_wait(ready + (size_t)q.c_begin * a.Hk, ps.epoch, a.status, ps.wait_ticks) != 0;
         // Per iteration: copies of chunk j, then the stores of chunk j - 3,
         // then vmcnt(kStores): loads and stores retire in order, so the copies
         // have landed while the stores may still be in flight; they are
@@ -1177,7 +1192,7 @@ __device__ __forceinline__ void sweep_wg(const SweepArgs& a, int x, unsigned cha
             // the next issue overwrites the other buffer, which the compute
             // waves finished with before this barrier
             if (kPipe && live && j + 1 < q.nch && !same_epoch(ahead, ps.epoch))
-                live = pipe_wait(ready + (c + 1) * a.Hk, ps.epoch) != 0;
+                live = pipe_wait(ready + (c + 1) * a.Hk, ps.epoch, a.status, ps.wait_ticks) != 0;
         }
         if (q.nch > 0) {   // the last three chunks, once the compute waves staged the last one
             __syncthreads();
@@ -1234,6 +1249,7 @@ __global__ __launch_bounds__(64 * (SW + PW)) void gdn_state_sweep_lds_kernel(Swe
 // (fp32 fragments are 2 KB; this path serves fp32 inputs, not the bf16 layer).
 __global__ __launch_bounds__(64) void gdn_state_sweep_f32_kernel(SweepArgs a) {
     typedef Frag<float> F;
+    mark_call(a, blockIdx.x);
     int u, sg;
     if (!sweep_unit(blockIdx.x, 8, a.N, a.Hk, a.Hv, u, sg)) return;
     const int n = u / a.Hv, h = u % a.Hv, hk = h / (a.Hv / a.Hk);
@@ -1398,9 +1414,10 @@ __device__ __forceinline__ void pipe_prep_unit(const PipeArgs& a, int b, int hal
 
 // Wave 0 of a post workgroup waits, the others meet it at a barrier; the
 // verdict goes through LDS word *box.
-__device__ __forceinline__ bool post_wait(const uint64_t* f, int count, uint64_t epoch, volatile int* box) {
+__device__ __forceinline__ bool post_wait(const uint64_t* f, int count, const PipeSync& ps, uint64_t* status,
+                                          volatile int* box) {
     if (threadIdx.x < 64) {
-        const bool ok = pipe_wait_all(f, count, epoch);
+        const bool ok = pipe_wait_all(f, count, ps.epoch, status, ps.wait_ticks);
         if (threadIdx.x == 0) *box = ok;
     }
     __syncthreads();
@@ -1418,7 +1435,8 @@ __device__ __forceinline__ bool pipe_norm_unit(const PipeArgs& a, int c, int hk,
     int n, t0, len, seq_start;
     if (!locate_chunk(a.prep, c, n, t0, len, seq_start)) return true;
     const int Hv = a.prep.Hv, group = Hv / a.prep.Hk, h0 = hk * group;
-    if (!post_wait(a.sync.oready + ((size_t)c * Hv + h0) * 8, group * 8, a.sync.epoch, box)) return false;
+    if (!post_wait(a.sync.oready + ((size_t)c * Hv + h0) * 8, group * 8, a.sync, a.sweep.status, box))
+        return false;
     uint16_t* out = static_cast<uint16_t*>(a.sweep.out) + (size_t)t0 * Hv * kD;
     const uint16_t* z = static_cast<const uint16_t*>(a.z) + (size_t)t0 * Hv * kD;
     const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(out, 0, 0x7fffffff, 0x00020000);
@@ -1486,7 +1504,7 @@ __device__ void pipe_post(const PipeArgs& a, int w, volatile int* box) {
             const int L = cs.cu ? cs.cu[n + 1] - cs.cu[n] : cs.T;
             if (live && L > 0 && cs.conv_state_in != nullptr) {
                 const size_t c0 = cs.cu ? a.sweep.chunk_off[n] : 0;
-                live = post_wait(a.sync.ready + c0 * Hk, Hk, a.sync.epoch, box);
+                live = post_wait(a.sync.ready + c0 * Hk, Hk, a.sync, a.sweep.status, box);
             }
             conv_state_channel<uint16_t>(cs, n, (it % nblk) * 512 + threadIdx.x);
         }
@@ -1671,11 +1689,9 @@ static int pipe_post_blocks(const PrefillPlan& p, int cus) {
 // also wait), at most three quarters, so that prep workgroups always find
 // CUs.  Workgroup x is dispatched to XCD x % 8 from that XCD's own share; the
 // sweep and post counts are multiples of 8, so the bound holds on every XCD.
-// GDN_PREFILL_PIPELINE=0 in the environment turns it off.
+// GDN_FLAG_SEPARATE_LAUNCHES (allow_pipe false) turns it off.
 static bool use_pipe(const PrefillPlan& p) {
-    if (!p.io_bf16 || p.sync.ready == nullptr || p.chunk_slots <= 0) return false;
-    const char* env = getenv("GDN_PREFILL_PIPELINE");
-    if (env != nullptr && env[0] == '0') return false;
+    if (!p.allow_pipe || !p.io_bf16 || p.sync.ready == nullptr || p.chunk_slots <= 0) return false;
     const int cus = device_cus(), ns = sweep_blocks(p);
     return 2 * ns <= cus && 4 * (ns + pipe_post_blocks(p, cus)) <= 3 * cus;
 }
@@ -1701,11 +1717,10 @@ static hipError_t launch_pipe(const PrefillPlan& p, hipStream_t s) {
     a.n_post = pipe_post_blocks(p, device_cus());
     a.post_first = pipe_post_first(p) ? 1 : 0;
     // prep units leave their fragments in the L2 of an XCD they share with
-    // all of their key unit's sweep workgroups; GDN_PIPE_L2=0 in the
-    // environment has them write the L2 back to memory always
+    // all of their key unit's sweep workgroups; GDN_FLAG_PREP_WRITE_BACK
+    // (l2_handoff false) has them write the L2 back to memory always
     a.sync.xcc_per = (p.prep.Hv / p.prep.Hk) * SweepLds<kSweepSW, kSweepNT>::kGroups;
-    const char* l2 = getenv("GDN_PIPE_L2");
-    if ((l2 != nullptr && l2[0] == '0') || a.sync.xcc_per > 64 || SweepLds<kSweepSW, kSweepNT>::kGroups > kD / 16)
+    if (!p.l2_handoff || a.sync.xcc_per > 64 || SweepLds<kSweepSW, kSweepNT>::kGroups > kD / 16)
         a.sync.xcc = nullptr;
     GDN_TRY(allow_dynamic_lds(nullptr, 0));
     auto kern = p.conv ? gdn_prefill_pipe_kernel<true> : gdn_prefill_pipe_kernel<false>;
@@ -1761,8 +1776,5 @@ hipError_t launch_prefill(const PrefillPlan& p, hipStream_t stream, KernelRecord
     return rec.call_end(stream);
 }
 
-hipError_t read_pipe_timeouts(uint32_t* count) {
-    return hipMemcpyFromSymbol(count, HIP_SYMBOL(gdn_pipe_timeouts), sizeof(uint32_t), 0, hipMemcpyDeviceToHost);
-}
 
 }  // namespace gdn

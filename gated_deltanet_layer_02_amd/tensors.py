@@ -45,10 +45,12 @@ class PrefillCall:
                  pass_cu: Optional[bool] = None, state_bf16: bool = False,
                  slots: Optional[np.ndarray] = None, num_state_slots: int = 0,
                  snapshot_every: int = 0, snapshot_base: Optional[np.ndarray] = None,
-                 num_snapshot_slots: int = 0, device="cuda"):
+                 num_snapshot_slots: int = 0, separate_launches: bool = False,
+                 prep_write_back: bool = False, device="cuda"):
         """x["state"] / x["conv_state"] hold num_state_slots rows (a pool)
         when `slots` is given, else N rows; x["state"] is float32 or, with
-        state_bf16, uint16 bf16 bits."""
+        state_bf16, uint16 bf16 bits.  separate_launches / prep_write_back set
+        GDN_FLAG_SEPARATE_LAUNCHES / GDN_FLAG_PREP_WRITE_BACK."""
         import torch
         self.cu_host = np.asarray(x["cu_seqlens"], dtype=np.int32)
         self.N = len(self.cu_host) - 1
@@ -73,7 +75,8 @@ class PrefillCall:
         self.extended = state_bf16 or slots is not None or self.num_state_slots > 0 or self.snapshot_every > 0
         sdt = torch.bfloat16 if state_bf16 else torch.float32
         self.desc = B.make_desc(self.N, self.T, Hk, Hv, B.GDN_BF16 if io_bf16 else B.GDN_F32,
-                                B.GDN_BF16 if state_bf16 else B.GDN_F32, scale, l2_eps, norm_eps, l2norm)
+                                B.GDN_BF16 if state_bf16 else B.GDN_F32, scale, l2_eps, norm_eps, l2norm,
+                                separate_launches=separate_launches, prep_write_back=prep_write_back)
         self.out = empty_like_io((max(self.T, 1), Hv, 128), io_bf16, d)
         self.final_state = (torch.empty((rows, Hv, 128, 128), dtype=sdt, device=d)
                             if want_final_state else None)
@@ -101,6 +104,16 @@ class PrefillCall:
             return
         B.gdn_prefill(self.desc, self.q, self.k, self.v, self.g, self.beta, stream=stream,
                       **self.kwargs())
+
+    def set_launch(self, separate_launches: bool = False, prep_write_back: bool = False):
+        """Choose the launch form of later calls (descriptor flags)."""
+        f = self.desc.flags & ~(B.GDN_FLAG_SEPARATE_LAUNCHES | B.GDN_FLAG_PREP_WRITE_BACK)
+        self.desc.flags = f | (B.GDN_FLAG_SEPARATE_LAUNCHES if separate_launches else 0) \
+            | (B.GDN_FLAG_PREP_WRITE_BACK if prep_write_back else 0)
+
+    def wait_status(self, stream=None) -> int:
+        """1 if a wait of the last call on this workspace gave up."""
+        return B.gdn_prefill_wait_status(self.workspace, stream=stream)
 
     def run_profiled(self, events, stream=None):
         return B.gdn_prefill_profiled(self.desc, self.q, self.k, self.v, self.g, self.beta,

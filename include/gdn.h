@@ -27,9 +27,13 @@
  *
  * Conventions common to every entry point
  *  - Pointers to tensors are DEVICE pointers owned by the caller.  The library
- *    never allocates, frees or synchronises; scratch memory comes from the
- *    caller's workspace.  It keeps no mutable global state: concurrent calls
- *    on different streams are safe when their buffers do not overlap.
+ *    never allocates or frees device memory and never synchronises (except
+ *    gdn_prefill_wait_status, a query that does so by definition); scratch
+ *    memory comes from the caller's workspace.  Whatever a call leaves behind
+ *    on the device lives in the caller's buffers; the host side keeps only
+ *    thread-safe caches (CU counts per device, an epoch counter).  Concurrent
+ *    calls on different streams are safe when their buffers (workspaces
+ *    included) do not overlap.
  *  - Calls are asynchronous in the order of `stream`.  GDN_OK means the work
  *    was enqueued.
  *  - Every argument is validated on the host before anything is enqueued; on
@@ -72,6 +76,18 @@ typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
 /* L2-normalise q and k (step 2).  Without it q and k enter the recurrence as
  * they leave the conv (or as given, without conv); scale is still applied. */
 #define GDN_FLAG_L2NORM_QK 0x1u
+/* Prefill launch form (see gdn_prefill, "Launches"): never the pipelined
+ * single launch, always the separate kernels one after another. */
+#define GDN_FLAG_SEPARATE_LAUNCHES 0x2u
+/* Pipelined prefill: every prep unit writes its results back to memory
+ * before publishing them, instead of leaving them in the L2 of the XCD that
+ * all of their readers run on (same results; a diagnostic switch). */
+#define GDN_FLAG_PREP_WRITE_BACK 0x4u
+/* Testing the failure report: every wait of a pipelined launch gives up at
+ * its first check instead of after about 2.7 s, so the call ends quickly with
+ * invalid outputs and gdn_prefill_wait_status reports it.  No effect on
+ * separate launches. */
+#define GDN_FLAG_TEST_WAITS_GIVE_UP 0x8u
 
 typedef struct {
     int32_t num_seqs;       /* N >= 1 */
@@ -92,10 +108,16 @@ typedef struct {
 /* Human-readable name of a status code (static storage). */
 const char* gdn_status_string(gdn_status s);
 
-/* Waits of pipelined prefill launches (see gdn_prefill) on the current
- * device that gave up since the library was loaded: 0 unless work on other
- * streams held every CU for seconds.  Synchronous (a device-to-host copy). */
-gdn_status gdn_pipeline_timeouts(uint32_t* count);
+/* Outcome of the last prefill call enqueued with `workspace` (see
+ * gdn_prefill, "Launches"): waits for `stream` (the stream that call ran on),
+ * then reads two words the call keeps at the start of its workspace.
+ * *failed = 1 when a wait of that call's pipelined launch gave up (its
+ * outputs are then invalid), 0 otherwise, and 0 for a workspace no prefill
+ * call has used yet.  Synchronous: the one entry point that blocks the host.
+ * GDN_ERR_WORKSPACE for a workspace smaller than 256 bytes, GDN_ERR_HIP when
+ * the synchronisation or the copy fails. */
+gdn_status gdn_prefill_wait_status(const void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream, int32_t* failed);
 
 /* Bytes of device workspace gdn_prefill needs for descriptor d (a bound that
  * depends on N and T_total only through total_tokens / 64 + N chunks). */
@@ -128,14 +150,28 @@ gdn_status gdn_prefill_workspace_size(const gdn_desc* d, size_t* bytes);
  * Launches: with bf16 io, when the sweep's workgroups need at most half of
  * the device's CUs (one or a few long sequences), the chunk prep and the
  * sweep run as one launch whose sweep workgroups wait for each chunk's prep
- * (bounded waits; GDN_PREFILL_PIPELINE=0 in the environment selects separate
- * launches).  In that launch a chunk's prep results stay in the L2 of the XCD
- * that all of their readers run on, where each sweep workgroup records its
- * XCD; units whose readers are elsewhere write them back to memory first
- * (GDN_PIPE_L2=0 in the environment: every unit does).  Both give the same
- * bits.  Work on other streams running beside such a call must leave it
- * CUs for its prep workgroups; a wait that gives up after about 2.7 s counts
- * itself in gdn_pipeline_timeouts and leaves that call's result invalid.
+ * units, and whose gated-norm workgroups wait for the sweep's output, through
+ * flags in the workspace (GDN_FLAG_SEPARATE_LAUNCHES selects separate
+ * launches instead).  A chunk's prep results stay in the L2 of the XCD that
+ * all of their readers run on, where each sweep workgroup records its XCD;
+ * units whose readers are elsewhere write them back to memory first
+ * (GDN_FLAG_PREP_WRITE_BACK: every unit does).  Every form gives the same
+ * bits.
+ * Forward progress of the pipelined launch rests on how the device dispatches
+ * one launch's workgroups, which the library arranges for but cannot enforce:
+ *  - workgroups start in increasing grid order, workgroup x on XCD x mod 8
+ *    (eight XCDs, each dispatching from its own share of the grid);
+ *  - one workgroup per CU (each takes more than half of a CU's 160 KB LDS);
+ *  - the waiting workgroups (the sweep's, at most half of the CUs, and the
+ *    gated norm's, together at most three quarters, counted per XCD) never
+ *    hold every CU: the prep workgroups they wait for always find one, unless
+ *    work on other streams occupies the remaining CUs until the waits give up.
+ * Every wait is bounded (about 2.7 s of wall clock).  One that gives up marks
+ * the call as failed in its workspace and stops waiting, so the launch still
+ * ends; that call's outputs are then invalid, and gdn_prefill_wait_status
+ * reports it.  Callers that cannot keep the CUs free for the call, or that
+ * must not depend on the dispatch order, pass GDN_FLAG_SEPARATE_LAUNCHES: the
+ * separate kernels never wait on each other.
  */
 gdn_status gdn_prefill(const gdn_desc* d,
                        const void* q, const void* k, const void* v,

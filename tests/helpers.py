@@ -13,6 +13,13 @@ from oracle import oracle
 # inputs and 1e-2 for bf16 inputs; conv states bit-exact.
 TOL_F32 = 1e-4
 TOL_BF16 = 1e-2
+# Localised-error guard on single (64-token chunk, value head) blocks of the
+# output, a multiple of the tolerance: the stated tolerance is a whole-tensor
+# bar, and a chunk whose outputs are small (the first chunks of a sequence
+# started from a small or zero state) carries a larger relative error after
+# the gated RMSNorm scales it back to unit size, while a chunk computed from
+# a wrong state or boundary is off by O(1).
+CHUNK_GUARD = 5.0
 
 
 def rel_l2(x, ref) -> float:
@@ -45,19 +52,126 @@ def gpu_prefill(p: gs.Problem, x: dict, **kw):
     return out, fs, cs, call
 
 
-def check_prefill(p: gs.Problem, x: dict, heads=None, tol=None, **kw):
-    """GPU prefill vs the oracle on value heads `heads` (default: all)."""
+def _chunk_starts(p: gs.Problem) -> np.ndarray:
+    """First token of every 64-token chunk of every sequence (the chunk grid
+    restarts at each sequence start), in packed token order."""
+    starts, t0 = [], 0
+    for L in p.seq_lens:
+        starts.extend(range(t0, t0 + L, 64))
+        t0 += L
+    return np.asarray(starts, dtype=np.int64)
+
+
+class HeadReport:
+    """Parity figures of one prefill over a range of value heads: squared
+    error and reference sums per value head and per (chunk, value head) of the
+    output, and per (sequence, value head) of the final state, so that batches
+    of heads combine into whole-tensor figures."""
+
+    def __init__(self):
+        self.o_err, self.o_ref = {}, {}          # head -> sums over tokens and dv
+        self.c_worst = (0.0, -1, -1)             # (rel_l2, chunk, head)
+        self.s_err, self.s_ref = {}, {}          # head -> sums over sequences, dv, dk
+        self.s_worst = (0.0, -1, -1)             # (rel_l2, sequence, head)
+
+    def add(self, p, out, fs, r_out, r_fs, h0):
+        starts = _chunk_starts(p)
+        for j in range(r_fs.shape[1]):
+            h = h0 + j
+            if p.T > 0:
+                d2 = np.sum((out[:, j] - r_out[:, j]) ** 2, axis=-1)     # [T]
+                r2 = np.sum(r_out[:, j] ** 2, axis=-1)
+                self.o_err[h], self.o_ref[h] = float(d2.sum()), float(r2.sum())
+                ce, cr = np.add.reduceat(d2, starts), np.add.reduceat(r2, starts)
+                rel = np.sqrt(ce / np.maximum(cr, 1e-300))
+                c = int(np.argmax(rel))
+                if rel[c] > self.c_worst[0]:
+                    self.c_worst = (float(rel[c]), c, h)
+            se = np.sum((fs[:, j] - r_fs[:, j]) ** 2, axis=(-2, -1))      # [N]
+            sr = np.sum(r_fs[:, j] ** 2, axis=(-2, -1))
+            self.s_err[h], self.s_ref[h] = float(se.sum()), float(sr.sum())
+            rel = np.sqrt(se / np.maximum(sr, 1e-300))
+            n = int(np.argmax(rel))
+            if rel[n] > self.s_worst[0]:
+                self.s_worst = (float(rel[n]), n, h)
+
+    @staticmethod
+    def _whole(err, ref):
+        e, r = sum(err.values()), sum(ref.values())
+        return float(np.sqrt(e / r)) if r > 0 else float(np.sqrt(e))
+
+    def head_worst(self, err, ref):
+        if not err:
+            return (0.0, -1)
+        rel = {h: np.sqrt(err[h] / ref[h]) if ref[h] > 0 else np.sqrt(err[h]) for h in err}
+        h = max(rel, key=rel.get)
+        return (float(rel[h]), h)
+
+    def figures(self):
+        return {"out": self._whole(self.o_err, self.o_ref) if self.o_err else 0.0,
+                "out_worst_head": self.head_worst(self.o_err, self.o_ref),
+                "out_worst_chunk": self.c_worst,
+                "state": self._whole(self.s_err, self.s_ref),
+                "state_worst_head": self.head_worst(self.s_err, self.s_ref),
+                "state_worst_seq_head": self.s_worst}
+
+    def check(self, tol, chunk_check=True, name=""):
+        f = self.figures()
+        assert f["out"] <= tol, f"{name}: out rel_l2 {f['out']:.3e} > {tol}"
+        assert f["state"] <= tol, f"{name}: final state rel_l2 {f['state']:.3e} > {tol}"
+        assert f["out_worst_head"][0] <= tol, f"{name}: out of head {f['out_worst_head']}"
+        assert f["state_worst_head"][0] <= tol, f"{name}: state of head {f['state_worst_head']}"
+        assert f["state_worst_seq_head"][0] <= tol, f"{name}: state (seq, head) {f['state_worst_seq_head']}"
+        if chunk_check:
+            assert f["out_worst_chunk"][0] <= CHUNK_GUARD * tol, \
+                f"{name}: out (chunk, head) {f['out_worst_chunk']}"
+        return f
+
+    def __str__(self):
+        f = self.figures()
+        return (f"rel_l2 out {f['out']:.2e} (worst head {f['out_worst_head'][1]}: {f['out_worst_head'][0]:.2e}; "
+                f"worst chunk {f['out_worst_chunk'][1]} of head {f['out_worst_chunk'][2]}: "
+                f"{f['out_worst_chunk'][0]:.2e}), state {f['state']:.2e} (worst head "
+                f"{f['state_worst_head'][1]}: {f['state_worst_head'][0]:.2e}; worst (seq, head) "
+                f"{f['state_worst_seq_head'][1:]}: {f['state_worst_seq_head'][0]:.2e})")
+
+
+def compare_heads(p, out, fs, r_out, r_fs, tol, chunk_check=True, h0=0):
+    """One comparison of GPU results (out [T, nh, dv], fs [N, nh, dv, dk],
+    value heads h0 ..) with the oracle's on the same heads: whole-tensor, per
+    head and per (chunk, head) rel-L2, every output finite."""
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(fs))
+    rep = HeadReport()
+    rep.add(p, out, fs, r_out, r_fs, h0)
+    rep.check(tol, chunk_check, p.name)
+    return rep
+
+
+def check_prefill(p: gs.Problem, x: dict, tol=None, batch=None, chunk_check=None, **kw):
+    """GPU prefill vs the oracle on every value head (the oracle runs `batch`
+    heads at a time to bound host memory).  Asserts the whole-tensor, per-head
+    and per-(sequence, head) rel-L2 of outputs and final states, and, for gated
+    bf16 layers, per (chunk, head) of the output against CHUNK_GUARD x tol;
+    every output finite; conv
+    state bit-exact.  Returns the HeadReport."""
     say(f"prefill case: {p.name} lens={list(p.seq_lens)[:8]}{'...' if p.N > 8 else ''} "
         f"Hk={p.Hk} Hv={p.Hv} io={p.io} conv={p.conv} gate={p.gate}")
     out, fs, cs, call = gpu_prefill(p, x, **kw)
-    h0, h1 = heads if heads is not None else (0, p.Hv)
-    r_out, r_fs, r_cs = oracle.run_problem(p, x, heads=(h0, h1))
     tol = tol if tol is not None else (TOL_F32 if p.io == gs.F32 else TOL_BF16)
-    e_out = rel_l2(out[:, h0:h1], r_out) if p.T > 0 else 0.0
-    e_fs = rel_l2(fs[:, h0:h1], r_fs)
-    assert np.all(np.isfinite(out[:, h0:h1]))
-    assert e_out <= tol, f"{p.name}: out rel_l2 {e_out:.3e} > {tol}"
-    assert e_fs <= tol, f"{p.name}: final state rel_l2 {e_fs:.3e} > {tol}"
+    if chunk_check is None:
+        chunk_check = p.gate and p.io == gs.BF16
+    assert np.all(np.isfinite(out)), f"{p.name}: non-finite outputs"
+    assert np.all(np.isfinite(fs)), f"{p.name}: non-finite final states"
+    batch = batch or p.Hv
+    rep = HeadReport()
+    r_cs = None
+    for h0 in range(0, p.Hv, batch):
+        h1 = min(p.Hv, h0 + batch)
+        r_out, r_fs, r_cs_b = oracle.run_problem(p, x, heads=(h0, h1))
+        r_cs = r_cs_b if r_cs is None else r_cs
+        rep.add(p, out[:, h0:h1], fs[:, h0:h1], r_out, r_fs, h0)
+        del r_out, r_fs
+    rep.check(tol, chunk_check, p.name)
     if cs is not None and r_cs is not None:
         assert np.array_equal(cs, r_cs), f"{p.name}: conv state not bit-exact"
-    return e_out, e_fs
+    return rep

@@ -81,7 +81,8 @@ def test_prefill_validation_errors():
         (dict(head_k_dim=64), {}, 3),
         (dict(head_v_dim=256), {}, 3),
         (dict(conv_kernel=3), {}, 3),
-        (dict(flags=0x8), {}, 3),
+        (dict(flags=0x10), {}, 3),
+        (dict(flags=0xF), dict(ws_bytes=1024), 6),        # the launch-form and test flags are accepted
         (dict(io_dtype=5), {}, 4),
         (dict(state_dtype=B.GDN_BF16), {}, 4),           # gdn_prefill: fp32 state (gdn_prefill_ex: either)
         (dict(scale=float("nan")), {}, 9),
@@ -112,6 +113,18 @@ def test_prefill_validation_errors():
     bad = B.make_desc(1, 10, head_dim=64)
     assert lib.gdn_prefill_workspace_size(ctypes.byref(bad), ctypes.byref(n)) == 3
     assert lib.gdn_prefill_workspace_size(ctypes.byref(B.make_desc(1, 10)), None) == 1
+
+
+def test_wait_status_validation():
+    """gdn_prefill_wait_status checks its arguments before it synchronises or
+    copies anything."""
+    lib = gdn.lib()
+    f = ctypes.c_int32(-1)
+    assert lib.gdn_prefill_wait_status(FAKE, 1 << 20, None, None) == 1              # NULL result
+    assert lib.gdn_prefill_wait_status(None, 1 << 20, None, ctypes.byref(f)) == 6     # no workspace
+    assert lib.gdn_prefill_wait_status(FAKE, 255, None, ctypes.byref(f)) == 6        # < 256 bytes
+    assert lib.gdn_prefill_wait_status(FAKE + 16, 1 << 20, None, ctypes.byref(f)) == 5
+    assert f.value == -1
 
 
 def test_prefill_profiled_needs_events():

@@ -1,9 +1,9 @@
 """The pipelined prefill launch (chunk prep and state sweep in one grid, with
 per-chunk flags between them) against separate launches of the same kernels
-(GDN_PREFILL_PIPELINE=0).  Both run the same arithmetic in the same order, so
-every output must match bit for bit; the pipelined result is also checked
-against the fp64 oracle.  Which form ran is read from the stage ids of a
-profiled call."""
+(GDN_FLAG_SEPARATE_LAUNCHES).  Both run the same arithmetic in the same order,
+so every output must match bit for bit; the pipelined result is also checked
+against the fp64 oracle on every value head.  Which form ran is read from the
+stage ids of a profiled call; every call's wait status must be clean."""
 import ctypes
 import zlib
 
@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 import gdn_synth as gs
-from helpers import TOL_BF16, io_to_f64, rel_l2, say
+from helpers import TOL_BF16, compare_heads, io_to_f64, rel_l2, say
 from oracle import oracle
 
 pytestmark = pytest.mark.gpu
@@ -62,15 +62,14 @@ def _outputs(call, rows=None):
     return res
 
 
-def _run_both(p, x, monkeypatch, expect_pipe, **kw):
+def _run_both(p, x, expect_pipe, **kw):
     """Outputs of the pipelined and of the separate launches (two calls each,
     on the same workspace, to cover flags left by an earlier call)."""
     import torch
     from gated_deltanet_layer_02_amd.tensors import PrefillCall
     res = {}
     for pipe in (True, False):
-        monkeypatch.setenv("GDN_PREFILL_PIPELINE", "1" if pipe else "0")
-        call = PrefillCall(x, Hk=p.Hk, Hv=p.Hv, io_bf16=True, **kw)
+        call = PrefillCall(x, Hk=p.Hk, Hv=p.Hv, io_bf16=True, separate_launches=not pipe, **kw)
         if not call.extended:
             st = _stages(call)
             say(f"  pipeline={int(pipe)}: stages {st}")
@@ -79,9 +78,11 @@ def _run_both(p, x, monkeypatch, expect_pipe, **kw):
         call.run()
         torch.cuda.synchronize()
         first = _outputs(call, rows)
+        assert call.wait_status() == 0
         call.workspace.fill_(0xA5)   # garbage in the flags must not read as published
         call.run()
         torch.cuda.synchronize()
+        assert call.wait_status() == 0
         again = _outputs(call, rows)
         for n in first:
             assert np.array_equal(first[n], again[n]), (pipe, n)
@@ -110,29 +111,23 @@ CASES = [
 
 
 @pytest.mark.parametrize("name,lens,heads,opts,expect_pipe", CASES, ids=[c[0] for c in CASES])
-def test_pipeline_matches_separate_launches(name, lens, heads, opts, expect_pipe, monkeypatch):
-    from gated_deltanet_layer_02_amd import binding as B
+def test_pipeline_matches_separate_launches(name, lens, heads, opts, expect_pipe):
     p = _problem(f"pipe-{name}", lens, Hk=heads[0], Hv=heads[1], **opts)
     x = gs.generate(p)
     say(f"pipeline case {name}: lens {lens} Hk={p.Hk} Hv={p.Hv} {opts}")
-    res = _run_both(p, x, monkeypatch, expect_pipe)
+    res = _run_both(p, x, expect_pipe)
     _assert_same(res)
-    # and the oracle (all heads up to 8, else a sample of 4)
-    hv = (0, p.Hv) if p.Hv <= 8 else (p.Hv - 4, p.Hv)
-    r_out, r_fs, r_cs = oracle.run_problem(p, x, heads=hv)
-    out = io_to_f64(res[True][0]["out"])
-    e_out = rel_l2(out[:, hv[0]:hv[1]], r_out) if p.T > 0 else 0.0
-    e_fs = rel_l2(res[True][0]["final_state"][:, hv[0]:hv[1]], r_fs)
-    say(f"  rel_l2 out {e_out:.2e} state {e_fs:.2e}")
-    assert e_out <= TOL_BF16 and e_fs <= TOL_BF16
+    # and the oracle, every value head
+    r_out, r_fs, r_cs = oracle.run_problem(p, x)
+    rep_ = compare_heads(p, io_to_f64(res[True][0]["out"]), res[True][0]["final_state"], r_out, r_fs,
+                         TOL_BF16, chunk_check=p.gate)
+    say(f"  {rep_}")
     assert np.array_equal(res[True][0]["conv_state_out"], r_cs)
-    assert B.gdn_pipeline_timeouts() == 0
 
 
-def test_pipeline_pool_bf16_state_snapshots(monkeypatch):
+def test_pipeline_pool_bf16_state_snapshots():
     """State pool rows by slot, bf16 state storage and chunk snapshots through
     the pipelined launch (the same shape's plain call is pipelined)."""
-    from gated_deltanet_layer_02_amd import binding as B
     lens = [64 * 6 + 10, 64 * 4]
     p = _problem("pipe-pool", lens, Hk=2, Hv=4)
     x = gs.generate(p)
@@ -144,11 +139,10 @@ def test_pipeline_pool_bf16_state_snapshots(monkeypatch):
     counts = [(L - 1) // (64 * every) for L in lens]
     base = np.array([0, counts[0]], np.int32)
     say(f"pipeline pool case: lens {lens}, slots {slots.tolist()}, snapshots {counts}")
-    res = _run_both(p, x, monkeypatch, True, state_bf16=True, slots=slots, num_state_slots=rows,
+    res = _run_both(p, x, True, state_bf16=True, slots=slots, num_state_slots=rows,
                     snapshot_every=every, snapshot_base=base, num_snapshot_slots=sum(counts))
     _assert_same(res)
     # the same shape as a plain call takes the pipelined form
-    monkeypatch.setenv("GDN_PREFILL_PIPELINE", "1")
     from gated_deltanet_layer_02_amd.tensors import PrefillCall
     assert "prep_sweep" in _stages(PrefillCall(x | {"state": None, "conv_state": None}, Hk=p.Hk,
                                                Hv=p.Hv, io_bf16=True))
@@ -157,25 +151,22 @@ def test_pipeline_pool_bf16_state_snapshots(monkeypatch):
     out = io_to_f64(res[True][0]["out"])
     fs = gs.bf16_bits_to_f32(res[True][0]["final_state"]).astype(np.float64)   # slot rows
     assert rel_l2(out, r_out) <= TOL_BF16 and rel_l2(fs, r_fs) <= TOL_BF16
-    assert B.gdn_pipeline_timeouts() == 0
 
 
-def test_pipeline_c1_shape(monkeypatch):
+def test_pipeline_c1_shape():
     """The 4096-token, 16 key / 32 value head layer: pipelined and separate
     launches agree bit for bit."""
-    from gated_deltanet_layer_02_amd import binding as B
     p = gs.configs()["C1"]
     x = gs.generate(p)
     say("pipeline case C1 shape")
-    res = _run_both(p, x, monkeypatch, True)
+    res = _run_both(p, x, True)
     _assert_same(res)
-    assert B.gdn_pipeline_timeouts() == 0
 
 
 def _kept_units(call):
     """Prep units of the last (bf16) call whose fragments stayed in an XCD's L2:
     their ready flag is the call's epoch + 1.  Reads the flags where the
-    workspace keeps them: after the chunk offsets, KB (32 units of 1 KB per
+    workspace keeps them: after the call status words, the chunk offsets, KB (32 units of 1 KB per
     chunk slot and key head) and VB (40 per chunk slot and value head), each
     region rounded up to 256 bytes; chunk slots = T / 64 + N with cu_seqlens,
     ceil(T / 64) without.  The output flags that follow all hold the epoch."""
@@ -183,7 +174,8 @@ def _kept_units(call):
     w = call.workspace.view(torch.int64).cpu().numpy().view(np.uint64)
     C = call.T // 64 + call.N if call.cu is not None else -(-call.T // 64)
     r256 = lambda n: (n + 255) // 256 * 256
-    off = r256(4 * (call.N + 1)) + r256(C * call.Hk * 32 * 1024) + r256(C * call.Hv * 40 * 1024)
+    # the call status words (256 bytes), the chunk offsets, KB, VB
+    off = 256 + r256(4 * (call.N + 1)) + r256(C * call.Hk * 32 * 1024) + r256(C * call.Hv * 40 * 1024)
     ready = w[off // 8: off // 8 + C * call.Hk]
     off += r256(C * call.Hk * 8)
     published = -(-call.T // 64) * call.Hv * 8
@@ -193,23 +185,22 @@ def _kept_units(call):
     return int(np.count_nonzero(ready == epoch + np.uint64(1)))
 
 
-def test_pipeline_l2_hand_off_matches_write_through(monkeypatch):
+def test_pipeline_l2_hand_off_matches_write_through():
     """Prep fragments left in the L2 of the sweep's XCD and fragments written
-    through to memory (GDN_PIPE_L2=0) give the same bits, in either order on
-    one workspace (the flags of the other form's call are stale)."""
+    through to memory (GDN_FLAG_PREP_WRITE_BACK) give the same bits, in either
+    order on one workspace (the flags of the other form's call are stale)."""
     import torch
-    from gated_deltanet_layer_02_amd import binding as B
     from gated_deltanet_layer_02_amd.tensors import PrefillCall
     p = gs.configs()["C1"]
     x = gs.generate(p)
-    monkeypatch.setenv("GDN_PREFILL_PIPELINE", "1")
     call = PrefillCall(x, Hk=p.Hk, Hv=p.Hv, io_bf16=True)
     call.workspace.zero_()
     res, kept = [], []
-    for mode in ("1", "0", "1"):
-        monkeypatch.setenv("GDN_PIPE_L2", mode)
+    for write_back in (False, True, False):
+        call.set_launch(prep_write_back=write_back)
         call.run()
         torch.cuda.synchronize()
+        assert call.wait_status() == 0
         res.append(_outputs(call))
         kept.append(_kept_units(call))
     say(f"pipeline L2 hand-off, C1 shape: units kept in L2 per call {kept} of {p.T // 64 * p.Hk}")
@@ -217,28 +208,26 @@ def test_pipeline_l2_hand_off_matches_write_through(monkeypatch):
     for r in res[1:]:
         for n in res[0]:
             assert np.array_equal(res[0][n], r[n]), n
-    assert B.gdn_pipeline_timeouts() == 0
 
 
-def test_pipeline_write_back_fallback(monkeypatch):
+def test_pipeline_write_back_fallback():
     """Two key heads: prep units are dealt chunk-major over every XCD while the
     sweep of a key head sits on one, so most units find a reader elsewhere and
     write their L2 back before publishing; the result equals the all-write-back
     form bit for bit."""
     import torch
-    from gated_deltanet_layer_02_amd import binding as B
     from gated_deltanet_layer_02_amd.tensors import PrefillCall
     p = _problem("pipe-fallback", [64 * 20 + 11], Hk=2, Hv=4)
     x = gs.generate(p)
-    monkeypatch.setenv("GDN_PREFILL_PIPELINE", "1")
     call = PrefillCall(x, Hk=p.Hk, Hv=p.Hv, io_bf16=True)
     assert "prep_sweep" in _stages(call)
     res, kept = [], []
-    for mode in ("1", "0"):
-        monkeypatch.setenv("GDN_PIPE_L2", mode)
+    for write_back in (False, True):
+        call.set_launch(prep_write_back=write_back)
         call.workspace.zero_()
         call.run()
         torch.cuda.synchronize()
+        assert call.wait_status() == 0
         res.append(_outputs(call))
         kept.append(_kept_units(call))
     units = -(-p.T // 64) * p.Hk
@@ -246,4 +235,34 @@ def test_pipeline_write_back_fallback(monkeypatch):
     assert 0 < kept[0] < units and kept[1] == 0
     for n in res[0]:
         assert np.array_equal(res[0][n], res[1][n]), n
-    assert B.gdn_pipeline_timeouts() == 0
+
+
+def test_wait_failure_is_reported_per_call():
+    """A wait that gives up marks its call as failed in the workspace, and the
+    next call on the same workspace starts clean.  The failure is forced from
+    the host (GDN_FLAG_TEST_WAITS_GIVE_UP: every wait gives up at its first
+    check), so every kernel still ends normally."""
+    import torch
+    from gated_deltanet_layer_02_amd import binding as B
+    from gated_deltanet_layer_02_amd.tensors import PrefillCall
+    p = _problem("pipe-fail", [64 * 10 + 3], Hk=2, Hv=4)
+    x = gs.generate(p)
+    ref = PrefillCall(x, Hk=p.Hk, Hv=p.Hv, io_bf16=True, separate_launches=True)
+    ref.run()
+    torch.cuda.synchronize()
+    assert ref.wait_status() == 0
+    call = PrefillCall(x, Hk=p.Hk, Hv=p.Hv, io_bf16=True)
+    assert "prep_sweep" in _stages(call)
+    assert call.wait_status() == 0
+    say("pipeline: every wait gives up at once (forced), then a normal call")
+    call.desc.flags |= B.GDN_FLAG_TEST_WAITS_GIVE_UP
+    call.run()
+    torch.cuda.synchronize()
+    assert call.wait_status() == 1
+    call.desc.flags &= ~B.GDN_FLAG_TEST_WAITS_GIVE_UP
+    call.run()
+    torch.cuda.synchronize()
+    assert call.wait_status() == 0
+    a, b = _outputs(call), _outputs(ref)
+    for n in a:
+        assert np.array_equal(a[n], b[n]), n

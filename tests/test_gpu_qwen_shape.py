@@ -50,16 +50,15 @@ def test_in_place_poisoned_side_stream(T):
 
 
 @pytest.mark.parametrize("pipeline", [True, False])
-def test_profiled_brackets_every_kernel(pipeline, monkeypatch):
+def test_profiled_brackets_every_kernel(pipeline):
     import torch
-    monkeypatch.setenv("GDN_PREFILL_PIPELINE", "1" if pipeline else "0")
     from gated_deltanet_layer_02_amd.binding import STAGE_NAMES
     from gated_deltanet_layer_02_amd.tensors import PrefillCall
     T = 64 * 40
     p = _qwen_shape("qwen-profiled", T, seed=9)
     x = gs.generate(p)
     say(f"profiled call: T={T}")
-    call = PrefillCall(x, Hk=16, Hv=32, io_bf16=True)
+    call = PrefillCall(x, Hk=16, Hv=32, io_bf16=True, separate_launches=not pipeline)
     hip = ctypes.CDLL("libamdhip64.so.7")
     hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
     hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,

@@ -123,22 +123,27 @@ def test_snapshots(every, state_bf16):
     assert rel_l2(_state_f64(to_host(call.final_state)), r_fs) <= TOL_BF16
 
 
-def test_snapshots_c1_shape_sampled_heads():
+def test_snapshots_c1_shape_all_heads():
     from gated_deltanet_layer_02_amd.tensors import PrefillCall, to_host
     import torch
     p = gs.configs()["C1"]
     x = gs.generate(p)
     every = 16                                           # every 1024 tokens: 3 snapshots
-    say("C1 shape, snapshots every 16 chunks, heads 30-31")
+    say("C1 shape, snapshots every 16 chunks, every value head")
     call = PrefillCall(x, Hk=p.Hk, Hv=p.Hv, io_bf16=True, snapshot_every=every,
                        snapshot_base=np.array([0], np.int32), num_snapshot_slots=3)
     call.run()
     torch.cuda.synchronize()
+    assert call.wait_status() == 0
     snaps = to_host(call.snapshots)
+    assert np.all(np.isfinite(snaps))
     zero_state = np.zeros((p.Hv, 128, 128), np.float32)
     zero_conv = np.zeros((3, p.Cch), np.uint16)
     for j in range(1, 4):
-        _, r_fs, _ = _oracle_seq(p, x, 0, 1024 * j, zero_state, zero_conv, heads=(30, 32))
-        e = rel_l2(snaps[j - 1][30:32].astype(np.float64), r_fs[0])
-        say(f"  snapshot {j}: rel_l2 {e:.2e}")
-        assert e <= TOL_BF16
+        _, r_fs, _ = _oracle_seq(p, x, 0, 1024 * j, zero_state, zero_conv, heads=(0, p.Hv))
+        got = snaps[j - 1].astype(np.float64)
+        e = rel_l2(got, r_fs[0])
+        per_head = [rel_l2(got[h], r_fs[0][h]) for h in range(p.Hv)]
+        worst = int(np.argmax(per_head))
+        say(f"  snapshot {j}: rel_l2 {e:.2e}, worst head {worst}: {per_head[worst]:.2e}")
+        assert e <= TOL_BF16 and max(per_head) <= TOL_BF16
