@@ -514,6 +514,40 @@ def cpu_baseline(pres, target_s: float):
             "host_cpu": cpu, "host_logical_cpus": os.cpu_count()}
 
 
+def calibrate_mfma(blocks: int = 1024, iters: int = 256):
+    """The MFMA loops of libgdn_calib.so (counter calibration): blocks x 4 waves
+    x iters x 8 MFMA instructions of each kind, 16x16x32 bf16 (16,384 flop)
+    then 16x16x16 bf16 (8,192 flop)."""
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "gated_deltanet_layer_02_amd", "libgdn_calib.so"))
+    lib.gdn_calib_mfma.restype = ctypes.c_int
+    lib.gdn_calib_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                   ctypes.c_void_p]
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    for kind in (0, 1):
+        assert lib.gdn_calib_mfma(kind, blocks, iters, out.data_ptr(), stream) == 0
+        torch.cuda.synchronize()
+        n = blocks * 4 * iters * 8
+        log(f"[bench] calibration MFMA loop kind {kind}: {n} instructions, "
+            f"{n * (16384 if kind == 0 else 8192)} flop")
+
+
+def run_only(args, hip, name):
+    """One configuration's prefill alone (for counter runs): warmup + steps
+    calls on one buffer set, the median printed as a JSON line."""
+    import gdn_synth as gs
+    from gated_deltanet_layer_02_amd.tensors import PrefillCall
+    p = gs.configs()[name]
+    log(f"[bench] only {name}: {p.N} sequence(s), {p.T} tokens")
+    x = gs.generate(p)
+    call = PrefillCall(x, Hk=p.Hk, Hv=p.Hv, io_bf16=p.io == gs.BF16, l2norm=p.l2norm, scale=p.scale,
+                       l2_eps=p.l2_eps, norm_eps=p.norm_eps)
+    ts = time_each(hip, [call.run], args.steps, args.warmup)
+    print(json.dumps({"config": name, "tokens": p.T, "launch": launch_form(hip, call),
+                      "calls": args.steps, "us_median": round(ts[len(ts) // 2] * 1e6, 2)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -529,6 +563,10 @@ def main():
                     help="skip the per-configuration prefill timings (C0-C3) and reference peaks")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a 512 MiB device-to-device copy first (counter calibration)")
+    ap.add_argument("--calibrate-mfma", action="store_true",
+                    help="run the MFMA loops of libgdn_calib.so first (counter calibration)")
+    ap.add_argument("--only", choices=["C0", "C1", "C2", "C3"],
+                    help="time one prefill configuration alone (counter runs) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -548,6 +586,11 @@ def main():
         torch.cuda.synchronize()
         log("[bench] calibration copy: 3 x 512 MiB device-to-device")
         del src, dst
+    if args.calibrate_mfma:
+        calibrate_mfma()
+    if args.only:
+        run_only(args, hip, args.only)
+        return
 
     pres = bench_prefill(args, hip)
     dec = None

@@ -11,6 +11,10 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgdn.so")
 SOURCES = ["gdn_api.cpp", "gdn_prefill.hip", "gdn_decode.hip", "gdn_verify.hip"]
+# counter calibration kernels (an MFMA loop of known instruction count): a
+# library of their own, used by the benchmark's profiling runs only
+CALIB_LIB = os.path.join(PKG, "libgdn_calib.so")
+CALIB_SOURCES = ["gdn_calib.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -33,19 +37,26 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libgdn.so (always rebuilds)."""
-    os.makedirs(BUILD, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str):
+    tmp = lib + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link libgdn.so and libgdn_calib.so (always
+    rebuilds)."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + CALIB_SOURCES
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], CALIB_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {CALIB_LIB}")
     return LIB
 
 
