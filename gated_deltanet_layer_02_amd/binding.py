@@ -30,7 +30,8 @@ STATUS_NAMES = {0: "GDN_OK", 1: "GDN_ERR_NULL_ARG", 2: "GDN_ERR_BAD_SHAPE",
 
 EXPORTED = ["gdn_status_string", "gdn_prefill_workspace_size", "gdn_prefill",
             "gdn_prefill_profiled", "gdn_prefill_ex", "gdn_decode", "gdn_decode_verify",
-            "gdn_decode_commit", "gdn_prefill_wait_status"]
+            "gdn_decode_commit", "gdn_prefill_wait_status", "gdn_prefill_static"]
+STATIC_SCRATCH_BYTES = 128 << 20   # GDN_STATIC_SCRATCH_BYTES
 
 
 class GdnError(RuntimeError):
@@ -111,6 +112,8 @@ def lib():
         l.gdn_prefill_profiled.argtypes = [dp] + [vp] * 14 + [vp, sz, vp, vp, i32, vp, vp]
         l.gdn_prefill_ex.restype = ctypes.c_int
         l.gdn_prefill_ex.argtypes = [dp, ctypes.POINTER(PrefillArgs), vp]
+        l.gdn_prefill_static.restype = ctypes.c_int
+        l.gdn_prefill_static.argtypes = [dp, ctypes.POINTER(PrefillArgs), vp]
         l.gdn_decode_verify.restype = ctypes.c_int
         l.gdn_decode_verify.argtypes = [dp, i32] + [vp] * 11 + [i32, vp, vp, vp, vp]
         l.gdn_decode_commit.restype = ctypes.c_int
@@ -210,6 +213,26 @@ def gdn_prefill_ex(desc: Desc, q, k, v, g, beta, *, z=None, conv_w=None, norm_w=
     rc = lib().gdn_prefill_ex(ctypes.byref(desc), ctypes.byref(a), _stream(stream))
     if check and rc != GDN_OK:
         raise GdnError(rc, "gdn_prefill_ex")
+    return rc
+
+
+def gdn_prefill_static(desc: Desc, q, k, v, g, beta, *, z=None, conv_w=None, norm_w=None,
+                       cu_seqlens=None, initial_state=None, final_state=None, conv_state_in=None,
+                       conv_state_out=None, state_slots=None, num_state_slots: int = 0,
+                       state_snapshots=None, snapshot_base=None, snapshot_every: int = 0,
+                       num_snapshot_slots: int = 0, out=None, stream=None, check: bool = True) -> int:
+    """gdn_prefill_static: gdn_prefill_ex's arguments without a workspace."""
+    a = PrefillArgs(q=_p(q), k=_p(k), v=_p(v), g=_p(g), beta=_p(beta), z=_p(z),
+                    conv_w=_p(conv_w), norm_w=_p(norm_w), cu_seqlens=_p(cu_seqlens),
+                    initial_state=_p(initial_state), final_state=_p(final_state),
+                    conv_state_in=_p(conv_state_in), conv_state_out=_p(conv_state_out),
+                    state_slots=_p(state_slots), num_state_slots=int(num_state_slots),
+                    state_snapshots=_p(state_snapshots), snapshot_base=_p(snapshot_base),
+                    snapshot_every=int(snapshot_every), num_snapshot_slots=int(num_snapshot_slots),
+                    out=_p(out), workspace=None, workspace_bytes=0)
+    rc = lib().gdn_prefill_static(ctypes.byref(desc), ctypes.byref(a), _stream(stream))
+    if check and rc != GDN_OK:
+        raise GdnError(rc, "gdn_prefill_static")
     return rc
 
 

@@ -292,6 +292,23 @@ gdn_status gdn_prefill_ex(const gdn_desc* d, const gdn_prefill_args* args, hipSt
     return prefill_impl(d, *args, stream, nullptr, 0, nullptr, nullptr);
 }
 
+gdn_status gdn_prefill_static(const gdn_desc* d, const gdn_prefill_args* args, hipStream_t stream) {
+    if (args == nullptr) return GDN_ERR_NULL_ARG;
+    if (args->workspace != nullptr || args->workspace_bytes != 0) return GDN_ERR_BAD_VALUE;
+    const gdn_status st = check_desc_common(d);
+    if (st != GDN_OK) return st;
+    gdn_desc ds = *d;
+    ds.flags |= GDN_FLAG_SEPARATE_LAUNCHES;
+    // the bound gdn_prefill_workspace_size states, checked before any HIP call
+    if (prefill_layout(&ds, true).total > gdn::kStaticScratchBytes) return GDN_ERR_WORKSPACE;
+    void* scratch = nullptr;
+    if (gdn::static_scratch(&scratch) != hipSuccess) return GDN_ERR_HIP;
+    gdn_prefill_args x = *args;
+    x.workspace = scratch;
+    x.workspace_bytes = gdn::kStaticScratchBytes;
+    return prefill_impl(&ds, x, stream, nullptr, 0, nullptr, nullptr);
+}
+
 gdn_status gdn_decode(const gdn_desc* d, const void* q, const void* k, const void* v,
                       const float* g, const float* beta, const void* z, const void* conv_w,
                       const void* norm_w, void* state, void* conv_state,

@@ -175,6 +175,10 @@ struct KernelRecorder {
 };
 
 hipError_t launch_prefill(const PrefillPlan& p, hipStream_t stream, KernelRecorder& rec);
+// Device address of the current device's static scratch (GDN_STATIC_SCRATCH_BYTES),
+// looked up once per device.
+constexpr size_t kStaticScratchBytes = GDN_STATIC_SCRATCH_BYTES;
+hipError_t static_scratch(void** ptr);
 hipError_t launch_decode(const DecodeArgs& a, bool io_bf16, bool state_bf16, bool conv,
                          hipStream_t stream);
 hipError_t launch_verify(const VerifyArgs& a, bool io_bf16, bool state_bf16, bool conv, hipStream_t s);

@@ -1764,6 +1764,32 @@ static hipError_t run_serial(const PrefillPlan& p, bool pipe, hipStream_t s, Ker
     return hipSuccess;
 }
 
+// ---------------------------------------------------------------------------
+// static scratch of gdn_prefill_static: the workspace of callers that cannot
+// allocate.  The host never uses the array's name as an address: per device,
+// with that device current, hipGetSymbolAddress gives that device's copy,
+// which is cached and passed to the kernels like any workspace.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+constexpr int kMaxDevices = 64;
+
+hipError_t static_scratch(void** out) {
+    static std::atomic<void*> cache[kMaxDevices];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    void* p = cache[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        cache[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return hipSuccess;
+}
+
 hipError_t launch_prefill(const PrefillPlan& p, hipStream_t stream, KernelRecorder& rec) {
     const bool pipe = use_pipe(p);
     const int n = (p.prep.cu != nullptr) +

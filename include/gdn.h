@@ -263,6 +263,29 @@ typedef struct {
 gdn_status gdn_prefill_ex(const gdn_desc* d, const gdn_prefill_args* args, hipStream_t stream);
 
 /*
+ * Prefill without a workspace and without any allocation, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Arguments as gdn_prefill_ex, except:
+ *  - args->workspace must be NULL and args->workspace_bytes 0
+ *    (GDN_ERR_BAD_VALUE otherwise).  The scratch is a static device array of
+ *    GDN_STATIC_SCRATCH_BYTES inside the library, one per GPU, held from the
+ *    library's loading on that GPU until the process ends.
+ *  - A call whose workspace (gdn_prefill_workspace_size of d) exceeds
+ *    GDN_STATIC_SCRATCH_BYTES fails with GDN_ERR_WORKSPACE before anything
+ *    runs.  At 16 key / 32 value heads with bf16 io that is T_total / 64 + N
+ *    <= 73 chunk slots: up to 4,671 tokens in one sequence.
+ *  - The separate launches always run (GDN_FLAG_SEPARATE_LAUNCHES is implied):
+ *    no kernel waits on another, so there is no failure to query.
+ *  - Every call on one GPU uses that GPU's one array, which keeps the last
+ *    call's contents (no call depends on them): calls that overlap in time on
+ *    one GPU (unordered streams, several threads) race and give undefined
+ *    results.  Calls in one stream's order do not overlap.
+ * The library calls no hipMalloc, hipFree or allocating routine here.
+ */
+#define GDN_STATIC_SCRATCH_BYTES ((size_t)128 << 20)
+gdn_status gdn_prefill_static(const gdn_desc* d, const gdn_prefill_args* args, hipStream_t stream);
+
+/*
  * Decode: one new token for each of N sequences against cached states.
  *   q, k           [N, Hk, dk] io dtype, raw
  *   v, z           [N, Hv, dv] io dtype (z NULL together with norm_w: out = o)

@@ -78,6 +78,16 @@ hipError_t launch_prefill(const PrefillPlan& p, hipStream_t, KernelRecorder&) {
 hipError_t launch_decode(const DecodeArgs&, bool, bool, bool, hipStream_t) { ++g_decodes; return hipSuccess; }
 hipError_t launch_verify(const VerifyArgs&, bool, bool, bool, hipStream_t) { ++g_verifies; return hipSuccess; }
 hipError_t launch_commit(const CommitArgs&, bool, bool, hipStream_t) { ++g_commits; return hipSuccess; }
+static void* g_scratch = nullptr;   // host stand-in for the static device scratch
+static int g_scratch_lookups = 0;
+hipError_t static_scratch(void** p) {
+    ++g_scratch_lookups;
+    if (g_scratch == nullptr) g_scratch = aligned_alloc(256, kStaticScratchBytes);
+    *p = g_scratch;
+    g_ws = (char*)g_scratch;
+    g_ws_bytes = kStaticScratchBytes;
+    return hipSuccess;
+}
 }  // namespace gdn
 
 extern "C" hipError_t hipStreamSynchronize(hipStream_t) { return hipSuccess; }
@@ -234,6 +244,33 @@ int main() {
         CHECK(gdn_prefill_wait_status(ws.p, 255, nullptr, &f) == GDN_ERR_WORKSPACE);
         CHECK(gdn_prefill_wait_status((char*)ws.p + 16, 1024, nullptr, &f) == GDN_ERR_MISALIGNED);
         CHECK(gdn_prefill_wait_status(ws.p, ws.n, nullptr, nullptr) == GDN_ERR_NULL_ARG);
+    }
+    // the static-scratch prefill: no workspace accepted, too-large calls refused
+    // before the scratch is even looked up, the others run the separate launches
+    {
+        const int64_t T = 4096;
+        const gdn_desc d = desc(1, T, 16, 32, GDN_BF16, GDN_F32, GDN_FLAG_L2NORM_QK);
+        Buf q(T * 16 * 256), v(T * 32 * 256), g(T * 32 * 4), z(T * 32 * 256), out(T * 32 * 256);
+        Buf fs(32 * 128 * 128 * 4), nw(256), cw(64 * 128 * 8);
+        gdn_prefill_args a{};
+        a.q = q.p; a.k = q.p; a.v = v.p; a.g = (const float*)g.p; a.beta = (const float*)g.p;
+        a.z = z.p; a.norm_w = nw.p; a.conv_w = cw.p; a.out = out.p; a.final_state = fs.p;
+        a.workspace = q.p;
+        CHECK(gdn_prefill_static(&d, &a, nullptr) == GDN_ERR_BAD_VALUE);
+        a.workspace = nullptr;
+        a.workspace_bytes = 16;
+        CHECK(gdn_prefill_static(&d, &a, nullptr) == GDN_ERR_BAD_VALUE);
+        a.workspace_bytes = 0;
+        CHECK(gdn_prefill_static(&d, nullptr, nullptr) == GDN_ERR_NULL_ARG);
+        const gdn_desc big = desc(1, 64 * 73, 16, 32, GDN_BF16, GDN_F32, GDN_FLAG_L2NORM_QK);
+        size_t need = 0;
+        CHECK(gdn_prefill_workspace_size(&big, &need) == GDN_OK && need > GDN_STATIC_SCRATCH_BYTES);
+        CHECK(gdn_prefill_static(&big, &a, nullptr) == GDN_ERR_WORKSPACE);
+        CHECK(gdn::g_scratch_lookups == 0);
+        const int before = g_prefills;
+        CHECK(gdn_prefill_static(&d, &a, nullptr) == GDN_OK);
+        CHECK(g_prefills == before + 1 && !g_last_pipe_allowed && gdn::g_scratch_lookups == 1);
+        free(gdn::g_scratch);
     }
     for (int s = 0; s <= 10; ++s) CHECK(gdn_status_string((gdn_status)s) != nullptr);
     if (failures) {

@@ -127,6 +127,26 @@ def test_wait_status_validation():
     assert f.value == -1
 
 
+def test_static_prefill_refusals():
+    """gdn_prefill_static refuses a workspace argument and calls whose
+    workspace would exceed its static scratch, before any HIP call."""
+    lib = gdn.lib()
+    p = _ptrs(20)
+    a = B.PrefillArgs(q=p[0], k=p[1], v=p[2], g=p[3], beta=p[4], out=p[5], final_state=p[6],
+                      workspace=p[7], workspace_bytes=1 << 20)
+    d = B.make_desc(1, 4096)
+    assert lib.gdn_prefill_static(ctypes.byref(d), ctypes.byref(a), None) == 9          # workspace given
+    a.workspace, a.workspace_bytes = None, 0
+    assert lib.gdn_prefill_static(ctypes.byref(d), None, None) == 1
+    # the limit: T_total / 64 + N chunk slots within GDN_STATIC_SCRATCH_BYTES
+    big = B.make_desc(1, 64 * 73)
+    assert gdn.gdn_prefill_workspace_size(big) > B.STATIC_SCRATCH_BYTES
+    assert gdn.gdn_prefill_workspace_size(B.make_desc(1, 4671)) <= B.STATIC_SCRATCH_BYTES
+    assert lib.gdn_prefill_static(ctypes.byref(big), ctypes.byref(a), None) == 6
+    bad = B.make_desc(1, 4096, head_dim=64)
+    assert lib.gdn_prefill_static(ctypes.byref(bad), ctypes.byref(a), None) == 3
+
+
 def test_prefill_profiled_needs_events():
     d = B.make_desc(1, 10)
     lib = gdn.lib()
