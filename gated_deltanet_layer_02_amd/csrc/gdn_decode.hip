@@ -201,13 +201,24 @@ __global__ __launch_bounds__(256) void gdn_decode_kernel(DecodeArgs a) {
     }
 }
 
+// Workgroups resident per CU.  With an fp32 state each workgroup streams
+// 64 KB per value head; the registers allow four per CU (64 MB of state rows
+// in flight on 256 CUs), which ran slower than two (C4, 256 sequences: 198-200
+// us at four or three, 192-193 us at two, 223 us at one), so the launch
+// reserves dynamic LDS that lets only two fit in a CU's 160 KB (60 KB each
+// beside the kernel's 2.5 KB of static LDS).  A bf16 state moves half the
+// bytes per workgroup and is fastest at the four the registers allow (106 us;
+// 129 us at two, 205 us at one).
+template <class ST> constexpr unsigned decode_lds_pad() { return sizeof(ST) == 4 ? 60u * 1024u : 0u; }
+
 template <class IO, class ST>
 static hipError_t launch_typed(const DecodeArgs& a, bool conv, hipStream_t stream) {
     const dim3 grid(a.N * a.Hk);
+    constexpr unsigned pad = decode_lds_pad<ST>();
     if (conv)
-        hipLaunchKernelGGL((gdn_decode_kernel<IO, ST, true>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((gdn_decode_kernel<IO, ST, true>), grid, dim3(256), pad, stream, a);
     else
-        hipLaunchKernelGGL((gdn_decode_kernel<IO, ST, false>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((gdn_decode_kernel<IO, ST, false>), grid, dim3(256), pad, stream, a);
     return hipGetLastError();
 }
 

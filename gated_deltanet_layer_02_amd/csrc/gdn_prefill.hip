@@ -744,6 +744,7 @@ typedef __attribute__((address_space(3))) uint16_t lds_u16;
 typedef __attribute__((address_space(3))) u16x4 lds_u16x4;
 typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
 typedef __attribute__((address_space(3))) float lds_f32;
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
 // XCD-aware mapping of blockIdx.x to (unit u = n*Hv + h, group sg).
 // Workgroups are dealt to the 8 XCDs round-robin (XCD = x % 8), each XCD
@@ -1245,16 +1246,31 @@ __global__ __launch_bounds__(64 * (SW + PW)) void gdn_state_sweep_lds_kernel(Swe
     sweep_wg<SW, NT, PW, false>(a, blockIdx.x, gdn_sweep_smem, PipeSync{});
 }
 
-// fp32 operands: the same sweep with operands read straight from memory
-// (fp32 fragments are 2 KB; this path serves fp32 inputs, not the bf16 layer).
-__global__ __launch_bounds__(64) void gdn_state_sweep_f32_kernel(SweepArgs a) {
+// fp32 operands (the fp32 layer): the chunk's fragments (2 KB units: 8 fp32
+// per lane) are staged in LDS and shared by kF32SW waves, one 16-row slice of
+// the value head each.  Every wave of the workgroup copies its share of the
+// 64 units with 16-byte DMA, one wait and barrier later every wave runs the
+// chunk from LDS.  (Read straight from memory inside the chunk step, each
+// fragment's load latency was exposed on the chain: about 20 us per chunk.)
+// LDS units: KB units 0..31 (Q, K^T), VB units 0..23 (W, P, gates) at 32..55,
+// the U~ units of the workgroup's slices at 56..63.
+constexpr int kF32SW = 4;
+constexpr int kF32Units = kKBUnits + kVB_U + 2 * kF32SW;
+constexpr unsigned kF32Lds = kF32Units * 2048u;
+static_assert(kF32Lds <= 160 * 1024, "one chunk of fp32 fragments fits a CU's LDS");
+
+__global__ __launch_bounds__(64 * kF32SW) void gdn_state_sweep_f32_kernel(SweepArgs a) {
     typedef Frag<float> F;
+    extern __shared__ __attribute__((aligned(16))) unsigned char gdn_f32_smem[];
+    lds_b16x8* buf = (lds_b16x8*)gdn_f32_smem;   // 16-byte elements: unit i at buf + 128 i
+    const lds_u8* lb = (const lds_u8*)gdn_f32_smem;
     mark_call(a, blockIdx.x);
     int u, sg;
-    if (!sweep_unit(blockIdx.x, 8, a.N, a.Hk, a.Hv, u, sg)) return;
+    if (!sweep_unit(blockIdx.x, 8 / kF32SW, a.N, a.Hk, a.Hv, u, sg)) return;
     const int n = u / a.Hv, h = u % a.Hv, hk = h / (a.Hv / a.Hk);
-    const int lane = threadIdx.x, l16 = lane & 15, g4 = lane >> 4;
-    const int s = sg;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, l16 = lane & 15, g4 = lane >> 4;
+    const int s = sg * kF32SW + wave;   // this wave's 16-row slice
     const SweepSeq q = sweep_seq(a, n);
 
     f32x4 S[1][8];
@@ -1264,27 +1280,52 @@ __global__ __launch_bounds__(64) void gdn_state_sweep_f32_kernel(SweepArgs a) {
     for (int m = 0; m < 8; ++m)
         S[0][m] = a.initial_state != nullptr ? state_load4(a.initial_state, a.state_bf16, srow + 16 * m + 4 * g4)
                                              : f32x4{0.f, 0.f, 0.f, 0.f};
+    // a fragment of LDS unit i: this lane's 8 fp32 (32 bytes)
+    auto frag = [&](int i) {
+        const lds_f32x4* p = reinterpret_cast<const lds_f32x4*>(lb + i * 2048 + lane * 32);
+        const f32x4 x = p[0], y = p[1];
+        F f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { f.v[e] = x[e]; f.v[4 + e] = y[e]; }
+        return f;
+    };
+    const lds_f32* G = reinterpret_cast<const lds_f32*>(lb + (kKBUnits + kVB_G) * 2048);
 #pragma unroll 1
     for (int j = 0; j < q.nch; ++j) {
         const size_t c = (size_t)q.c_begin + j;
-        const F* KB = static_cast<const F*>(a.KB) + (c * a.Hk + hk) * kKBUnits * 64 + lane;
-        const F* VB = static_cast<const F*>(a.VB) + (c * a.Hv + h) * kVBUnits * 64 + lane;
-        const float* Uf = reinterpret_cast<const float*>(VB + (kVB_U + 2 * s) * 64);
-        const float* G = reinterpret_cast<const float*>(VB - lane + kVB_G * 64);
+        {   // copy the chunk's 64 units (128 pieces of 1 KB) into LDS
+            const char* kb = static_cast<const char*>(a.KB) + (c * a.Hk + hk) * kKBUnits * 2048;
+            const char* vb = static_cast<const char*>(a.VB) + (c * a.Hv + h) * kVBUnits * 2048;
+            const char* ub = vb + (kVB_U + 2 * kF32SW * sg) * 2048;
+            for (int i = wave; i < 2 * kF32Units; i += kF32SW) {
+                const int unit = i >> 1;
+                const char* src = unit < kKBUnits ? kb + unit * 2048
+                                : unit < kKBUnits + kVB_U ? vb + (unit - kKBUnits) * 2048
+                                                          : ub + (unit - kKBUnits - kVB_U) * 2048;
+                __builtin_amdgcn_global_load_lds(src + (i & 1) * 1024 + lane * 16, buf + i * 64, 16, 0, 0);
+            }
+            __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0)
+            __syncthreads();
+        }
+        const int ubase = kKBUnits + kVB_U + 2 * wave;   // this slice's U~ units
         f32x4 O[1][4];
         sweep_chunk<float, 1>(
-            S, O, [&](int f) { return frag_load(VB + (kVB_W + f) * 64); },
-            [&](int f) { return frag_load(KB + (kKB_Q + f) * 64); },
-            [&](int f) { return frag_load(KB + (kKB_KT + f) * 64); },
-            [&](int f) { return frag_load(VB + (kVB_P + f) * 64); },
-            [&](int, int mt) { return *reinterpret_cast<const f32x4*>(Uf + (mt >> 1) * 64 * 8 + (mt & 1) * 4); },
+            S, O, [&](int f) { return frag(kKBUnits + kVB_W + f); },
+            [&](int f) { return frag(kKB_Q + f); },
+            [&](int f) { return frag(kKB_KT + f); },
+            [&](int f) { return frag(kKBUnits + kVB_P + f); },
+            [&](int, int mt) {   // U~: unit (2 s + mt / 2), this lane's 4 of the token-tile pair
+                return *reinterpret_cast<const lds_f32x4*>(lb + (ubase + (mt >> 1)) * 2048 + lane * 32 +
+                                                           (mt & 1) * 16);
+            },
             [&](int i) {
-                return *reinterpret_cast<const f32x4*>(G + (i >> 2) * 64 + 16 * (i & 3) + 4 * g4);
+                return *reinterpret_cast<const lds_f32x4*>(G + (i >> 2) * 64 + 16 * (i & 3) + 4 * g4);
             },
             G[63]);
-        store_o(static_cast<float*>(a.out), O[0], q.seq_start + j * kChunk,
-                min(kChunk, q.L - j * kChunk), a.Hv, h, s, l16, g4);
+        store_o(static_cast<float*>(a.out), O[0], q.seq_start + j * kChunk, min(kChunk, q.L - j * kChunk), a.Hv, h,
+                s, l16, g4);
         state_snapshot<1>(a, n, j, q.nch, h, s, S, l16, g4);
+        __syncthreads();   // every wave is done with the LDS copy before the next one
     }
     if (a.final_state != nullptr) state_put<1>(a.final_state, a, row, h, s, S, l16, g4);
 }
@@ -1572,9 +1613,12 @@ static hipError_t allow_dynamic_lds(const void* kern, unsigned bytes) {
     static const hipError_t pipe_noconv = hipFuncSetAttribute(
         reinterpret_cast<const void*>(gdn_prefill_pipe_kernel<false>),
         hipFuncAttributeMaxDynamicSharedMemorySize, kPipeSmem);
+    static const hipError_t sweep_f32 = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(gdn_state_sweep_f32_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+        kF32Lds);
     (void)kern;
     (void)bytes;
-    for (hipError_t e : {bf16_conv, bf16_noconv, f32_conv, f32_noconv, sweep, pipe_conv, pipe_noconv})
+    for (hipError_t e : {bf16_conv, bf16_noconv, f32_conv, f32_noconv, sweep, pipe_conv, pipe_noconv, sweep_f32})
         if (e != hipSuccess) return e;
     return hipSuccess;
 }
@@ -1601,13 +1645,15 @@ static hipError_t launch_prep(const PrefillPlan& p, int slots, hipStream_t s) {
 
 static int sweep_blocks(const PrefillPlan& p) {
     const SweepArgs& a = p.sweep;
-    return sweep_grid(p.io_bf16 ? SweepCfg::kGroups : 8, a.N, a.Hk, a.Hv);
+    return sweep_grid(p.io_bf16 ? SweepCfg::kGroups : 8 / kF32SW, a.N, a.Hk, a.Hv);
 }
 
 static hipError_t launch_sweep(const PrefillPlan& p, hipStream_t s) {
     const SweepArgs& a = p.sweep;
     if (!p.io_bf16) {
-        hipLaunchKernelGGL(gdn_state_sweep_f32_kernel, dim3(sweep_blocks(p)), dim3(64), 0, s, a);
+        hipError_t e = allow_dynamic_lds(nullptr, 0);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(gdn_state_sweep_f32_kernel, dim3(sweep_blocks(p)), dim3(64 * kF32SW), kF32Lds, s, a);
     } else {
         hipError_t e = allow_dynamic_lds(nullptr, 0);
         if (e != hipSuccess) return e;
