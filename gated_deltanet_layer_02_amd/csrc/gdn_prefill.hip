@@ -101,6 +101,9 @@ __device__ __forceinline__ bool locate_chunk(const PrepArgs& a, int c, int& n, i
 // conflict-free.  Element offset of token group `g` in row `row`:
 __device__ __forceinline__ int tsw(int row, int g) { return 4 * (g ^ ((row >> 3) & 15)); }
 
+// Both layouts below offer the same accessors: q / k rows, K^T / V^T rows,
+// and A[t][i] (i < t, the ten lower 16x16 blocks) and the diagonal 16x16 blocks
+// of T, in fp32.
 template <class MT>
 struct PrepSmem {
     static constexpr int kRowPad = sizeof(MT) == 2 ? 16 : 8;   // elements
@@ -119,7 +122,50 @@ struct PrepSmem {
     float G[kChunk];                       // inclusive cumsum of g
     float b[kChunk];                       // beta
     float bg[kChunk];                      // beta * exp(G)
+    __device__ __forceinline__ MT* qrow(int t) { return qa.q[t]; }
+    __device__ __forceinline__ MT* krow(int t) { return ka.k[t]; }
+    __device__ __forceinline__ MT* ktrow(int d) { return kt[d]; }
+    __device__ __forceinline__ MT* vtrow(int d) { return vt[d]; }
+    __device__ __forceinline__ float* A(int t, int i) { return &ka.a[t][i]; }
+    __device__ __forceinline__ float* T(int t, int i) { return &qa.t[t][i]; }
 };
+
+// The bf16 layout that lets three units share a CU (at most a third of its
+// 160 KB): q rows share their space with V^T (q is dead once the K Q^T cells
+// and Q fragments are formed, V^T is written after), and k rows with A and T,
+// of which only the ten lower 16x16 blocks of A and the four diagonal blocks
+// of T are kept (rows padded to 20 floats so that the 16-row reads spread
+// over the banks).
+struct PrepSmemLean {
+    static constexpr int kRowLd = kD + 8;          // bf16 row stride of q, k rows
+    static constexpr int kColLd = kChunk + 4;      // bf16 row stride of K^T, V^T
+    static constexpr int kBlkLd = 20;              // fp32 row stride of a 16x16 block
+    union QV {
+        bf16 q[kChunk][kRowLd];
+        bf16 vt[kD][kColLd];
+    } qv;
+    union KAT {
+        bf16 k[kChunk][kRowLd];
+        struct {
+            float a[10][16][kBlkLd];   // A block (R, M), M <= R, at R (R + 1) / 2 + M
+            float t[4][16][kBlkLd];    // diagonal block R of T
+        } at;
+    } kat;
+    bf16 kt[kD][kColLd];
+    float G[kChunk];
+    float b[kChunk];
+    float bg[kChunk];
+    __device__ __forceinline__ bf16* qrow(int t) { return qv.q[t]; }
+    __device__ __forceinline__ bf16* krow(int t) { return kat.k[t]; }
+    __device__ __forceinline__ bf16* ktrow(int d) { return kt[d]; }
+    __device__ __forceinline__ bf16* vtrow(int d) { return qv.vt[d]; }
+    __device__ __forceinline__ float* A(int t, int i) {
+        const int R = t >> 4, M = i >> 4;
+        return &kat.at.a[R * (R + 1) / 2 + M][t & 15][i & 15];
+    }
+    __device__ __forceinline__ float* T(int t, int i) { return &kat.at.t[t >> 4][t & 15][i & 15]; }
+};
+static_assert(3 * sizeof(PrepSmemLean) <= 160 * 1024, "three lean units fit a CU's LDS");
 
 // Raw rows of 8 channels for 4 consecutive tokens and the 3 before them.
 // src is [T][heads][128]; col = head * 128 + 8 cg; chan = the conv channel
@@ -359,15 +405,19 @@ template <> struct PrepStore<true> {
 // (kCo, ps), `local` (valid in wave 0) tells whether every sweep workgroup of
 // the unit's key unit recorded this XCD in ps->xcc (read after phase 1, when
 // the sweep workgroups, dispatched first, have long recorded theirs).
-template <class IO, bool kConv, bool kCo = false>
+// kLean (bf16 only): the PrepSmemLean layout, no register prefetch of the
+// next value head's v rows, and the K K^T / K Q^T cells formed from fragments
+// read when each cell needs them, so that the unit fits 168 VGPRs and three
+// units share a CU.
+template <class IO, bool kConv, bool kCo = false, bool kLean = false>
 __device__ __forceinline__ bool prep_unit(const PrepArgs& a, int c, int hk, unsigned char* smem, int tid,
                                           const PipeSync* ps = nullptr, bool* local = nullptr) {
     typedef typename MathOf<IO>::T MT;
     typedef Frag<MT> F;
-    typedef PrepSmem<MT> Smem;
+    static_assert(!kLean || sizeof(MT) == 2, "the lean layout is for bf16 operands");
+    typedef std::conditional_t<kLean, PrepSmemLean, PrepSmem<MT>> Smem;
     typedef PrepStore<kCo> St;
     Smem& sm = *reinterpret_cast<Smem*>(smem);
-    constexpr int LD = Smem::kLdA;
 
     int n, t0, len, seq_start;
     if (!locate_chunk(a, c, n, t0, len, seq_start)) return false;
@@ -390,7 +440,7 @@ __device__ __forceinline__ bool prep_unit(const PrepArgs& a, int c, int hk, unsi
     const int h0 = hk * group;
     // v rows are prefetched one phase early on interior chunks (bf16 rows:
     // the fp32 layer keeps its registers for the math instead)
-    const bool inner = sizeof(IO) == 2 && t0 - 3 >= seq_start && len == kChunk;   // uniform
+    const bool inner = !kLean && sizeof(IO) == 2 && t0 - 3 >= seq_start && len == kChunk;   // uniform
     Quad<IO, kConv> xv;        // raw v rows of the next value head
     float gl = 0.f, bl = 0.f;  // its g and beta (wave 0, lane = token)
     {
@@ -428,17 +478,17 @@ __device__ __forceinline__ bool prep_unit(const PrepArgs& a, int c, int hk, unsi
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
             finish(tt, a.scale, y4[tt]);
-            st8(&sm.qa.q[tq + tt][8 * cg], y4[tt]);
+            st8(sm.qrow(tq + tt) + 8 * cg, y4[tt]);
         }
         conv_quad(xk, y4);   // k of the four tokens, also stored transposed
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
             finish(tt, 1.0f, y4[tt]);
-            st8(&sm.ka.k[tq + tt][8 * cg], y4[tt]);
+            st8(sm.krow(tq + tt) + 8 * cg, y4[tt]);
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-            st4(&sm.kt[8 * cg + e][tsw(8 * cg + e, tq >> 2)], y4[0][e], y4[1][e], y4[2][e], y4[3][e]);
+            st4(sm.ktrow(8 * cg + e) + tsw(8 * cg + e, tq >> 2), y4[0][e], y4[1][e], y4[2][e], y4[3][e]);
     }
     __syncthreads();
     const bool probe = kCo && ps != nullptr && ps->xcc != nullptr;   // uniform
@@ -456,7 +506,7 @@ __device__ __forceinline__ bool prep_unit(const PrepArgs& a, int c, int hk, unsi
             const int row = 16 * (fi >> 2) + l16, kb = 32 * (fi & 3);
             F fr;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) fr.v[j] = sm.qa.q[row][kb + kidx(g4, j)];
+            for (int j = 0; j < 8; ++j) fr.v[j] = sm.qrow(row)[kb + kidx(g4, j)];
             St::frag(KB + (kKB_Q + fi) * 64, lane, fr);
         }
         {   // K^T: rows = dk (tile fi / 2), K = token block fi % 2
@@ -465,7 +515,7 @@ __device__ __forceinline__ bool prep_unit(const PrepArgs& a, int c, int hk, unsi
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int t = kb + kidx(g4, j);
-                fr.v[j] = sm.kt[row][tsw(row, t >> 2) + (t & 3)];
+                fr.v[j] = sm.ktrow(row)[tsw(row, t >> 2) + (t & 3)];
             }
             St::frag(KB + (kKB_KT + fi) * 64, lane, fr);
         }
@@ -510,8 +560,8 @@ __device__ __forceinline__ bool prep_unit(const PrepArgs& a, int c, int hk, unsi
                 for (int q = 0; q < 4; ++q)
 #pragma unroll
                     for (int j = 0; j < 8; ++j) {
-                        if (kuse[tile]) kf[tile][q].v[j] = sm.ka.k[16 * tile + l16][32 * q + kidx(g4, j)];
-                        if (quse[tile]) qf[tile][q].v[j] = sm.qa.q[16 * tile + l16][32 * q + kidx(g4, j)];
+                        if (kuse[tile]) kf[tile][q].v[j] = sm.krow(16 * tile + l16)[32 * q + kidx(g4, j)];
+                        if (quse[tile]) qf[tile][q].v[j] = sm.qrow(16 * tile + l16)[32 * q + kidx(g4, j)];
                     }
 #pragma unroll
             for (int c = 0; c < 3; ++c) {
@@ -531,11 +581,63 @@ __device__ __forceinline__ bool prep_unit(const PrepArgs& a, int c, int hk, unsi
                             mma(KQ[jb][h], kf[2 * kPP[jb] + h][q], qf[kPT[jb]][q]);   // rows i, cols t
                 }
         };
-        switch (wave) {
-            case 0: cells(std::integral_constant<int, 0>{}); break;
-            case 1: cells(std::integral_constant<int, 1>{}); break;
-            case 2: cells(std::integral_constant<int, 2>{}); break;
-            default: cells(std::integral_constant<int, 3>{}); break;
+        // lean: each cell reads its two tiles' fragments when it is formed
+        // (tiles shared by cells are read again), so that only two tiles'
+        // fragments are live at a time
+        auto cells_lean = [&](auto wc) {
+            constexpr int W = decltype(wc)::value;
+            constexpr int kNK = W >= 2 ? 3 : 2, kNP = W >= 2 ? 1 : 2;
+            constexpr int kTT[3] = {W >= 2 ? W : (W == 0 ? 0 : 1), W >= 2 ? W : (W == 0 ? 3 : 1), W};
+            constexpr int kTI[3] = {0, W >= 2 ? 1 : (W == 0 ? 3 : 1), 2};
+            constexpr int kPT[2] = {W, W >= 2 ? W : 3 - W};
+            constexpr int kPP[2] = {0, 1};
+            auto tile = [&](MT* (Smem::*row)(int), int t, F (&f)[4]) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) f[q].v[j] = (sm.*row)(16 * t + l16)[32 * q + kidx(g4, j)];
+            };
+#pragma unroll
+            for (int c = 0; c < 3; ++c) {
+                KK[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (c < kNK) {
+                    F ft[4], fi[4];
+                    tile(&Smem::krow, kTT[c], ft);
+                    tile(&Smem::krow, kTI[c], fi);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) mma(KK[c], ft[q], fi[q]);
+                }
+            }
+#pragma unroll
+            for (int jb = 0; jb < 2; ++jb) {
+                F fq[4];
+                if (jb < kNP) tile(&Smem::qrow, kPT[jb], fq);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    KQ[jb][h] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    if (jb < kNP && 2 * kPP[jb] + h <= kPT[jb]) {
+                        F fk[4];
+                        tile(&Smem::krow, 2 * kPP[jb] + h, fk);
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) mma(KQ[jb][h], fk[q], fq[q]);
+                    }
+                }
+            }
+        };
+        if constexpr (kLean) {
+            switch (wave) {
+                case 0: cells_lean(std::integral_constant<int, 0>{}); break;
+                case 1: cells_lean(std::integral_constant<int, 1>{}); break;
+                case 2: cells_lean(std::integral_constant<int, 2>{}); break;
+                default: cells_lean(std::integral_constant<int, 3>{}); break;
+            }
+        } else {
+            switch (wave) {
+                case 0: cells(std::integral_constant<int, 0>{}); break;
+                case 1: cells(std::integral_constant<int, 1>{}); break;
+                case 2: cells(std::integral_constant<int, 2>{}); break;
+                default: cells(std::integral_constant<int, 3>{}); break;
+            }
         }
     }
     __syncthreads();   // q / k rows are dead from here on; their LDS holds A and T
@@ -577,7 +679,7 @@ __device__ __forceinline__ bool prep_unit(const PrepArgs& a, int c, int hk, unsi
             }
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                st4(&sm.vt[8 * cg + e][tsw(8 * cg + e, tq >> 2)], y[0][e], y[1][e], y[2][e], y[3][e]);
+                st4(sm.vtrow(8 * cg + e) + tsw(8 * cg + e, tq >> 2), y[0][e], y[1][e], y[2][e], y[3][e]);
             if (wave == 0) {   // G = inclusive cumsum of g over the chunk (padding: g = b = 0)
                 const float G = wave_incl_scan(gcur);
                 const float Gn = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, G), 63));
@@ -600,7 +702,7 @@ __device__ __forceinline__ bool prep_unit(const PrepArgs& a, int c, int hk, unsi
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int t = 16 * tt + 4 * g4 + r, i = 16 * ti + l16;
-                    sm.ka.a[t][i] = (i < t) ? sm.b[t] * KK[c][r] * exp_f32(sm.G[t] - sm.G[i]) : 0.f;
+                    *sm.A(t, i) = (i < t) ? sm.b[t] * KK[c][r] * exp_f32(sm.G[t] - sm.G[i]) : 0.f;
                 }
             }
         }
@@ -633,11 +735,11 @@ __device__ __forceinline__ bool prep_unit(const PrepArgs& a, int c, int hk, unsi
             for (int r = 0; r < 16; ++r) {
                 float s = (r == j) ? 1.f : 0.f;
 #pragma unroll
-                for (int m = 0; m < r; ++m) s = fmaf(-sm.ka.a[16 * bb + r][16 * bb + m], X[m], s);
+                for (int m = 0; m < r; ++m) s = fmaf(-*sm.A(16 * bb + r, 16 * bb + m), X[m], s);
                 X[r] = s;
             }
 #pragma unroll
-            for (int r = 0; r < 16; ++r) sm.qa.t[16 * bb + r][16 * bb + j] = X[r];
+            for (int r = 0; r < 16; ++r) *sm.T(16 * bb + r, 16 * bb + j) = X[r];
         }
         __syncthreads();
 
@@ -653,26 +755,24 @@ __device__ __forceinline__ bool prep_unit(const PrepArgs& a, int c, int hk, unsi
         //     the sweep reads (rows dk, columns tokens), stored negated.
         {
             typedef Mm16<MT> P;
-            const float* Ab = &sm.ka.a[0][0];
-            const float* Tb = &sm.qa.t[0][0];
             typename P::Op X[3][4];   // B operands of X_0 .. X_2 per column tile
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 // T_rr: A operand (lane (row l16, g4): columns 4 g4 ..) and B operand of T_rr^T
                 const typename P::Op Top =
-                    P::op(*reinterpret_cast<const f32x4*>(Tb + (16 * r + l16) * LD + 16 * r + 4 * g4));
+                    P::op(*reinterpret_cast<const f32x4*>(sm.T(16 * r + l16, 16 * r + 4 * g4)));
                 f32x4 Z[4];   // column tiles q: dk 2w, 2w + 1, dv 2w, 2w + 1
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int col = 16 * (2 * wave + (q & 1)) + l16;
-                    const MT* y = (q < 2 ? &sm.kt[col][0] : &sm.vt[col][0]) + tsw(col, 4 * r + g4);
+                    const MT* y = (q < 2 ? sm.ktrow(col) : sm.vtrow(col)) + tsw(col, 4 * r + g4);
                     const float* sc = (q < 2 ? sm.bg : sm.b) + 16 * r + 4 * g4;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) Z[q][i] = sc[i] * static_cast<float>(y[i]);
                 }
 #pragma unroll
                 for (int m = 0; m < r; ++m) {
-                    const f32x4 a4 = *reinterpret_cast<const f32x4*>(Ab + (16 * r + l16) * LD + 16 * m + 4 * g4);
+                    const f32x4 a4 = *reinterpret_cast<const f32x4*>(sm.A(16 * r + l16, 16 * m + 4 * g4));
                     const typename P::Op Aop = P::op(-a4);
 #pragma unroll
                     for (int q = 0; q < 4; ++q) Z[q] = P::mul(Aop, X[m][q], Z[q]);
@@ -702,10 +802,17 @@ __device__ __forceinline__ bool prep_unit(const PrepArgs& a, int c, int hk, unsi
     return true;
 }
 
+// The separate prep kernel: bf16 units in the lean layout, three per CU;
+// fp32 units (twice the bytes per element) two per CU.
+template <class IO> constexpr bool prep_lean() { return sizeof(IO) == 2; }
+template <class IO> constexpr unsigned prep_smem_bytes() {
+    return prep_lean<IO>() ? sizeof(PrepSmemLean) : sizeof(PrepSmem<typename MathOf<IO>::T>);
+}
+
 template <class IO, bool kConv>
-__global__ __launch_bounds__(256, 2) void gdn_chunk_prep_kernel(PrepArgs a) {
+__global__ __launch_bounds__(256, prep_lean<IO>() ? 3 : 2) void gdn_chunk_prep_kernel(PrepArgs a) {
     extern __shared__ __attribute__((aligned(16))) unsigned char gdn_prep_smem[];
-    prep_unit<IO, kConv>(a, blockIdx.x, blockIdx.y, gdn_prep_smem, threadIdx.x);
+    prep_unit<IO, kConv, false, prep_lean<IO>()>(a, blockIdx.x, blockIdx.y, gdn_prep_smem, threadIdx.x);
 }
 
 // ===========================================================================
@@ -1594,16 +1701,16 @@ __global__ __launch_bounds__(512) void gdn_prefill_pipe_kernel(PipeArgs a) {
 static hipError_t allow_dynamic_lds(const void* kern, unsigned bytes) {
     static const hipError_t bf16_conv = hipFuncSetAttribute(
         reinterpret_cast<const void*>(gdn_chunk_prep_kernel<uint16_t, true>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, sizeof(PrepSmem<bf16>));
+        hipFuncAttributeMaxDynamicSharedMemorySize, prep_smem_bytes<uint16_t>());
     static const hipError_t bf16_noconv = hipFuncSetAttribute(
         reinterpret_cast<const void*>(gdn_chunk_prep_kernel<uint16_t, false>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, sizeof(PrepSmem<bf16>));
+        hipFuncAttributeMaxDynamicSharedMemorySize, prep_smem_bytes<uint16_t>());
     static const hipError_t f32_conv = hipFuncSetAttribute(
         reinterpret_cast<const void*>(gdn_chunk_prep_kernel<float, true>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, sizeof(PrepSmem<float>));
+        hipFuncAttributeMaxDynamicSharedMemorySize, prep_smem_bytes<float>());
     static const hipError_t f32_noconv = hipFuncSetAttribute(
         reinterpret_cast<const void*>(gdn_chunk_prep_kernel<float, false>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, sizeof(PrepSmem<float>));
+        hipFuncAttributeMaxDynamicSharedMemorySize, prep_smem_bytes<float>());
     static const hipError_t sweep = hipFuncSetAttribute(
         reinterpret_cast<const void*>(gdn_state_sweep_lds_kernel<kSweepSW, kSweepNT, kSweepPW>),
         hipFuncAttributeMaxDynamicSharedMemorySize, SweepCfg::kBytes);
@@ -1634,8 +1741,7 @@ static hipError_t launch_chunk_table(const PrefillPlan& p, hipStream_t s) {
 
 template <class IO>
 static hipError_t launch_prep(const PrefillPlan& p, int slots, hipStream_t s) {
-    typedef typename MathOf<IO>::T MT;
-    const unsigned smem = sizeof(PrepSmem<MT>);
+    const unsigned smem = prep_smem_bytes<IO>();
     auto kern = p.conv ? gdn_chunk_prep_kernel<IO, true> : gdn_chunk_prep_kernel<IO, false>;
     hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(kern), smem);
     if (e != hipSuccess) return e;
