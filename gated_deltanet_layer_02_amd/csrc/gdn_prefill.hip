@@ -1523,11 +1523,19 @@ __global__ __launch_bounds__(256) void gdn_conv_state_kernel(ConvStateArgs a) {
 // workgroups per head.
 constexpr int kSweepSW = 4, kSweepNT = 1, kSweepPW = 4;
 typedef SweepLds<kSweepSW, kSweepNT> SweepCfg;
-constexpr unsigned kPipePrepStride = (sizeof(PrepSmem<bf16>) + 255) / 256 * 256;
-constexpr unsigned kPipeSmem =
-    2 * kPipePrepStride > (unsigned)SweepCfg::kBytes ? 2 * kPipePrepStride : (unsigned)SweepCfg::kBytes;
-static_assert(kPipeSmem <= 160 * 1024, "fits one CU's LDS");
-static_assert(kPipeSmem > 80 * 1024, "one workgroup per CU");
+// Two forms of the launch: prep workgroups of two full-layout units (512
+// threads), or of three lean units (768 threads; sweep and post workgroups
+// then leave their last four waves idle).  Either way one workgroup per CU.
+template <bool kLean> struct PipeForm {
+    static constexpr int kUnits = kLean ? 3 : 2;                    // prep units per workgroup
+    static constexpr int kThreads = 256 * kUnits;
+    static constexpr unsigned kPrepStride =
+        ((kLean ? sizeof(PrepSmemLean) : sizeof(PrepSmem<bf16>)) + 255) / 256 * 256;
+    static constexpr unsigned kSmem = kUnits * kPrepStride > (unsigned)SweepCfg::kBytes ? kUnits * kPrepStride
+                                                                                        : (unsigned)SweepCfg::kBytes;
+    static_assert(kSmem <= 160 * 1024, "fits one CU's LDS");
+    static_assert(kSmem > 80 * 1024, "one workgroup per CU");
+};
 
 // Prep unit of half `half` of prep workgroup b.  The first n_single
 // workgroups run one unit each (half 1 has none) for the chunks below
@@ -1538,11 +1546,12 @@ static_assert(kPipeSmem > 80 * 1024, "one workgroup per CU");
 // round-robin; n_sweep, n_single and n_post are multiples of 8) and takes units of the
 // key heads hk = b (mod 8), which the sweep also keeps on that XCD; otherwise
 // units go chunk-major over all key heads.  c = chunk_slots: no unit.
+template <int kUnits>
 __device__ __forceinline__ void pipe_prep_unit(const PipeArgs& a, int b, int half, int& c, int& hk) {
     const int Hk = a.prep.Hk;
     const bool single = b < a.n_single;
     const int u = single ? b : b - a.n_single;   // workgroup index within its kind
-    const int k = single ? 1 : 2;                // units per workgroup
+    const int k = single ? 1 : kUnits;           // units per workgroup
     if (a.prep_xcd) {
         const int per = Hk >> 3;
         const int ui = k * (u >> 3) + (single ? 0 : half);
@@ -1659,28 +1668,31 @@ __device__ void pipe_post(const PipeArgs& a, int w, volatile int* box) {
     }
 }
 
-template <bool kConv>
-__global__ __launch_bounds__(512) void gdn_prefill_pipe_kernel(PipeArgs a) {
-    static_assert(64 * (kSweepSW + kSweepPW) == 512, "a sweep workgroup fills the launch");
+template <bool kConv, bool kLean>
+__global__ __launch_bounds__(PipeForm<kLean>::kThreads) void gdn_prefill_pipe_kernel(PipeArgs a) {
+    typedef PipeForm<kLean> Form;
+    static_assert(64 * (kSweepSW + kSweepPW) == 512, "a sweep workgroup's waves");
     extern __shared__ __attribute__((aligned(16))) unsigned char gdn_pipe_smem[];
     if ((int)blockIdx.x < a.n_sweep) {
+        if (threadIdx.x >= 512) return;   // waves beyond the sweep workgroup's eight
         sweep_wg<kSweepSW, kSweepNT, kSweepPW, true>(a.sweep, blockIdx.x, gdn_pipe_smem, a.sync);
         return;
     }
     const int r = (int)blockIdx.x - a.n_sweep;   // index past the sweep workgroups
     const int post = a.post_first ? r : r - a.n_prep;
     if (post >= 0 && post < a.n_post) {
+        if (threadIdx.x >= 512) return;   // the post work is laid out for 512 threads
         pipe_post(a, post, reinterpret_cast<volatile int*>(gdn_pipe_smem));
         return;
     }
     // uniform per wave: an SGPR, so the unit's LDS base stays scalar
     const int half = __builtin_amdgcn_readfirstlane(threadIdx.x >> 8), tid = threadIdx.x & 255;
     int c, hk;
-    pipe_prep_unit(a, a.post_first ? r - a.n_post : r, half, c, hk);
+    pipe_prep_unit<Form::kUnits>(a, a.post_first ? r - a.n_post : r, half, c, hk);
     if (c >= a.chunk_slots) return;
     bool local = false;
-    if (!prep_unit<uint16_t, kConv, true>(a.prep, c, hk, gdn_pipe_smem + half * kPipePrepStride, tid, &a.sync,
-                                          &local))
+    if (!prep_unit<uint16_t, kConv, true, kLean>(a.prep, c, hk, gdn_pipe_smem + half * Form::kPrepStride, tid,
+                                                 &a.sync, &local))
         return;
     // publish: every wave's stores are complete in this XCD's L2 (vmcnt counts
     // stores on this architecture), then one flag: epoch + 1 for readers on
@@ -1697,6 +1709,7 @@ __global__ __launch_bounds__(512) void gdn_prefill_pipe_kernel(PipeArgs a) {
 // ===========================================================================
 // host-side launch sequence
 // ===========================================================================
+
 // Dynamic LDS above 64 KB must be allowed per kernel; done once per kernel.
 static hipError_t allow_dynamic_lds(const void* kern, unsigned bytes) {
     static const hipError_t bf16_conv = hipFuncSetAttribute(
@@ -1715,17 +1728,24 @@ static hipError_t allow_dynamic_lds(const void* kern, unsigned bytes) {
         reinterpret_cast<const void*>(gdn_state_sweep_lds_kernel<kSweepSW, kSweepNT, kSweepPW>),
         hipFuncAttributeMaxDynamicSharedMemorySize, SweepCfg::kBytes);
     static const hipError_t pipe_conv = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(gdn_prefill_pipe_kernel<true>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, kPipeSmem);
+        reinterpret_cast<const void*>(gdn_prefill_pipe_kernel<true, false>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, PipeForm<false>::kSmem);
     static const hipError_t pipe_noconv = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(gdn_prefill_pipe_kernel<false>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, kPipeSmem);
+        reinterpret_cast<const void*>(gdn_prefill_pipe_kernel<false, false>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, PipeForm<false>::kSmem);
+    static const hipError_t pipe_conv_lean = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(gdn_prefill_pipe_kernel<true, true>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, PipeForm<true>::kSmem);
+    static const hipError_t pipe_noconv_lean = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(gdn_prefill_pipe_kernel<false, true>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, PipeForm<true>::kSmem);
     static const hipError_t sweep_f32 = hipFuncSetAttribute(
         reinterpret_cast<const void*>(gdn_state_sweep_f32_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
         kF32Lds);
     (void)kern;
     (void)bytes;
-    for (hipError_t e : {bf16_conv, bf16_noconv, f32_conv, f32_noconv, sweep, pipe_conv, pipe_noconv, sweep_f32})
+    for (hipError_t e : {bf16_conv, bf16_noconv, f32_conv, f32_noconv, sweep, pipe_conv, pipe_noconv,
+                         pipe_conv_lean, pipe_noconv_lean, sweep_f32})
         if (e != hipSuccess) return e;
     return hipSuccess;
 }
@@ -1848,7 +1868,15 @@ static bool use_pipe(const PrefillPlan& p) {
     return 2 * ns <= cus && 4 * (ns + pipe_post_blocks(p, cus)) <= 3 * cus;
 }
 
-static hipError_t launch_pipe(const PrefillPlan& p, hipStream_t s) {
+// The prep form of a pipelined launch: three lean units per workgroup for long
+// sequences (whose time the prep's throughput sets: 65,536 tokens 1.835 ms
+// against 1.906 ms with two full units), two full units otherwise (the
+// sweep's chain sets the time, and the full unit is the faster one alone at
+// the start: 4,096 tokens 140 us against 150 us).
+static bool pipe_lean(const PrefillPlan& p) { return pipe_post_first(p); }
+
+template <bool kLean>
+static hipError_t launch_pipe_form(const PrefillPlan& p, hipStream_t s) {
     PipeArgs a;
     a.prep = p.prep;
     a.sweep = p.sweep;
@@ -1863,8 +1891,9 @@ static hipError_t launch_pipe(const PrefillPlan& p, hipStream_t s) {
     a.prep_xcd = p.prep.Hk % 8 == 0;
     a.c_single = std::min(p.chunk_slots, kPipeSingleChunks);
     a.n_single = (a.c_single * p.prep.Hk + 7) / 8 * 8;
-    const int64_t units = (int64_t)(p.chunk_slots - a.c_single) * p.prep.Hk;   // two per workgroup
-    const int64_t prep_wgs = a.prep_xcd ? 8 * ((units / 8 + 1) / 2) : (units + 1) / 2;
+    constexpr int64_t ku = PipeForm<kLean>::kUnits;   // units per workgroup
+    const int64_t units = (int64_t)(p.chunk_slots - a.c_single) * p.prep.Hk;
+    const int64_t prep_wgs = a.prep_xcd ? 8 * ((units / 8 + ku - 1) / ku) : (units + ku - 1) / ku;
     a.n_prep = a.n_single + (int32_t)((prep_wgs + 7) / 8 * 8);
     a.n_post = pipe_post_blocks(p, device_cus());
     a.post_first = pipe_post_first(p) ? 1 : 0;
@@ -1875,9 +1904,15 @@ static hipError_t launch_pipe(const PrefillPlan& p, hipStream_t s) {
     if (!p.l2_handoff || a.sync.xcc_per > 64 || SweepLds<kSweepSW, kSweepNT>::kGroups > kD / 16)
         a.sync.xcc = nullptr;
     GDN_TRY(allow_dynamic_lds(nullptr, 0));
-    auto kern = p.conv ? gdn_prefill_pipe_kernel<true> : gdn_prefill_pipe_kernel<false>;
-    hipLaunchKernelGGL(kern, dim3((unsigned)(a.n_sweep + a.n_prep + a.n_post)), dim3(512), kPipeSmem, s, a);
+    typedef PipeForm<kLean> Form;
+    auto kern = p.conv ? gdn_prefill_pipe_kernel<true, kLean> : gdn_prefill_pipe_kernel<false, kLean>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)(a.n_sweep + a.n_prep + a.n_post)), dim3(Form::kThreads), Form::kSmem,
+                       s, a);
     return hipGetLastError();
+}
+
+static hipError_t launch_pipe(const PrefillPlan& p, hipStream_t s) {
+    return pipe_lean(p) ? launch_pipe_form<true>(p, s) : launch_pipe_form<false>(p, s);
 }
 
 
