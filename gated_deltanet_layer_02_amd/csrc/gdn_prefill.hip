@@ -1583,55 +1583,105 @@ __device__ __forceinline__ bool post_wait(const uint64_t* f, int count, const Pi
     return ok;
 }
 
-// Gated norm, in place, of the rows of unit (chunk slot c, key head hk) once
-// the sweep has published them: out = o rsqrt(mean(o^2) + eps) w SiLU(z).
-// Rows 4 wave + g, + 32, ... (a row is 16 lanes x 8 channels; o is read with
-// coherent loads).  Returns false when the wait gave up.
-__device__ __forceinline__ bool pipe_norm_unit(const PipeArgs& a, int c, int hk, const float (&w)[8],
-                                               volatile int* box) {
-    int n, t0, len, seq_start;
-    if (!locate_chunk(a.prep, c, n, t0, len, seq_start)) return true;
-    const int Hv = a.prep.Hv, group = Hv / a.prep.Hk, h0 = hk * group;
-    if (!post_wait(a.sync.oready + ((size_t)c * Hv + h0) * 8, group * 8, a.sync, a.sweep.status, box))
-        return false;
-    uint16_t* out = static_cast<uint16_t*>(a.sweep.out) + (size_t)t0 * Hv * kD;
-    const uint16_t* z = static_cast<const uint16_t*>(a.z) + (size_t)t0 * Hv * kD;
-    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(out, 0, 0x7fffffff, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rz =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(z), 0, 0x7fffffff, 0x00020000);
-    const int l16 = threadIdx.x & 15;
-    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-    constexpr int kB = 4;   // rows per lane in flight: all loads issued before any math
-    for (int r0 = threadIdx.x >> 4; r0 < len * group; r0 += 32 * kB) {
-        u32x4 ov[kB], zv[kB];
-        uint32_t e[kB];
+// Gated norm units of the pipelined launch: out = o rsqrt(mean(o^2) + eps) w
+// SiLU(z), in place, for the rows of unit (chunk slot c, key head hk) once the
+// sweep has published them.  A row is one token of one value head, 16 lanes x
+// 8 channels; lane group g = threadIdx.x / 16 of the 512 threads takes rows
+// g + 32 b (b < kNormB) of each pass of 32 kNormB rows.  SiLU(z) does not
+// depend on the sweep: it is formed before the unit's wait, and the next
+// unit's z rows are loaded while this unit's o rows are in flight, so that a
+// unit costs one round trip to memory after its flags are up.  The products
+// are taken in the order of the separate norm kernel, ((o r) w) SiLU(z), so
+// that both launch forms give the same bits.
+constexpr int kNormB = 4;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+struct NormLoc {
+    int c, hk, t0, rows;   // rows = tokens x value heads of the key head; 0: no unit
+};
+__device__ __forceinline__ NormLoc norm_loc(const PipeArgs& a, int c, int hk) {
+    NormLoc u{c, hk, 0, 0};
+    int n, len, seq_start;
+    if (locate_chunk(a.prep, c, n, u.t0, len, seq_start)) u.rows = len * (a.prep.Hv / a.prep.Hk);
+    return u;
+}
+// Element offsets of this lane's 8 channels in its rows of a pass, from
+// token u.t0's row, for key head 0 (a unit adds hk * group * kD): computed
+// once per workgroup, since they do not depend on the unit.  Addresses are the
+// unit's base + a 32-bit offset.
+struct NormRows {
+    uint32_t off[kNormB];
+};
+__device__ __forceinline__ NormRows norm_rows(const PipeArgs& a, int pass) {
+    const int Hv = a.prep.Hv, group = Hv / a.prep.Hk;
+    NormRows nr;
 #pragma unroll
-        for (int b = 0; b < kB; ++b) {
-            const int r = r0 + 32 * b;
-            e[b] = (uint32_t)((r / group) * Hv + h0 + r % group) * kD + 8 * l16;   // element
-            if (r < len * group) {
-                ov[b] = __builtin_amdgcn_raw_buffer_load_b128(ro, (int)(2 * e[b]), 0, 16);   // coherent
-                zv[b] = __builtin_amdgcn_raw_buffer_load_b128(rz, (int)(2 * e[b]), 0, 0);
-            }
-        }
-#pragma unroll
-        for (int b = 0; b < kB; ++b) {
-            if (r0 + 32 * b >= len * group) continue;
-            const u16x8 o8 = __builtin_bit_cast(u16x8, ov[b]), z8 = __builtin_bit_cast(u16x8, zv[b]);
-            float x[8];
-            float ss = 0.f;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                x[i] = bf16_bits_to_f32(o8[i]);
-                ss = fmaf(x[i], x[i], ss);
-            }
-            const float rr = rsqrt_f32(row16_sum(ss) * (1.0f / kD) + a.norm_eps);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) x[i] = x[i] * rr * w[i] * silu_f32(bf16_bits_to_f32(z8[i]));
-            store8(out + e[b], x);
-        }
+    for (int b = 0; b < kNormB; ++b) {
+        const int r = pass * 32 * kNormB + (int)(threadIdx.x >> 4) + 32 * b;
+        nr.off[b] = (uint32_t)((r / group) * Hv + r % group) * kD + 8 * (threadIdx.x & 15);
     }
-    return true;
+    return nr;
+}
+__device__ __forceinline__ uint32_t norm_elem(const PipeArgs& a, const NormLoc& u, const NormRows& nr, int b) {
+    return nr.off[b] + (uint32_t)(u.hk * (a.prep.Hv / a.prep.Hk) * kD);
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t norm_rsrc(const void* base, const PipeArgs& a, const NormLoc& u) {
+    const uint16_t* p = static_cast<const uint16_t*>(base) + (size_t)u.t0 * a.prep.Hv * kD;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p), 0, 0x7fffffff, 0x00020000);
+}
+__device__ __forceinline__ int norm_row(int pass, int b) { return pass * 32 * kNormB + (int)(threadIdx.x >> 4) + 32 * b; }
+
+// raw z rows of one pass (rows past the unit read as zero)
+__device__ __forceinline__ void norm_z_load(const PipeArgs& a, const NormLoc& u, const NormRows& nr, int pass,
+                                            u32x4 (&zr)[kNormB]) {
+    const __amdgpu_buffer_rsrc_t rz = norm_rsrc(a.z, a, u);
+#pragma unroll
+    for (int b = 0; b < kNormB; ++b) {
+        const int r = norm_row(pass, b);
+        zr[b] = r < u.rows ? __builtin_amdgcn_raw_buffer_load_b128(rz, (int)(2 * norm_elem(a, u, nr, b)), 0, 0)
+                           : u32x4{0u, 0u, 0u, 0u};
+    }
+}
+__device__ __forceinline__ void norm_silu(const u32x4 (&zr)[kNormB], float (&sz)[kNormB][8]) {
+#pragma unroll
+    for (int b = 0; b < kNormB; ++b) {
+        const u16x8 z8 = __builtin_bit_cast(u16x8, zr[b]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sz[b][i] = silu_f32(bf16_bits_to_f32(z8[i]));
+    }
+}
+// One pass of unit u whose flags are up: the o rows (agent-coherent loads),
+// then, when nx is given, the z rows of nx's first pass (rows nr0) into zr,
+// then the normalised rows out.
+__device__ __forceinline__ void norm_pass(const PipeArgs& a, const NormLoc& u, const NormRows& nr, int pass,
+                                          const float (&w)[8], const float (&sz)[kNormB][8], const NormLoc* nx,
+                                          const NormRows& nr0, u32x4 (&zr)[kNormB]) {
+    const __amdgpu_buffer_rsrc_t ro = norm_rsrc(a.sweep.out, a, u);
+    u32x4 ov[kNormB];
+#pragma unroll
+    for (int b = 0; b < kNormB; ++b) {
+        const int r = norm_row(pass, b);
+        if (r < u.rows) ov[b] = __builtin_amdgcn_raw_buffer_load_b128(ro, (int)(2 * norm_elem(a, u, nr, b)), 0, 16);
+    }
+    if (nx != nullptr) norm_z_load(a, *nx, nr0, 0, zr);
+    uint16_t* out = static_cast<uint16_t*>(a.sweep.out) + (size_t)u.t0 * a.prep.Hv * kD;
+#pragma unroll
+    for (int b = 0; b < kNormB; ++b) {
+        const int r = norm_row(pass, b);
+        if (r >= u.rows) continue;
+        const u16x8 o8 = __builtin_bit_cast(u16x8, ov[b]);
+        float x[8];
+        float ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            x[i] = bf16_bits_to_f32(o8[i]);
+            ss = fmaf(x[i], x[i], ss);
+        }
+        const float rr = rsqrt_f32(row16_sum(ss) * (1.0f / kD) + a.norm_eps);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = x[i] * rr * w[i] * sz[b][i];
+        store8(out + norm_elem(a, u, nr, b), x);
+    }
 }
 
 // Workgroups after the prep ones: gated norm units (chunk-major; with
@@ -1644,13 +1694,55 @@ __device__ void pipe_post(const PipeArgs& a, int w, volatile int* box) {
     if (a.z != nullptr) {
         float wv[8];
         load8(static_cast<const uint16_t*>(a.norm_w) + 8 * (threadIdx.x & 15), wv);
-        if (a.prep_xcd) {
-            const int per = Hk >> 3, nw = a.n_post >> 3;
-            for (int ui = w >> 3; live && ui < a.chunk_slots * per; ui += nw)
-                live = pipe_norm_unit(a, ui / per, (w & 7) + 8 * (ui % per), wv, box);
-        } else {
-            for (int u = w; live && u < a.chunk_slots * Hk; u += a.n_post)
-                live = pipe_norm_unit(a, u / Hk, u % Hk, wv, box);
+        // i-th unit of this workgroup: chunk-major; with prep_xcd, the units of
+        // the key heads on this workgroup's XCD
+        auto unit_at = [&](int i, NormLoc& u) -> bool {
+            int c, hk;
+            if (a.prep_xcd) {
+                const int per = Hk >> 3, ui = (w >> 3) + i * (a.n_post >> 3);
+                if (ui >= a.chunk_slots * per) return false;
+                c = ui / per;
+                hk = (w & 7) + 8 * (ui % per);
+            } else {
+                const int ui = w + i * a.n_post;
+                if (ui >= a.chunk_slots * Hk) return false;
+                c = ui / Hk;
+                hk = ui % Hk;
+            }
+            u = norm_loc(a, c, hk);
+            return true;
+        };
+        const int group = a.prep.Hv / Hk;
+        const NormRows nr0 = norm_rows(a, 0);
+        NormLoc u;
+        if (unit_at(0, u)) {
+            u32x4 zr[kNormB];
+            float sz[kNormB][8];
+            norm_z_load(a, u, nr0, 0, zr);
+            norm_silu(zr, sz);
+            for (int i = 0; live; ++i) {
+                NormLoc nx;
+                const bool more = unit_at(i + 1, nx);
+                if (u.rows > 0) {
+                    live = post_wait(a.sync.oready + ((size_t)u.c * a.prep.Hv + u.hk * group) * 8, group * 8,
+                                     a.sync, a.sweep.status, box);
+                    if (!live) break;
+                    norm_pass(a, u, nr0, 0, wv, sz, more ? &nx : nullptr, nr0, zr);
+                    for (int pass = 1; pass * 32 * kNormB < u.rows; ++pass) {   // more than 32 kNormB rows
+                        const NormRows nr = norm_rows(a, pass);
+                        u32x4 z2[kNormB];
+                        float sz2[kNormB][8];
+                        norm_z_load(a, u, nr, pass, z2);
+                        norm_silu(z2, sz2);
+                        norm_pass(a, u, nr, pass, wv, sz2, nullptr, nr0, z2);
+                    }
+                } else if (more) {
+                    norm_z_load(a, nx, nr0, 0, zr);
+                }
+                if (!more) break;
+                norm_silu(zr, sz);
+                u = nx;
+            }
         }
     }
     const ConvStateArgs& cs = a.conv_state;
