@@ -72,6 +72,16 @@ def test_zero_tokens_passes_states_through():
     assert np.array_equal(cs, x["conv_state"])
 
 
+def test_many_short_sequences_qwen_shape():
+    """Nine sequences of 0 to 6 chunks at 16 key / 32 value heads: 576 sweep
+    workgroups, more than one round of CUs, so the sweep runs with split
+    operand buffers; the lengths take it through its first iterations and the
+    copies it repeats past a sequence's last chunk."""
+    p = gs.Problem("short-seqs-qwen", [0, 1, 63, 64, 65, 130, 200, 257, 330], Hk=16, Hv=32,
+                   init_state_std=0.01, conv_state_std=0.01, seed=4242)
+    say(f"short sequences {check_prefill(p, gs.generate(p), batch=16)}")
+
+
 # Full sizes, every value head against the oracle (the bench's launch
 # configuration: plain calls, which take the pipelined form for C1 and C2 and
 # separate launches for C3).
