@@ -30,17 +30,30 @@ __device__ __forceinline__ int row_dk(const float*, int l16, int e) {
     return e < 4 ? 4 * l16 + e : 64 + 4 * l16 + (e - 4);
 }
 __device__ __forceinline__ int row_dk(const uint16_t*, int l16, int e) { return 8 * l16 + e; }
-__device__ __forceinline__ void load_row8(const float* row, int l16, float* o) {
-    const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row) + l16);
-    const f32x4 b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + 64) + l16);
+// Raw state rows as loaded (fp32: two 16-byte pieces, bf16: one), widened to
+// fp32 one row at a time when used.
+template <class ST> struct RawRow;
+template <> struct RawRow<float> {
+    f32x4 a, b;
+    __device__ __forceinline__ void load(const float* row, int l16) {
+        a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row) + l16);
+        b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + 64) + l16);
+    }
+    __device__ __forceinline__ void widen(float* o) const {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) { o[e] = a[e]; o[4 + e] = b[e]; }
-}
-__device__ __forceinline__ void load_row8(const uint16_t* row, int l16, float* o) {
-    const u16x8 v = __builtin_nontemporal_load(reinterpret_cast<const u16x8*>(row) + l16);
+        for (int e = 0; e < 4; ++e) { o[e] = a[e]; o[4 + e] = b[e]; }
+    }
+};
+template <> struct RawRow<uint16_t> {
+    u16x8 v;
+    __device__ __forceinline__ void load(const uint16_t* row, int l16) {
+        v = __builtin_nontemporal_load(reinterpret_cast<const u16x8*>(row) + l16);
+    }
+    __device__ __forceinline__ void widen(float* o) const {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = bf16_bits_to_f32(v[e]);
-}
+        for (int e = 0; e < 8; ++e) o[e] = bf16_bits_to_f32(v[e]);
+    }
+};
 __device__ __forceinline__ void store_row8(float* row, int l16, const float* x) {
     __builtin_nontemporal_store(f32x4{x[0], x[1], x[2], x[3]}, reinterpret_cast<f32x4*>(row) + l16);
     __builtin_nontemporal_store(f32x4{x[4], x[5], x[6], x[7]}, reinterpret_cast<f32x4*>(row + 64) + l16);
@@ -87,8 +100,38 @@ __global__ __launch_bounds__(256) void gdn_decode_kernel(DecodeArgs a) {
     IO* out = static_cast<IO*>(a.out);
     ST* state = static_cast<ST*>(a.state);
 
-    // conv (kernel 4) + SiLU of one channel; shifts the raw token into the conv state
+    // conv (kernel 4) + SiLU of one channel: its history h (the conv state's
+    // rows) and taps w are loaded first, then applied to the raw token x,
+    // which is shifted into the conv state
+    auto conv_load = [&](int ch, float (&h)[kConvK - 1], float (&w)[kConvK]) {
+#pragma unroll
+        for (int j = 0; j < kConvK - 1; ++j)
+            h[j] = cs ? io_to_f32(cs[((size_t)slot * (kConvK - 1) + j) * Cch + ch]) : 0.f;
+#pragma unroll
+        for (int j = 0; j < kConvK; ++j) w[j] = kConv ? io_to_f32(conv_w[(size_t)ch * kConvK + j]) : 0.f;
+    };
+    auto conv_apply = [&](int ch, float x, const float (&h)[kConvK - 1], const float (&w)[kConvK]) -> float {
+        if (cs) {
+#pragma unroll
+            for (int j = 0; j < kConvK - 2; ++j)
+                cs[((size_t)slot * (kConvK - 1) + j) * Cch + ch] = f32_to_io<IO>(h[j + 1]);
+            cs[((size_t)slot * (kConvK - 1) + kConvK - 2) * Cch + ch] = f32_to_io<IO>(x);
+        }
+        if (!kConv) return x;
+        float acc = 0.f;
+#pragma unroll
+        for (int j = 0; j < kConvK - 1; ++j) acc = fmaf(w[j], h[j], acc);
+        acc = fmaf(w[kConvK - 1], x, acc);
+        return silu_f32(acc);
+    };
+    // the same in one piece; an fp32 state loads the taps after the conv
+    // state is shifted (the bf16 state's order ran slower with it)
     auto conv_channel = [&](int ch, float x) -> float {
+        if (sizeof(ST) == 2) {
+            float h[kConvK - 1], w[kConvK];
+            conv_load(ch, h, w);
+            return conv_apply(ch, x, h, w);
+        }
         float h[kConvK - 1];
 #pragma unroll
         for (int j = 0; j < kConvK - 1; ++j)
@@ -107,14 +150,43 @@ __global__ __launch_bounds__(256) void gdn_decode_kernel(DecodeArgs a) {
         return silu_f32(acc);
     };
 
-    // q and k of key head hk
+    // q and k of key head hk.  With a bf16 state their loads go out first,
+    // then the first value head's state rows: the memory counters retire in
+    // order, so the waits of the conv below do not cover the rows, which
+    // stream in while the conv, the normalisation and the first head's v and
+    // z are formed (C4b, 256 sequences: 104.6 us against 106.7).  An fp32
+    // state, twice the bytes per row in flight, ran slower that way (200.7
+    // against 194.0) and loads its rows in the head loop.
+    constexpr bool kEarly = sizeof(ST) == 2;
+    const int l16 = tid & 15, rbase = tid >> 4;   // 16 lanes per state row, 8 dk each
+    RawRow<ST> R[8];   // the current value head's rows, widened one at a time when used
     {
         const int which = tid >> 7, i = tid & (kD - 1);
         const int ch = which * a.Hk * kD + hk * kD + i;
         const float x = io_to_f32((which ? k : q)[((size_t)n * a.Hk + hk) * kD + i]);
-        s_qk[tid] = conv_channel(ch, x);
+        if (kEarly) {
+            float h[kConvK - 1], w[kConvK];
+            conv_load(ch, h, w);
+            asm volatile("" ::: "memory");
+            const ST* srow = state + (((size_t)slot * a.Hv + hk * group) * kD) * kD;
+#pragma unroll
+            for (int p = 0; p < 8; ++p) R[p].load(srow + (size_t)(rbase + 16 * p) * kD, l16);
+            asm volatile("" ::: "memory");
+            s_qk[tid] = conv_apply(ch, x, h, w);
+        } else {
+            s_qk[tid] = conv_channel(ch, x);
+        }
     }
-    __syncthreads();
+    if (kEarly) {
+        // s_qk is complete once each wave's LDS writes are (lgkmcnt(0)); a
+        // bare barrier, so that the state rows stay in flight
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // vmcnt(63) expcnt(7) lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    } else {
+        __syncthreads();
+    }
 
     // L2 normalisation factors and k.q (every wave computes them)
     const int lane = tid & 63;
@@ -130,7 +202,6 @@ __global__ __launch_bounds__(256) void gdn_decode_kernel(DecodeArgs a) {
         }
     }
     rq *= a.scale;
-    const int l16 = tid & 15, rbase = tid >> 4;   // 16 lanes per state row, 8 dk each
     float kf[8], qf[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -159,26 +230,45 @@ __global__ __launch_bounds__(256) void gdn_decode_kernel(DecodeArgs a) {
         const float bb = a.beta[(size_t)n * a.Hv + h];
 
         ST* srow = state + (((size_t)slot * a.Hv + h) * kD) * kD;
+        // bf16: raw rows, widened one at a time when used (the first head's
+        // are in flight since the prologue); fp32: rows loaded as they are
         float Sr[8][8];
+        if (kEarly) {
+            if (vh > 0) {
 #pragma unroll
-        for (int p = 0; p < 8; ++p) load_row8(srow + (size_t)(rbase + 16 * p) * kD, l16, Sr[p]);
+                for (int p = 0; p < 8; ++p) R[p].load(srow + (size_t)(rbase + 16 * p) * kD, l16);
+            }
+        } else {
+#pragma unroll
+            for (int p = 0; p < 8; ++p) {
+                R[p].load(srow + (size_t)(rbase + 16 * p) * kD, l16);
+                R[p].widen(Sr[p]);
+            }
+        }
         __syncthreads();   // s_v, s_zw ready
 
 #pragma unroll
         for (int p = 0; p < 8; ++p) {
             const int i = rbase + 16 * p;
+            float Sp[8];
+            if (kEarly) {
+                R[p].widen(Sp);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) Sp[e] = Sr[p][e];
+            }
             float dk = 0.f, dq = 0.f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                dk = fmaf(Sr[p][e], kf[e], dk);
-                dq = fmaf(Sr[p][e], qf[e], dq);
+                dk = fmaf(Sp[e], kf[e], dk);
+                dq = fmaf(Sp[e], qf[e], dq);
             }
             dk = sum16(dk);
             dq = sum16(dq);
             const float u = bb * (s_v[i] - aa * dk);
             float nr[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) nr[e] = fmaf(aa, Sr[p][e], u * kf[e]);
+            for (int e = 0; e < 8; ++e) nr[e] = fmaf(aa, Sp[e], u * kf[e]);
             store_row8(srow + (size_t)i * kD, l16, nr);
             if (l16 == 0) s_o[i] = fmaf(aa, dq, u * kq);
         }
