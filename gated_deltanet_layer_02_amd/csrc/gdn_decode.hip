@@ -150,14 +150,14 @@ __global__ __launch_bounds__(256) void gdn_decode_kernel(DecodeArgs a) {
         return silu_f32(acc);
     };
 
-    // q and k of key head hk.  With a bf16 state their loads go out first,
+    // q and k of key head hk.  With a bf16 state (bf16 io, conv) their loads go out first,
     // then the first value head's state rows: the memory counters retire in
     // order, so the waits of the conv below do not cover the rows, which
     // stream in while the conv, the normalisation and the first head's v and
     // z are formed (C4b, 256 sequences: 104.6 us against 106.7).  An fp32
     // state, twice the bytes per row in flight, ran slower that way (200.7
     // against 194.0) and loads its rows in the head loop.
-    constexpr bool kEarly = sizeof(ST) == 2;
+    constexpr bool kEarly = sizeof(ST) == 2 && sizeof(IO) == 2 && kConv;
     const int l16 = tid & 15, rbase = tid >> 4;   // 16 lanes per state row, 8 dk each
     RawRow<ST> R[8];   // the current value head's rows, widened one at a time when used
     {
@@ -214,10 +214,53 @@ __global__ __launch_bounds__(256) void gdn_decode_kernel(DecodeArgs a) {
     for (int e = 0; e < 8; ++e) kq = fmaf(kf[e], qf[e], kq);
     kq = sum16(kq);
 
+    // bf16 state: a head's v / z inputs and its rows are requested while the
+    // previous head's rows are updated (the inputs first, then each row as
+    // soon as the previous head's copy of it is done, in the same registers),
+    // and the barriers between heads wait for LDS only, so the rows stay in
+    // flight across them.  vz_load / vz_apply split the v conv and SiLU(z) of
+    // a head into loads and arithmetic.
+    struct VZ {
+        float x, h[kConvK - 1], w[kConvK];   // v channel tid (tid < kD)
+        float zz, ww;                         // z and norm weight of channel tid - kD
+    };
+    auto vz_load = [&](int h, VZ& t) {
+        if (tid < kD) {
+            const int ch = 2 * a.Hk * kD + h * kD + tid;
+            t.x = io_to_f32(v[((size_t)n * a.Hv + h) * kD + tid]);
+            conv_load(ch, t.h, t.w);
+        } else if (z != nullptr || norm_w != nullptr) {
+            const int i = tid - kD;
+            t.zz = z ? io_to_f32(z[((size_t)n * a.Hv + h) * kD + i]) : 0.f;
+            t.ww = norm_w ? io_to_f32(norm_w[i]) : 1.f;
+        }
+    };
+    auto vz_apply = [&](int h, const VZ& t) {
+        if (tid < kD) {
+            s_v[tid] = conv_apply(2 * a.Hk * kD + h * kD + tid, t.x, t.h, t.w);
+        } else if (z != nullptr || norm_w != nullptr) {
+            s_zw[tid - kD] = (z ? silu_f32(t.zz) : 1.f) * t.ww;
+        }
+    };
+    auto barrier = [&] {
+        if (kEarly) {
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_waitcnt(0xC07F);   // vmcnt(63) expcnt(7) lgkmcnt(0)
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+        } else {
+            __syncthreads();
+        }
+    };
+    VZ vz;
+    if (kEarly) vz_load(hk * group, vz);
+
 #pragma unroll 1
     for (int vh = 0; vh < group; ++vh) {
         const int h = hk * group + vh;
-        if (tid < kD) {
+        if (kEarly) {
+            vz_apply(h, vz);
+        } else if (tid < kD) {
             const int ch = 2 * a.Hk * kD + h * kD + tid;
             s_v[tid] = conv_channel(ch, io_to_f32(v[((size_t)n * a.Hv + h) * kD + tid]));
         } else if (z != nullptr || norm_w != nullptr) {
@@ -233,20 +276,22 @@ __global__ __launch_bounds__(256) void gdn_decode_kernel(DecodeArgs a) {
         // bf16: raw rows, widened one at a time when used (the first head's
         // are in flight since the prologue); fp32: rows loaded as they are
         float Sr[8][8];
-        if (kEarly) {
-            if (vh > 0) {
-#pragma unroll
-                for (int p = 0; p < 8; ++p) R[p].load(srow + (size_t)(rbase + 16 * p) * kD, l16);
-            }
-        } else {
+        if (!kEarly) {
 #pragma unroll
             for (int p = 0; p < 8; ++p) {
                 R[p].load(srow + (size_t)(rbase + 16 * p) * kD, l16);
                 R[p].widen(Sr[p]);
             }
         }
-        __syncthreads();   // s_v, s_zw ready
+        barrier();   // s_v, s_zw ready
 
+        const bool next = kEarly && vh + 1 < group;   // uniform
+        const ST* nrow = state + (((size_t)slot * a.Hv + h + 1) * kD) * kD;
+        if (next) {
+            asm volatile("" ::: "memory");
+            vz_load(h + 1, vz);
+            asm volatile("" ::: "memory");
+        }
 #pragma unroll
         for (int p = 0; p < 8; ++p) {
             const int i = rbase + 16 * p;
@@ -271,8 +316,9 @@ __global__ __launch_bounds__(256) void gdn_decode_kernel(DecodeArgs a) {
             for (int e = 0; e < 8; ++e) nr[e] = fmaf(aa, Sp[e], u * kf[e]);
             store_row8(srow + (size_t)i * kD, l16, nr);
             if (l16 == 0) s_o[i] = fmaf(aa, dq, u * kq);
+            if (next) R[p].load(nrow + (size_t)(rbase + 16 * p) * kD, l16);
         }
-        __syncthreads();   // s_o ready
+        barrier();   // s_o ready
 
         if (tid < 64) {
             const float o0 = s_o[tid], o1 = s_o[64 + tid];
@@ -287,7 +333,7 @@ __global__ __launch_bounds__(256) void gdn_decode_kernel(DecodeArgs a) {
                 dst[64 + tid] = f32_to_io<IO>(o1);
             }
         }
-        __syncthreads();   // before the next head reuses s_v, s_zw, s_o
+        barrier();   // before the next head reuses s_v, s_zw, s_o
     }
 }
 
