@@ -150,13 +150,14 @@ __global__ __launch_bounds__(256) void gdn_decode_kernel(DecodeArgs a) {
         return silu_f32(acc);
     };
 
-    // q and k of key head hk.  With a bf16 state (bf16 io, conv) their loads go out first,
-    // then the first value head's state rows: the memory counters retire in
-    // order, so the waits of the conv below do not cover the rows, which
-    // stream in while the conv, the normalisation and the first head's v and
-    // z are formed (C4b, 256 sequences: 104.6 us against 106.7).  An fp32
-    // state, twice the bytes per row in flight, ran slower that way (200.7
-    // against 194.0) and loads its rows in the head loop.
+    // q and k of key head hk.  With a bf16 state (bf16 io, conv) their loads
+    // go out first, then the first value head's state rows: the memory
+    // counters retire in order, so the waits of the conv below do not cover
+    // the rows, which stream in while the conv, the normalisation and the
+    // first head's v and z are formed (256 sequences, 16 key / 32 value heads:
+    // 104.6 us against 106.7).  An fp32 state, twice the bytes per row in
+    // flight, ran slower that way (200.7 against 194.0) and loads its rows in
+    // the head loop.
     constexpr bool kEarly = sizeof(ST) == 2 && sizeof(IO) == 2 && kConv;
     const int l16 = tid & 15, rbase = tid >> 4;   // 16 lanes per state row, 8 dk each
     RawRow<ST> R[8];   // the current value head's rows, widened one at a time when used
@@ -339,8 +340,8 @@ __global__ __launch_bounds__(256) void gdn_decode_kernel(DecodeArgs a) {
 
 // Workgroups resident per CU.  With an fp32 state each workgroup streams
 // 64 KB per value head; the registers allow four per CU (64 MB of state rows
-// in flight on 256 CUs), which ran slower than two (C4, 256 sequences: 198-200
-// us at four or three, 192-193 us at two, 223 us at one), so the launch
+// in flight on 256 CUs), which ran slower than two (256 sequences, 16 key / 32
+// value heads: 198-200 us at four or three, 192-193 us at two, 223 us at one), so the launch
 // reserves dynamic LDS that lets only two fit in a CU's 160 KB (60 KB each
 // beside the kernel's 2.5 KB of static LDS).  A bf16 state moves half the
 // bytes per workgroup and is fastest at the four the registers allow (106 us;
