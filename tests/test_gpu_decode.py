@@ -72,6 +72,23 @@ def test_decode_variants(Hk, Hv, conv, gate):
     check_decode(p, gs.generate(p))
 
 
+# bf16 state with bf16 io and conv: each head's inputs and rows are loaded
+# while the previous head is updated; one, two and four value heads per key
+# head, the gate on and off, and a state pool through slots.
+@pytest.mark.parametrize("Hk,Hv,gate", [(1, 4, True), (4, 4, True), (2, 4, False)])
+def test_decode_bf16_state_variants(Hk, Hv, gate):
+    p = gs.Problem(f"dec-bf16state-{Hk}x{Hv}{gate}", [1] * 6, Hk=Hk, Hv=Hv, gate=gate, state_dtype=gs.BF16,
+                   init_state_std=0.01, conv_state_std=0.01, seed=24, decode=True)
+    check_decode(p, gs.generate(p))
+
+
+def test_decode_bf16_state_slots():
+    p = gs.Problem("slots-bf16state", [1] * 5, Hk=2, Hv=4, state_dtype=gs.BF16, init_state_std=0.01,
+                   conv_state_std=0.01, seed=25, decode=True)
+    slots = np.array([6, 1, 3, 8, 0], dtype=np.int32)
+    check_decode(p, gs.generate(p), slots=slots, pool=9)
+
+
 def test_decode_steps_equal_prefill_on_gpu():
     """T decode steps through gdn_decode == one gdn_prefill of T tokens."""
     import torch
