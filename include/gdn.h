@@ -29,8 +29,9 @@
  *  - Pointers to tensors are DEVICE pointers owned by the caller.  The library
  *    never allocates or frees device memory and never synchronises (except
  *    gdn_prefill_wait_status, a query that does so by definition); scratch
- *    memory comes from the caller's workspace.  Whatever a call leaves behind
- *    on the device lives in the caller's buffers; the host side keeps only
+ *    memory comes from the caller's workspace (gdn_prefill_static: a static
+ *    array inside the library, below).  Whatever a call leaves behind on the
+ *    device lives in the caller's buffers (or that array); the host side keeps only
  *    thread-safe caches (CU counts per device, an epoch counter).  Concurrent
  *    calls on different streams are safe when their buffers (workspaces
  *    included) do not overlap.
