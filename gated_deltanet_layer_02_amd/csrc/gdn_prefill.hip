@@ -1343,7 +1343,8 @@ __device__ __forceinline__ void sweep_wg(const SweepArgs& a, int x, unsigned cha
             sweep_issue_part<SW, NT, PW, false>(a, c * a.Hk + hk, c * a.Hv + h, sg, p, lane, B[jj & 1]);
         };
         constexpr int kA = kSplitA / PW, kB = kSplitB / PW;   // copies per wave and part
-        static_assert(kA == 10 && kB == 6, "the wait counts below");
+        constexpr int kS = 64 * (L::kRows / 8) / (64 * PW);   // 16-byte output stores per lane and chunk
+        static_assert(kA == 10 && kB == 6 && kS == 2, "the wait counts below");
         if (q.nch > 0) {
             issueA(0);
             issueB(0);
@@ -1352,11 +1353,11 @@ __device__ __forceinline__ void sweep_wg(const SweepArgs& a, int x, unsigned cha
         // Per iteration j: wait for A_j, barrier; copy B_{j+1}; store the
         // output of chunk j - 3; wait for B_j, barrier; copy A_{j+2}.  Loads
         // and stores retire in order, so each wait allows exactly what was
-        // issued after the part it waits for: before A_j, B_j (6), the stores
-        // of iteration j - 1 (2, from j = 4 on) and A_{j+1} (10); before B_j,
+        // issued after the part it waits for: before A_j, B_j (kB), the stores
+        // of iteration j - 1 (kS, from j = 4 on) and A_{j+1} (kA); before B_j,
         // those stores, A_{j+1}, B_{j+1} and this iteration's stores (from j = 3).
         for (int j = 0; j < q.nch; ++j) {
-            if (j >= 4) __builtin_amdgcn_s_waitcnt(vm_wait(kB + 2 + kA));
+            if (j >= 4) __builtin_amdgcn_s_waitcnt(vm_wait(kB + kS + kA));
             else __builtin_amdgcn_s_waitcnt(vm_wait(kB + kA));
             __builtin_amdgcn_s_barrier();   // part A of chunk j is in place
             asm volatile("" ::: "memory");
@@ -1366,8 +1367,8 @@ __device__ __forceinline__ void sweep_wg(const SweepArgs& a, int x, unsigned cha
                 store_staged<SW, NT, PW, false, true>(a, slot(j - 3), q.seq_start + (j - 3) * kChunk, kChunk, h, sg,
                                                       p, lane);
             asm volatile("" ::: "memory");
-            if (j >= 4) __builtin_amdgcn_s_waitcnt(vm_wait(2 + kA + kB + 2));
-            else if (j == 3) __builtin_amdgcn_s_waitcnt(vm_wait(kA + kB + 2));
+            if (j >= 4) __builtin_amdgcn_s_waitcnt(vm_wait(kS + kA + kB + kS));
+            else if (j == 3) __builtin_amdgcn_s_waitcnt(vm_wait(kA + kB + kS));
             else __builtin_amdgcn_s_waitcnt(vm_wait(kA + kB));
             __builtin_amdgcn_s_barrier();   // part B of chunk j is in place; part A of chunk j was read
             asm volatile("" ::: "memory");
