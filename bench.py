@@ -230,6 +230,18 @@ def bench_decode(args, hip, cfg):
         dc.run(stream=stream)
     torch.cuda.synchronize()
     reps = max(5, args.steps)
+    # the decode loop: `reps` steps back to back between two events on the
+    # stream (as the prefill line times its steps), then the same steps with
+    # an event between every two calls for the per-call median
+    ev0, ev1 = hip.event(), hip.event()
+    hip.record(ev0, stream)
+    for i in range(reps):
+        dc.run(stream=stream)
+    hip.record(ev1, stream)
+    torch.cuda.synchronize()
+    t = hip.ms(ev0, ev1) * 1e-3 / reps
+    hip.destroy(ev0)
+    hip.destroy(ev1)
     evs = [hip.event() for _ in range(reps + 1)]
     hip.record(evs[0], stream)
     for i in range(reps):
@@ -239,13 +251,16 @@ def bench_decode(args, hip, cfg):
     times = sorted(hip.ms(evs[i], evs[i + 1]) for i in range(reps))
     for e in evs:
         hip.destroy(e)
-    t = times[len(times) // 2] * 1e-3
+    t_call = times[len(times) // 2] * 1e-3
     sb = 2 if p.state_dtype == gs.BF16 else 4
     state_bytes = 2 * p.N * p.Hv * D * D * sb
     other = (2 * p.N * p.Hk * D + 3 * p.N * p.Hv * D) * 2 + 2 * p.N * p.Hv * 4 \
         + 2 * p.N * 3 * p.Cch * 2 + p.Cch * 4 * 2
     traffic = measured_traffic("decode_" + p.state_dtype)
     return {"state_dtype": p.state_dtype, "us": round(t * 1e6, 2),
+            "timing": f"{reps} decode steps back to back between two events on the stream",
+            "us_per_call_median": round(t_call * 1e6, 2),
+            "frac_per_call_median": round((state_bytes + other) / t_call / HBM_PEAK, 4),
             "state_GBps": round(state_bytes / t / 1e9, 1),
             "total_GBps": round((state_bytes + other) / t / 1e9, 1),
             "tokens_per_s": round(p.N / t, 1),
