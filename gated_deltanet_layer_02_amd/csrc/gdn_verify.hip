@@ -26,7 +26,11 @@ __device__ __forceinline__ float wave_sum(float x) {
 }
 
 // 8 dk elements of a state row per lane, each load / store instruction
-// covering contiguous bytes (fp32: two 256 B halves; bf16: one 256 B row)
+// covering contiguous bytes (fp32: two 256 B halves; bf16: one 256 B row).
+// The cached state is read once and every checkpoint written once per call;
+// bf16 rows go through nontemporal loads and stores (256 sequences x 4 draft
+// tokens: 287 us against 302), fp32 rows through plain ones (nontemporal:
+// 553 us against 541).
 __device__ __forceinline__ int row_dk(const float*, int l16, int e) {
     return e < 4 ? 4 * l16 + e : 64 + 4 * l16 + (e - 4);
 }
@@ -38,7 +42,7 @@ __device__ __forceinline__ void row_load(const float* row, int l16, float* o) {
     for (int e = 0; e < 4; ++e) { o[e] = a[e]; o[4 + e] = b[e]; }
 }
 __device__ __forceinline__ void row_load(const uint16_t* row, int l16, float* o) {
-    const u16x8 v = reinterpret_cast<const u16x8*>(row)[l16];
+    const u16x8 v = __builtin_nontemporal_load(reinterpret_cast<const u16x8*>(row) + l16);
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = bf16_bits_to_f32(v[e]);
 }
@@ -50,7 +54,7 @@ __device__ __forceinline__ void row_store(uint16_t* row, int l16, const float* x
     u16x8 v;
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = f32_to_bf16_bits(x[e]);
-    reinterpret_cast<u16x8*>(row)[l16] = v;
+    __builtin_nontemporal_store(v, reinterpret_cast<u16x8*>(row) + l16);
 }
 
 }  // namespace
