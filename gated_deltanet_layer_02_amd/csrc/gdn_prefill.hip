@@ -1604,8 +1604,21 @@ __global__ __launch_bounds__(256) void gdn_gated_norm_kernel(IO* __restrict__ ou
          row += (int64_t)gridDim.x * 16) {
         IO* o = out + row * kD + 8 * l16;
         float x[8], zz[8];
-        load8(o, x);
-        load8(z + row * kD + 8 * l16, zz);
+        // bf16 rows are read and written once: nontemporal loads and stores
+        // (16 packed sequences of the 16 key / 32 value head layer: 253 us
+        // against 274)
+        if constexpr (sizeof(IO) == 2) {
+            const u16x8 ov = __builtin_nontemporal_load(reinterpret_cast<const u16x8*>(o));
+            const u16x8 zv = __builtin_nontemporal_load(reinterpret_cast<const u16x8*>(z + row * kD + 8 * l16));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                x[e] = bf16_bits_to_f32(ov[e]);
+                zz[e] = bf16_bits_to_f32(zv[e]);
+            }
+        } else {
+            load8(o, x);
+            load8(z + row * kD + 8 * l16, zz);
+        }
         float ss = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
@@ -1613,7 +1626,14 @@ __global__ __launch_bounds__(256) void gdn_gated_norm_kernel(IO* __restrict__ ou
         const float r = rsqrt_f32(ss * (1.0f / kD) + eps);
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[e] = x[e] * r * w[e] * silu_f32(zz[e]);
-        store8(o, x);
+        if constexpr (sizeof(IO) == 2) {
+            u16x8 v;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = f32_to_bf16_bits(x[e]);
+            __builtin_nontemporal_store(v, reinterpret_cast<u16x8*>(o));
+        } else {
+            store8(o, x);
+        }
     }
 }
 
