@@ -4,6 +4,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <atomic>
 #include <chrono>
 #include <random>
@@ -82,6 +83,7 @@ PrefillLayout prefill_layout(const gdn_desc* d, bool varlen) {
     auto take = [&](size_t bytes) { size_t at = off; off = round_up(off + bytes, 256); return at; };
     L.status = take(gdn::kStatusBytes);   // offset 0, whatever the descriptor
     L.chunk_off = take(sizeof(int32_t) * ((size_t)d->num_seqs + 1));
+    L.order = take(sizeof(int32_t) * std::min<size_t>(d->num_seqs, gdn::kOrderMaxSeqs));
     L.KB = take(C * Hk * gdn::kKBUnits * frag);
     L.VB = take(C * Hv * gdn::kVBUnits * frag);
     L.ready = take(C * Hk * sizeof(uint64_t));
@@ -180,6 +182,7 @@ gdn_status prefill_impl(const gdn_desc* d, const gdn_prefill_args& x, hipStream_
     s.snap_every = snaps ? x.snapshot_every : 0;
     s.slots = x.state_slots; s.state_bf16 = d->state_dtype == GDN_BF16 ? 1 : 0;
     s.out = x.out; s.cu = x.cu_seqlens; s.chunk_off = a.chunk_off;
+    s.order = varlen && N <= gdn::kOrderMaxSeqs ? reinterpret_cast<int32_t*>(ws + L.order) : nullptr;
     s.T = a.T; s.N = a.N; s.Hk = a.Hk; s.Hv = a.Hv;
 
     p.sync.ready = reinterpret_cast<uint64_t*>(ws + L.ready);

@@ -58,8 +58,14 @@ struct SweepArgs {
     const int32_t* slots; int32_t state_bf16;
     void* out;
     const int32_t* cu; const int32_t* chunk_off;
+    // separate launches of packed sequences: order[i] = the sequence with the
+    // i-th most chunks, whose workgroups come i-th in the sweep's grid (NULL:
+    // sequence order)
+    const int32_t* order;
     int32_t T, N, Hk, Hv;
 };
+// sequences up to which the chunk table also orders them by length
+constexpr int kOrderMaxSeqs = 1024;
 
 struct ConvStateArgs {
     const void* q; const void* k; const void* v;
@@ -123,7 +129,7 @@ struct PrefillPlan {
 // The first 256 bytes hold the call status words (SweepArgs::status), at the
 // same offset for every descriptor so that gdn_prefill_wait_status finds them.
 struct PrefillLayout {
-    size_t status, chunk_off, KB, VB, ready, oready, xcc, total;
+    size_t status, chunk_off, order, KB, VB, ready, oready, xcc, total;
 };
 constexpr size_t kStatusBytes = 256;
 

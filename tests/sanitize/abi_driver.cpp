@@ -60,6 +60,7 @@ hipError_t launch_prefill(const PrefillPlan& p, hipStream_t, KernelRecorder&) {
     const Region regions[] = {
         {p.sweep.status, kStatusBytes},
         {p.prep.chunk_off, p.prep.chunk_off ? sizeof(int32_t) * (N + 1) : 0},
+        {p.sweep.order, p.sweep.order ? sizeof(int32_t) * N : 0},
         {p.prep.KB, C * Hk * kKBUnits * frag},
         {p.prep.VB, C * Hv * kVBUnits * frag},
         {p.sync.ready, C * Hk * sizeof(uint64_t)},
@@ -73,6 +74,7 @@ hipError_t launch_prefill(const PrefillPlan& p, hipStream_t, KernelRecorder&) {
     CHECK((const char*)p.sweep.status == g_ws);   // status words at offset 0
     CHECK(p.sweep.epoch != 0 && (p.sweep.epoch & 1) == 0 && p.sync.epoch == p.sweep.epoch);
     CHECK(p.prep.KB == p.sweep.KB && p.prep.VB == p.sweep.VB);
+    CHECK(p.sweep.order == nullptr || (p.prep.cu != nullptr && N <= (size_t)kOrderMaxSeqs));
     return hipSuccess;
 }
 hipError_t launch_decode(const DecodeArgs&, bool, bool, bool, hipStream_t) { ++g_decodes; return hipSuccess; }

@@ -166,16 +166,18 @@ def test_pipeline_c1_shape():
 def _kept_units(call):
     """Prep units of the last (bf16) call whose fragments stayed in an XCD's L2:
     their ready flag is the call's epoch + 1.  Reads the flags where the
-    workspace keeps them: after the call status words, the chunk offsets, KB (32 units of 1 KB per
-    chunk slot and key head) and VB (40 per chunk slot and value head), each
-    region rounded up to 256 bytes; chunk slots = T / 64 + N with cu_seqlens,
-    ceil(T / 64) without.  The output flags that follow all hold the epoch."""
+    workspace keeps them: after the call status words, the chunk offsets, the
+    sweep order (min(N, 1024) int32), KB (32 units of 1 KB per chunk slot and
+    key head) and VB (40 per chunk slot and value head), each region rounded
+    up to 256 bytes; chunk slots = T / 64 + N with cu_seqlens, ceil(T / 64)
+    without.  The output flags that follow all hold the epoch."""
     import torch
     w = call.workspace.view(torch.int64).cpu().numpy().view(np.uint64)
     C = call.T // 64 + call.N if call.cu is not None else -(-call.T // 64)
     r256 = lambda n: (n + 255) // 256 * 256
-    # the call status words (256 bytes), the chunk offsets, KB, VB
-    off = 256 + r256(4 * (call.N + 1)) + r256(C * call.Hk * 32 * 1024) + r256(C * call.Hv * 40 * 1024)
+    # the call status words (256 bytes), the chunk offsets, the sweep order, KB, VB
+    off = 256 + r256(4 * (call.N + 1)) + r256(4 * min(call.N, 1024)) + r256(C * call.Hk * 32 * 1024) \
+        + r256(C * call.Hv * 40 * 1024)
     ready = w[off // 8: off // 8 + C * call.Hk]
     off += r256(C * call.Hk * 8)
     published = -(-call.T // 64) * call.Hv * 8
