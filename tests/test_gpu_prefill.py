@@ -82,6 +82,17 @@ def test_many_short_sequences_qwen_shape():
     say(f"short sequences {check_prefill(p, gs.generate(p), batch=16)}")
 
 
+@pytest.mark.parametrize("N", [1024, 1500])
+def test_many_sequences_chunk_table(N):
+    """1,024 packed sequences (the most the chunk table orders by length) and
+    1,500 (sequence order, and a chunk-offset scan over two blocks of 1,024),
+    lengths 0 to 200 tokens, 2 key / 4 value heads."""
+    rng = np.random.default_rng(N)
+    lens = [int(x) for x in rng.choice([0, 1, 5, 63, 64, 65, 127, 130, 200], size=N)]
+    p = small(f"many-seqs-{N}", lens, init_state_std=0.01, conv_state_std=0.01)
+    say(f"{N} sequences, {sum(lens)} tokens {check_prefill(p, gs.generate(p))}")
+
+
 # Full sizes, every value head against the oracle (the bench's launch
 # configuration: plain calls, which take the pipelined form for C1 and C2 and
 # separate launches for C3).
