@@ -18,12 +18,17 @@
 // and the fp32 state never leaves the wave's registers.
 //
 // Kernels, in stream order:
-//   gdn_chunk_table_kernel      chunk offsets of packed sequences (varlen only)
+//   gdn_chunk_table_kernel      chunk offsets of packed sequences, and their
+//                               order by length for the sweep (varlen only)
 //   gdn_chunk_prep_kernel       conv + SiLU + L2 + scale; gates; K K^T, Q K^T;
 //                               T = (I + A)^-1; W, U~, P as MFMA fragments
 //   gdn_state_sweep_*_kernel    sequential chunk sweep; writes O, final states
 //   gdn_gated_norm_kernel       z-gated RMSNorm of O, in place (when gated)
 //   gdn_conv_state_kernel       conv state out (when requested)
+// or, for the bf16 layer when the sweep needs at most half of the CUs (one or
+// two long sequences at 16 key heads), after the chunk table:
+//   gdn_prefill_pipe_kernel     prep, sweep, gated norm and conv state in one
+//                               launch, the sweep waiting on per-chunk flags
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
