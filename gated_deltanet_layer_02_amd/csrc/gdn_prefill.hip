@@ -860,10 +860,33 @@ template <class IO> constexpr unsigned prep_smem_bytes() {
     return prep_lean<IO>() ? sizeof(PrepSmemLean) : sizeof(PrepSmem<typename MathOf<IO>::T>);
 }
 
+// Grid: one workgroup per (chunk slot, key head), slots * Hk of them in one
+// dimension.  Workgroup w runs on XCD w mod 8, and the key heads of a chunk
+// are dealt to one XCD: the g and beta of a token are one row over all value
+// heads (128 bytes at 32 heads) of which a unit reads two values, so that
+// XCD's L2 fetches each row once per chunk instead of once per key head
+// (16 packed sequences of the 16 key / 32 value head layer: the prep reads
+// 1.11 GB instead of 1.50, the call takes 1.332 ms against 1.350).  Whole
+// groups of 8 chunks take XCD slot s = w / 8 to (chunk 8 (s / Hk) + w mod 8,
+// key head s mod Hk); the chunks past the last whole group go chunk-major.
+__device__ __forceinline__ void prep_slot(int w, int slots, int Hk, int& c, int& hk) {
+    const int grouped = (slots / 8) * 8 * Hk;
+    if (w < grouped) {
+        const int s = w >> 3;
+        c = 8 * (s / Hk) + (w & 7);
+        hk = s % Hk;
+    } else {
+        c = w / Hk;
+        hk = w % Hk;
+    }
+}
+
 template <class IO, bool kConv, bool kNT = false>
-__global__ __launch_bounds__(256, prep_lean<IO>() ? 3 : 2) void gdn_chunk_prep_kernel(PrepArgs a) {
+__global__ __launch_bounds__(256, prep_lean<IO>() ? 3 : 2) void gdn_chunk_prep_kernel(PrepArgs a, int32_t slots) {
     extern __shared__ __attribute__((aligned(16))) unsigned char gdn_prep_smem[];
-    prep_unit<IO, kConv, false, prep_lean<IO>(), kNT>(a, blockIdx.x, blockIdx.y, gdn_prep_smem, threadIdx.x);
+    int c, hk;
+    prep_slot(blockIdx.x, slots, a.Hk, c, hk);
+    prep_unit<IO, kConv, false, prep_lean<IO>(), kNT>(a, c, hk, gdn_prep_smem, threadIdx.x);
 }
 
 // ===========================================================================
@@ -880,6 +903,7 @@ __global__ __launch_bounds__(256, prep_lean<IO>() ? 3 : 2) void gdn_chunk_prep_k
 // LDS units of one chunk buffer: KB (Q, K^T), VB units 0..23 (W, P, gates),
 // then the U~ units of the workgroup's tiles.
 constexpr int kLdsQ = 0, kLdsKT = 16, kLdsW = 32, kLdsP = 48, kLdsG = 54, kLdsU = 56;
+static_assert(kLdsG == kLdsW + kVB_G && kVB_G + 2 == kVB_U, "VB unit 23, after the gates, is unused");
 // After the two operand buffers: three O staging slots.  A slot holds one
 // chunk's output of the workgroup's dv rows, dv-major ([rows][64 tokens],
 // row stride kStageLd bf16 = 136 B, so that the compute waves' 8-byte writes
@@ -1180,7 +1204,12 @@ __device__ __forceinline__ void sweep_issue(const SweepArgs& a, size_t ck, size_
         const int u0 = i * PW;
         const char* src = u0 < kLdsW ? kb + u0 * 1024 : u0 < kLdsU ? vb + (u0 - kLdsW) * 1024
                                                                    : ub + (u0 - kLdsU) * 1024;
-        __builtin_amdgcn_global_load_lds(src + lo, buf + (u0 + p) * 64, 16, 0, kAux);
+        // VB unit 23 holds nothing: the copy into its LDS unit (read by no
+        // one) takes the gates unit again, which the same step's copy of it
+        // brings into L2, so every producer still issues the same number of
+        // copies and no memory is read for it
+        const uint32_t off = u0 + p == kLdsG + 1 ? lo - 1024u : lo;
+        __builtin_amdgcn_global_load_lds(src + off, buf + (u0 + p) * 64, 16, 0, kAux);
     }
 }
 
@@ -1198,6 +1227,7 @@ constexpr int kSplitA = 40, kSplitB = 24;
 constexpr int vm_wait(int n) { return 0x0070 | (n & 0xF) | ((n >> 4) << 14); }
 static_assert(vm_wait(2) == 0x0072 && vm_wait(16) == 0x4070, "s_waitcnt encoding");
 constexpr int kSpQ = 0, kSpW = 16, kSpU = 32, kSpKT = 0, kSpP = 16, kSpG = 22;
+static_assert(kSpG == kSpP + kVB_G - kVB_P && kSplitB == kSpG + 2, "part B ends with the gates and VB unit 23");
 static_assert(2 * (kSplitA + kSplitB) * 1024 == SweepLds<4, 1>::kOps, "the split buffers fill the operand LDS");
 
 // One chunk of a compute wave: wait until the producers' copies of its
@@ -1267,7 +1297,10 @@ __device__ __forceinline__ void sweep_issue_part(const SweepArgs& a, size_t ck, 
                                                                : ub + (u0 - kSpU) * 1024;
         else
             src = u0 < kSpP ? kb + (kKB_KT + u0) * 1024 : vb + (kVB_P + u0 - kSpP) * 1024;   // P, then gates
-        __builtin_amdgcn_global_load_lds(src + lo, buf + (u0 + p) * 64, 16, 0, 0);
+        // the unit after the gates (VB unit 23) holds nothing: copy the gates
+        // unit again from L2 instead (same copy count for every producer)
+        const uint32_t off = !kPartA && u0 + p == kSpG + 1 ? lo - 1024u : lo;
+        __builtin_amdgcn_global_load_lds(src + off, buf + (u0 + p) * 64, 16, 0, 0);
     }
 }
 
@@ -2081,9 +2114,12 @@ static hipError_t launch_prep(const PrefillPlan& p, int slots, hipStream_t s) {
     const bool nt = sizeof(IO) == 2 && sweep_blocks(p) > device_cus();
     auto kern = p.conv ? (nt ? gdn_chunk_prep_kernel<IO, true, sizeof(IO) == 2> : gdn_chunk_prep_kernel<IO, true>)
                        : (nt ? gdn_chunk_prep_kernel<IO, false, sizeof(IO) == 2> : gdn_chunk_prep_kernel<IO, false>);
+    // one grid dimension: at most 2^32 - 1 work-items (256 per workgroup)
+    const int64_t units = (int64_t)slots * p.prep.Hk;
+    if (units > (int64_t)(UINT32_MAX / 256)) return hipErrorInvalidConfiguration;
     hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(kern), smem);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(slots, p.prep.Hk), dim3(256), smem, s, p.prep);
+    hipLaunchKernelGGL(kern, dim3((uint32_t)units), dim3(256), smem, s, p.prep, slots);
     return hipGetLastError();
 }
 
