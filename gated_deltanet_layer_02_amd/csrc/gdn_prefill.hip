@@ -478,10 +478,12 @@ __device__ __forceinline__ bool prep_unit(const PrepArgs& a, int c, int hk, unsi
     // interior chunk: the conv window of every token lies inside the sequence,
     // so the separate prep kernel loads rows without per-row checks (uniform;
     // 16 sequences of the 16 key / 32 value head layer: 1.465 ms per call
-    // against 1.491).  Units of the pipelined launch keep the checked loads:
-    // there the unchecked ones made a 65,536-token call 2.15 ms against 1.82.
+    // against 1.491).  So do the full units of the pipelined launch (4,096
+    // tokens: 118.2 us against 121.1); its lean units keep the checked loads:
+    // at 65,536 tokens the unchecked ones sped the units up but slowed the
+    // sweep's 1,024-step chain beside them (2.14 ms per call against 1.84).
     const bool in_seq = t0 - 3 >= seq_start && len == kChunk;
-    const bool interior = !kCo && in_seq;
+    const bool interior = !(kCo && kLean) && in_seq;
     const bool inner = !kLean && sizeof(IO) == 2 && in_seq;   // uniform
     Quad<IO, kConv> xv;        // raw v rows of the next value head
     float gl = 0.f, bl = 0.f;  // its g and beta (wave 0, lane = token)
