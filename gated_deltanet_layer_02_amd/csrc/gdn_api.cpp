@@ -43,7 +43,7 @@ gdn_status check_desc_common(const gdn_desc* d) {
     if (d->head_k_dim != gdn::kD || d->head_v_dim != gdn::kD) return GDN_ERR_UNSUPPORTED;
     if (d->conv_kernel != gdn::kConvK) return GDN_ERR_UNSUPPORTED;
     if (d->flags & ~(GDN_FLAG_L2NORM_QK | GDN_FLAG_SEPARATE_LAUNCHES | GDN_FLAG_PREP_WRITE_BACK |
-                     GDN_FLAG_TEST_WAITS_GIVE_UP))
+                     GDN_FLAG_TEST_WAITS_GIVE_UP | GDN_FLAG_SEGMENTS))
         return GDN_ERR_UNSUPPORTED;
     if (d->io_dtype != GDN_F32 && d->io_dtype != GDN_BF16) return GDN_ERR_BAD_DTYPE;
     if (d->state_dtype != GDN_F32 && d->state_dtype != GDN_BF16) return GDN_ERR_BAD_DTYPE;
@@ -89,6 +89,14 @@ PrefillLayout prefill_layout(const gdn_desc* d, bool varlen) {
     L.ready = take(C * Hk * sizeof(uint64_t));
     L.oready = take(C * Hv * 8 * sizeof(uint64_t));
     L.xcc = take((size_t)d->num_seqs * Hv * (gdn::kD / 16) * sizeof(uint64_t));   // <= one per 16 dv rows
+    if ((d->flags & GDN_FLAG_SEGMENTS) && d->num_seqs == 1) {
+        // segment-parallel form, sized for the most segments: finals and maps,
+        // start states, identity-chain outputs of every token
+        const size_t st = Hv * gdn::kD * gdn::kD * sizeof(float);
+        L.seg_state = take((2 * gdn::kSegMax - 1) * st);
+        L.seg_x = take((gdn::kSegMax - 1) * st);
+        L.seg_out = take((size_t)d->total_tokens * Hv * gdn::kD * 2);
+    }
     L.total = off;
     return L;
 }
@@ -155,6 +163,11 @@ gdn_status prefill_impl(const gdn_desc* d, const gdn_prefill_args& x, hipStream_
     p.io_bf16 = d->io_dtype == GDN_BF16;
     p.allow_pipe = (d->flags & GDN_FLAG_SEPARATE_LAUNCHES) == 0;
     p.l2_handoff = (d->flags & GDN_FLAG_PREP_WRITE_BACK) == 0;
+    p.seg_ok = (d->flags & GDN_FLAG_SEGMENTS) && !varlen && N == 1 && T > 0 && d->io_dtype == GDN_BF16 &&
+               d->state_dtype == GDN_F32 && x.state_slots == nullptr && !snaps && L.seg_state != 0;
+    p.seg_state = p.seg_ok ? reinterpret_cast<float*>(ws + L.seg_state) : nullptr;
+    p.seg_x = p.seg_ok ? reinterpret_cast<float*>(ws + L.seg_x) : nullptr;
+    p.seg_out = p.seg_ok ? ws + L.seg_out : nullptr;
     p.conv = x.conv_w != nullptr;
     p.gated = x.z != nullptr && x.norm_w != nullptr;
     p.total_tokens = T;

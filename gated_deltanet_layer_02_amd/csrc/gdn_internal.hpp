@@ -63,6 +63,33 @@ struct SweepArgs {
     // sequence order)
     const int32_t* order;
     int32_t T, N, Hk, Hv;
+    // Segment-parallel sweep (seg_n > 1: one sequence, no cu, fp32 state, no
+    // slots or snapshots).  Grid sequence n < seg_n is segment n: chunks
+    // [n seg_chunks, (n + 1) seg_chunks), from initial_state (n = 0) or zero,
+    // output to out, final state to seg_state row n.  n >= seg_n is the
+    // identity chain of segment s = n - seg_n + 1: initial state I (row r =
+    // e_r), U~ taken as zero, output to seg_out ([T][Hv][dk] bf16, token
+    // indexed like out), final state (the segment's map Phi) to seg_state row n.
+    void* seg_out; float* seg_state;
+    int32_t seg_n, seg_chunks;
+};
+// Segments per call at most, and the least chunks of a segment.
+constexpr int kSegMax = 8;
+constexpr int kSegMinChunks = 4;
+
+// Composition and output fix-up of the segment-parallel sweep.
+//   seg_state [2 seg_n - 1][Hv][dv][dk] fp32: rows 0..seg_n-1 the segments'
+//             final states from their own start (F_s), rows seg_n.. the maps
+//             Phi_s of segments s = 1..seg_n-1;
+//   seg_x     [seg_n - 1][Hv][dv][dk] fp32: X_s, the state at the start of
+//             segment s (X_1 = F_0, X_{s+1} = F_s + X_s Phi_s); X_{seg_n} is
+//             the final state;
+//   seg_out   the identity chains' outputs r_t: [T][Hv][dk] bf16;
+//   out       o of every token, [T][Hv][dv] bf16, corrected in place.
+struct SegArgs {
+    const float* seg_state; float* seg_x; float* final_state;
+    const void* seg_out; void* out;
+    int32_t T, Hv, seg_n, seg_chunks;
 };
 // sequences up to which the chunk table also orders them by length
 constexpr int kOrderMaxSeqs = 1024;
@@ -116,6 +143,8 @@ struct PrefillPlan {
     bool io_bf16, conv, gated;
     bool allow_pipe;              // the pipelined launch may serve this call
     bool l2_handoff;              // pipelined prep units may leave their results in L2
+    bool seg_ok;                  // the segment-parallel form may serve this call
+    float* seg_state; float* seg_x; void* seg_out;   // its workspace buffers
     int64_t total_tokens;
     int32_t chunk_slots;          // grid rows of the prep kernel
     const void* z; const void* norm_w; float norm_eps;
@@ -129,7 +158,9 @@ struct PrefillPlan {
 // The first 256 bytes hold the call status words (SweepArgs::status), at the
 // same offset for every descriptor so that gdn_prefill_wait_status finds them.
 struct PrefillLayout {
-    size_t status, chunk_off, order, KB, VB, ready, oready, xcc, total;
+    size_t status, chunk_off, order, KB, VB, ready, oready, xcc;
+    size_t seg_state, seg_x, seg_out;   // GDN_FLAG_SEGMENTS with one sequence; else 0
+    size_t total;
 };
 constexpr size_t kStatusBytes = 256;
 

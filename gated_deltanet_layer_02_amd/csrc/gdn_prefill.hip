@@ -1022,6 +1022,15 @@ __device__ __forceinline__ SweepSeq sweep_seq(const SweepArgs& a, int n) {
     q.nch = (q.L + kChunk - 1) / kChunk;
     return q;
 }
+// Segment s of a segment-parallel sweep (one sequence of a.T tokens).
+__device__ __forceinline__ SweepSeq seg_seq(const SweepArgs& a, int s) {
+    SweepSeq q;
+    q.c_begin = s * a.seg_chunks;
+    q.seq_start = q.c_begin * kChunk;
+    q.L = max(0, min(a.T - q.seq_start, a.seg_chunks * kChunk));
+    q.nch = (q.L + kChunk - 1) / kChunk;
+    return q;
+}
 
 // One chunk of the sweep for the NT 16-row tiles of this wave:
 //   U = U~ - W S^T;  O = diag(gamma) Q S^T + P U;  S <- gamma_n S + K^T diag(e) U
@@ -1152,12 +1161,12 @@ __device__ __forceinline__ void stage_o(lds_u16* slot, const f32x4 (&O)[NT][4], 
 // gated norm running in the same launch.
 // kFull: a whole chunk, every lane stores (the producer's wait counts on it).
 template <int SW, int NT, int PW, bool kCo, bool kFull>
-__device__ __forceinline__ void store_staged(const SweepArgs& a, const lds_u16* slot, int t0, int len, int h,
-                                             int sg, int p, int lane) {
+__device__ __forceinline__ void store_staged(const SweepArgs& a, void* out, const lds_u16* slot, int t0, int len,
+                                             int h, int sg, int p, int lane) {
     typedef SweepLds<SW, NT> L;
     constexpr int kPer = L::kRows / 8;                    // pieces per token
     static_assert((64 * kPer) % (64 * PW) == 0, "pieces split evenly over the producers");
-    uint16_t* base = static_cast<uint16_t*>(a.out) + ((size_t)t0 * a.Hv + h) * kD + sg * L::kRows;
+    uint16_t* base = static_cast<uint16_t*>(out) + ((size_t)t0 * a.Hv + h) * kD + sg * L::kRows;
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(base, 0, 0x7fffffff, 0x00020000);
 #pragma unroll
     for (int k = 0; k < 64 * kPer / (64 * PW); ++k) {
@@ -1237,10 +1246,10 @@ static_assert(2 * (kSplitA + kSplitB) * 1024 == SweepLds<4, 1>::kOps, "the split
 // the second part when split, then a second barrier before the second
 // phase).  The previous chunk's output (Oprev) is stored after the barrier,
 // so its stores complete behind this chunk's work.
-template <int SW, int NT, bool kSplit = false>
+template <int SW, int NT, bool kSplit = false, bool kSeg = false>
 __device__ __forceinline__ void sweep_lds_step(int j, int wave, f32x4 (&S)[NT][8], f32x4 (&Oprev)[NT][4],
                                                const lds_b16x8* __restrict__ cur, lds_u16* stage,
-                                               const lds_b16x8* __restrict__ curB = nullptr) {
+                                               const lds_b16x8* __restrict__ curB = nullptr, bool zero_u = false) {
     typedef SweepLds<SW, NT> L;
     const int lane = threadIdx.x & 63, l16 = lane & 15, g4 = lane >> 4;
     __syncthreads();                      // chunk j's operands (its part A) are in cur
@@ -1262,6 +1271,7 @@ __device__ __forceinline__ void sweep_lds_step(int j, int wave, f32x4 (&S)[NT][8
         [&](int f) { F x; x.v = KT[f * 64]; return x; },
         [&](int f) { F x; x.v = P[f * 64]; return x; },
         [&](int nt, int mt) {   // U~ of tile nt, token tile mt (pairs of token tiles per unit)
+            if (kSeg && zero_u) return f32x4{0.f, 0.f, 0.f, 0.f};   // identity chain of a segment
             const bf16x8 u = UU[(2 * nt + (mt >> 1)) * 64];
             const int o = (mt & 1) * 4;
             return f32x4{(float)u[o], (float)u[o + 1], (float)u[o + 2], (float)u[o + 3]};
@@ -1383,10 +1393,11 @@ __device__ __noinline__ bool pipe_wait_all(const uint64_t* f, int count, uint64_
 // copies are in flight, so a published chunk costs no extra round trip) and,
 // for a gated norm in the same launch, publish each chunk's output two
 // iterations after storing it.
-template <int SW, int NT, int PW, bool kPipe, bool kSplit = false>
+template <int SW, int NT, int PW, bool kPipe, bool kSplit = false, bool kSeg = false>
 __device__ __forceinline__ void sweep_wg(const SweepArgs& a, int x, unsigned char* smem, const PipeSync& ps) {
     typedef SweepLds<SW, NT> L;
     static_assert(!kSplit || (!kPipe && SW == 4 && NT == 1 && PW == 4), "split buffers: separate launches");
+    static_assert(!kSeg || (!kPipe && !kSplit), "segments: separate launches, one buffer per chunk");
     lds_b16x8* buf0 = (lds_b16x8*)(smem);   // generic -> LDS address space
     lds_b16x8* buf1 = buf0 + L::kUnits * 64;
     lds_u16* stage = (lds_u16*)(smem + L::kOps);
@@ -1398,7 +1409,11 @@ __device__ __forceinline__ void sweep_wg(const SweepArgs& a, int x, unsigned cha
     // the wave index is uniform; readfirstlane lets the compiler keep it in an SGPR
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63, l16 = lane & 15, g4 = lane >> 4;
-    const SweepSeq q = sweep_seq(a, n);
+    // segments: grid sequence n >= seg_n is the identity chain of segment
+    // n - seg_n + 1, which writes its outputs to seg_out
+    const bool chain = kSeg && n >= a.seg_n;
+    const SweepSeq q = kSeg ? seg_seq(a, chain ? n - a.seg_n + 1 : n) : sweep_seq(a, n);
+    void* const outp = chain ? a.seg_out : a.out;
 
     if (kSplit && wave >= SW) {   // producer, split buffers
         const int p = wave - SW;
@@ -1438,7 +1453,7 @@ __device__ __forceinline__ void sweep_wg(const SweepArgs& a, int x, unsigned cha
             issueB(j + 1);
             asm volatile("" ::: "memory");
             if (j >= 3)
-                store_staged<SW, NT, PW, false, true>(a, slot(j - 3), q.seq_start + (j - 3) * kChunk, kChunk, h, sg,
+                store_staged<SW, NT, PW, false, true>(a, outp, slot(j - 3), q.seq_start + (j - 3) * kChunk, kChunk, h, sg,
                                                       p, lane);
             asm volatile("" ::: "memory");
             if (j >= 4) __builtin_amdgcn_s_waitcnt(vm_wait(kS + kA + kB + kS));
@@ -1452,7 +1467,7 @@ __device__ __forceinline__ void sweep_wg(const SweepArgs& a, int x, unsigned cha
             __syncthreads();
             asm volatile("" ::: "memory");
             for (int jj = q.nch >= 3 ? q.nch - 3 : 0; jj < q.nch; ++jj)
-                store_staged<SW, NT, PW, false, false>(a, slot(jj), q.seq_start + jj * kChunk,
+                store_staged<SW, NT, PW, false, false>(a, outp, slot(jj), q.seq_start + jj * kChunk,
                                                        min(kChunk, q.L - jj * kChunk), h, sg, p, lane);
             __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): no copy lands after the workgroup ends
         }
@@ -1493,7 +1508,7 @@ __device__ __forceinline__ void sweep_wg(const SweepArgs& a, int x, unsigned cha
             // A bare barrier (no fence: a workgroup release would wait for the
             // stores too); the waits before it cover what the consumers read.
             if (j >= 3) {   // staged at step j - 2, complete before the last barrier
-                store_staged<SW, NT, PW, kPipe, true>(a, slot(j - 3), q.seq_start + (j - 3) * kChunk, kChunk, h,
+                store_staged<SW, NT, PW, kPipe, true>(a, outp, slot(j - 3), q.seq_start + (j - 3) * kChunk, kChunk, h,
                                                       sg, p, lane);
                 asm volatile("" ::: "memory");
                 __builtin_amdgcn_s_waitcnt(0x0072);   // vmcnt(2) lgkmcnt(0): the copies have landed
@@ -1512,7 +1527,7 @@ __device__ __forceinline__ void sweep_wg(const SweepArgs& a, int x, unsigned cha
             asm volatile("" ::: "memory");
             if (pub && q.nch >= 5) publish_o(ps, a, (size_t)q.c_begin + q.nch - 5, h, k, lane);
             for (int jj = q.nch >= 3 ? q.nch - 3 : 0; jj < q.nch; ++jj)
-                store_staged<SW, NT, PW, kPipe, false>(a, slot(jj), q.seq_start + jj * kChunk,
+                store_staged<SW, NT, PW, kPipe, false>(a, outp, slot(jj), q.seq_start + jj * kChunk,
                                                        min(kChunk, q.L - jj * kChunk), h, sg, p, lane);
             if (pub) {
                 __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
@@ -1524,15 +1539,28 @@ __device__ __forceinline__ void sweep_wg(const SweepArgs& a, int x, unsigned cha
     }
 
     const int s0 = (sg * SW + wave) * NT;
-    const int row = a.slots ? a.slots[n] : n;   // state pool row
+    const int row = kSeg ? 0 : a.slots ? a.slots[n] : n;   // state pool row
     f32x4 S[NT][8];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         const size_t srow = state_row(a, row, h, s0 + nt, l16);
 #pragma unroll
-        for (int m = 0; m < 8; ++m)
-            S[nt][m] = a.initial_state != nullptr ? state_load4(a.initial_state, a.state_bf16, srow + 16 * m + 4 * g4)
-                                                  : f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int m = 0; m < 8; ++m) {
+            if constexpr (kSeg) {
+                if (chain) {   // S = I: element (dv 16 (s0 + nt) + l16, dk 16 m + 4 g4 + r)
+                    const int d = 16 * (s0 + nt) + l16 - 16 * m - 4 * g4;
+                    S[nt][m] = f32x4{d == 0 ? 1.f : 0.f, d == 1 ? 1.f : 0.f, d == 2 ? 1.f : 0.f, d == 3 ? 1.f : 0.f};
+                } else {
+                    S[nt][m] = a.initial_state != nullptr && n == 0
+                                   ? state_load4(a.initial_state, a.state_bf16, srow + 16 * m + 4 * g4)
+                                   : f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+            } else {
+                S[nt][m] = a.initial_state != nullptr
+                               ? state_load4(a.initial_state, a.state_bf16, srow + 16 * m + 4 * g4)
+                               : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
     }
 
     f32x4 O[NT][4];
@@ -1559,24 +1587,25 @@ __device__ __forceinline__ void sweep_wg(const SweepArgs& a, int x, unsigned cha
     }
 #pragma unroll 1
     for (int j = 0; j < q.nch; j += 2) {
-        sweep_lds_step<SW, NT>(j, wave, S, O, buf0, stage);
-        state_snapshot<NT>(a, n, j, q.nch, h, s0, S, l16, g4);
+        sweep_lds_step<SW, NT, false, kSeg>(j, wave, S, O, buf0, stage, nullptr, chain);
+        if (!kSeg) state_snapshot<NT>(a, n, j, q.nch, h, s0, S, l16, g4);
         if (j + 1 < q.nch) {
-            sweep_lds_step<SW, NT>(j + 1, wave, S, O, buf1, stage);
-            state_snapshot<NT>(a, n, j + 1, q.nch, h, s0, S, l16, g4);
+            sweep_lds_step<SW, NT, false, kSeg>(j + 1, wave, S, O, buf1, stage, nullptr, chain);
+            if (!kSeg) state_snapshot<NT>(a, n, j + 1, q.nch, h, s0, S, l16, g4);
         }
     }
     if (q.nch > 0) {   // stage the last chunk's output for the producers
         stage_o<SW, NT>(stage + ((q.nch - 1) % 3) * (L::kStage / 2), O, wave, l16, g4);
         __syncthreads();
     }
-    if (a.final_state != nullptr) state_put<NT>(a.final_state, a, row, h, s0, S, l16, g4);
+    if (kSeg) state_put<NT>(a.seg_state, a, n, h, s0, S, l16, g4);   // F_s or Phi_s (fp32)
+    else if (a.final_state != nullptr) state_put<NT>(a.final_state, a, row, h, s0, S, l16, g4);
 }
 
-template <int SW, int NT, int PW, bool kSplit>
+template <int SW, int NT, int PW, bool kSplit, bool kSeg = false>
 __global__ __launch_bounds__(64 * (SW + PW)) void gdn_state_sweep_lds_kernel(SweepArgs a) {
     extern __shared__ __attribute__((aligned(16))) unsigned char gdn_sweep_smem[];
-    sweep_wg<SW, NT, PW, false, kSplit>(a, blockIdx.x, gdn_sweep_smem, PipeSync{});
+    sweep_wg<SW, NT, PW, false, kSplit, kSeg>(a, blockIdx.x, gdn_sweep_smem, PipeSync{});
 }
 
 // fp32 operands (the fp32 layer): the chunk's fragments (2 KB units: 8 fp32
@@ -1747,6 +1776,109 @@ __device__ __forceinline__ void conv_state_channel(const ConvStateArgs& a, int n
 template <class IO>
 __global__ __launch_bounds__(256) void gdn_conv_state_kernel(ConvStateArgs a) {
     conv_state_channel<IO>(a, blockIdx.y, blockIdx.x * 256 + threadIdx.x);
+}
+
+// ===========================================================================
+// segment-parallel sweep: the segments' start states and their part of the
+// outputs
+//
+// Over one segment the chunk recurrence is affine in the state on entry:
+// S_end = S_start Phi + F and o_t = o'_t + S_start r_t (rows of S never mix),
+// where the sweep forms F and o'_t from a zero start and Phi and r_t from the
+// identity start with U~ = 0 (SweepArgs, seg_*).  With X_s the state at the
+// start of segment s: X_1 = F_0, X_{s+1} = F_s + X_s Phi_s, and X_P (P
+// segments) is the final state.
+// ===========================================================================
+// Workgroup (h, b) carries rows 16 b .. 16 b + 15 of value head h through the
+// segments one after the other; thread t holds rows 16 b + 2 (t / 32) + {0, 1},
+// columns 4 (t % 32) .. + 3, in fp32 (X_s in LDS while X_s Phi_s is formed).
+__global__ __launch_bounds__(256) void gdn_seg_compose_kernel(SegArgs a) {
+    __shared__ float X[16][kD + 4];
+    const int h = blockIdx.x >> 3, b = blockIdx.x & 7;
+    const int t = threadIdx.x, cq = 4 * (t & 31), r0 = 2 * (t >> 5);
+    auto mat = [&](auto* base, int i) { return base + ((size_t)i * a.Hv + h) * (size_t)(kD * kD); };
+    const size_t o0 = (size_t)(16 * b + r0) * kD + cq, o1 = o0 + kD;
+    f32x4 x0 = *reinterpret_cast<const f32x4*>(mat(a.seg_state, 0) + o0);   // X_1 = F_0
+    f32x4 x1 = *reinterpret_cast<const f32x4*>(mat(a.seg_state, 0) + o1);
+    for (int s = 1;; ++s) {
+        if (s == a.seg_n) {   // x = X_P: the final state
+            if (a.final_state != nullptr) {
+                *reinterpret_cast<f32x4*>(mat(a.final_state, 0) + o0) = x0;
+                *reinterpret_cast<f32x4*>(mat(a.final_state, 0) + o1) = x1;
+            }
+            return;
+        }
+        *reinterpret_cast<f32x4*>(mat(a.seg_x, s - 1) + o0) = x0;   // X_s
+        *reinterpret_cast<f32x4*>(mat(a.seg_x, s - 1) + o1) = x1;
+        *reinterpret_cast<f32x4*>(&X[r0][cq]) = x0;
+        *reinterpret_cast<f32x4*>(&X[r0 + 1][cq]) = x1;
+        __syncthreads();
+        const float* phi = mat(a.seg_state, a.seg_n + s - 1) + cq;   // Phi_s
+        f32x4 y0 = *reinterpret_cast<const f32x4*>(mat(a.seg_state, s) + o0);   // F_s
+        f32x4 y1 = *reinterpret_cast<const f32x4*>(mat(a.seg_state, s) + o1);
+#pragma unroll 8
+        for (int r = 0; r < kD; ++r) {
+            const f32x4 ph = *reinterpret_cast<const f32x4*>(phi + (size_t)r * kD);
+            y0 += X[r0][r] * ph;
+            y1 += X[r0 + 1][r] * ph;
+        }
+        __syncthreads();   // every thread has read X_s
+        x0 = y0;
+        x1 = y1;
+    }
+}
+
+// o_t += X_s r_t for the tokens of segments 1..P-1: workgroup (chunk c of
+// segment s = c / seg_chunks >= 1, value head h), four waves.  As a product,
+// the chunk's o^T (dv x tokens) gains X_s (dv x dk) R^T (dk x tokens), R the
+// identity chain's outputs; wave w forms dv rows 32 w .. 32 w + 31 (two
+// 16-row tiles) for the four 16-token tiles on bf16 MFMA (X_s rounded to
+// bf16), K = dk in four blocks of 32 of which lane (l16, g4) supplies dk
+// 32 p + 8 g4 .. + 7 of its row in both operands.  Accumulator lane (l16, g4)
+// then holds dv 4 g4 .. + 3 of token l16: an 8-byte read-modify-write of o.
+__global__ __launch_bounds__(256) void gdn_seg_fixup_kernel(SegArgs a) {
+    const int c = a.seg_chunks + (int)(blockIdx.x / (unsigned)a.Hv), h = (int)(blockIdx.x % (unsigned)a.Hv);
+    const int s = c / a.seg_chunks;
+    const int t0 = c * kChunk, len = min(kChunk, a.T - t0);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l16 = lane & 15, g4 = lane >> 4;
+    const float* X = a.seg_x + ((size_t)(s - 1) * a.Hv + h) * (size_t)(kD * kD);
+    typedef Frag<bf16> F;
+    F xa[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const float* src = X + (size_t)(32 * wave + 16 * i + l16) * kD + 32 * p + 8 * g4;
+            xa[i][p] = acc_to_frag<bf16>(*reinterpret_cast<const f32x4*>(src),
+                                         *reinterpret_cast<const f32x4*>(src + 4));
+        }
+    const uint16_t* R = static_cast<const uint16_t*>(a.seg_out);
+    uint16_t* O = static_cast<uint16_t*>(a.out);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+        const int tt = 16 * mt + l16;   // token of this lane's B column and accumulator column
+        const bool ok = tt < len;
+        const size_t row = ((size_t)(t0 + tt) * a.Hv + h) * kD;
+        F rb[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            if (ok) rb[p].v = *reinterpret_cast<const bf16x8*>(R + row + 32 * p + 8 * g4);
+            else rb[p].v = bf16x8{};
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int p = 0; p < 4; ++p) mma(acc, xa[i][p], rb[p]);
+            if (ok) {
+                u16x4* op = reinterpret_cast<u16x4*>(O + row + 32 * wave + 16 * i + 4 * g4);
+                u16x4 ov = *op;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) ov[r] = f32_to_bf16_bits(bf16_bits_to_f32(ov[r]) + acc[r]);
+                *op = ov;
+            }
+        }
+    }
 }
 
 // ===========================================================================
@@ -2074,6 +2206,9 @@ static hipError_t allow_dynamic_lds(const void* kern, unsigned bytes) {
     static const hipError_t sweep_split = hipFuncSetAttribute(
         reinterpret_cast<const void*>(gdn_state_sweep_lds_kernel<kSweepSW, kSweepNT, kSweepPW, true>),
         hipFuncAttributeMaxDynamicSharedMemorySize, SweepCfg::kBytes);
+    static const hipError_t sweep_seg = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(gdn_state_sweep_lds_kernel<kSweepSW, kSweepNT, kSweepPW, false, true>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, SweepCfg::kBytes);
     static const hipError_t pipe_conv = hipFuncSetAttribute(
         reinterpret_cast<const void*>(gdn_prefill_pipe_kernel<true, false>),
         hipFuncAttributeMaxDynamicSharedMemorySize, PipeForm<false>::kSmem);
@@ -2092,7 +2227,8 @@ static hipError_t allow_dynamic_lds(const void* kern, unsigned bytes) {
     (void)kern;
     (void)bytes;
     for (hipError_t e : {bf16_conv, bf16_noconv, bf16_conv_nt, bf16_noconv_nt, f32_conv, f32_noconv, sweep,
-                         sweep_split, pipe_conv, pipe_noconv, pipe_conv_lean, pipe_noconv_lean, sweep_f32})
+                         sweep_split, sweep_seg, pipe_conv, pipe_noconv, pipe_conv_lean, pipe_noconv_lean,
+                         sweep_f32})
         if (e != hipSuccess) return e;
     return hipSuccess;
 }
@@ -2130,6 +2266,25 @@ static int sweep_blocks(const PrefillPlan& p) {
     return sweep_grid(p.io_bf16 ? SweepCfg::kGroups : 8 / kF32SW, a.N, a.Hk, a.Hv);
 }
 
+// Segments of a segment-parallel call (GDN_FLAG_SEGMENTS, one qualifying
+// sequence): as many as fit one round of CUs with their identity chains
+// (2 P - 1 sweep sequences), at most kSegMax, each at least kSegMinChunks
+// chunks long; 1 when the form does not apply.  *chunks: chunks per segment
+// (every segment non-empty: P = ceil(C / chunks)).
+static int seg_count(const PrefillPlan& p, int* chunks) {
+    *chunks = p.chunk_slots;
+    if (!p.seg_ok || p.chunk_slots < 2 * kSegMinChunks) return 1;
+    const int cus = device_cus();
+    int best = 1;
+    for (int P = 2; P <= kSegMax; ++P)
+        if (sweep_grid(SweepCfg::kGroups, 2 * P - 1, p.sweep.Hk, p.sweep.Hv) <= cus &&
+            P * kSegMinChunks <= p.chunk_slots)
+            best = P;
+    if (best < 2) return 1;
+    *chunks = (p.chunk_slots + best - 1) / best;
+    return (p.chunk_slots + *chunks - 1) / *chunks;
+}
+
 
 static hipError_t launch_sweep(const PrefillPlan& p, hipStream_t s) {
     const SweepArgs& a = p.sweep;
@@ -2154,6 +2309,56 @@ static hipError_t launch_sweep(const PrefillPlan& p, hipStream_t s) {
             hipLaunchKernelGGL((gdn_state_sweep_lds_kernel<kSweepSW, kSweepNT, kSweepPW, false>), grid, block,
                                SweepCfg::kBytes, s, a);
     }
+    return hipGetLastError();
+}
+
+// Segment-parallel sweep: P segments and P - 1 identity chains in one grid.
+static hipError_t launch_seg_sweep(const PrefillPlan& p, int P, int chunks, hipStream_t s) {
+    SweepArgs a = p.sweep;
+    a.N = 2 * P - 1;
+    a.cu = nullptr;
+    a.chunk_off = nullptr;
+    a.order = nullptr;
+    a.slots = nullptr;
+    a.snap_every = 0;
+    a.state_bf16 = 0;
+    a.seg_n = P;
+    a.seg_chunks = chunks;
+    a.seg_out = p.seg_out;
+    a.seg_state = p.seg_state;
+    const hipError_t e = allow_dynamic_lds(nullptr, 0);
+    if (e != hipSuccess) return e;
+    const int blocks = sweep_grid(SweepCfg::kGroups, a.N, a.Hk, a.Hv);
+    hipLaunchKernelGGL((gdn_state_sweep_lds_kernel<kSweepSW, kSweepNT, kSweepPW, false, true>), dim3(blocks),
+                       dim3(64 * (kSweepSW + kSweepPW)), SweepCfg::kBytes, s, a);
+    return hipGetLastError();
+}
+
+static SegArgs seg_args(const PrefillPlan& p, int P, int chunks) {
+    SegArgs g;
+    g.seg_state = p.seg_state;
+    g.seg_x = p.seg_x;
+    g.final_state = static_cast<float*>(p.sweep.final_state);
+    g.seg_out = p.seg_out;
+    g.out = p.sweep.out;
+    g.T = p.sweep.T;
+    g.Hv = p.sweep.Hv;
+    g.seg_n = P;
+    g.seg_chunks = chunks;
+    return g;
+}
+
+static hipError_t launch_seg_compose(const PrefillPlan& p, int P, int chunks, hipStream_t s) {
+    hipLaunchKernelGGL(gdn_seg_compose_kernel, dim3((unsigned)(8 * p.sweep.Hv)), dim3(256), 0, s,
+                       seg_args(p, P, chunks));
+    return hipGetLastError();
+}
+
+static hipError_t launch_seg_fixup(const PrefillPlan& p, int P, int chunks, hipStream_t s) {
+    const int64_t blocks = (int64_t)(p.chunk_slots - chunks) * p.sweep.Hv;
+    if (blocks <= 0) return hipSuccess;
+    if (blocks > (int64_t)INT32_MAX) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(gdn_seg_fixup_kernel, dim3((unsigned)blocks), dim3(256), 0, s, seg_args(p, P, chunks));
     return hipGetLastError();
 }
 
@@ -2231,6 +2436,9 @@ static int pipe_post_blocks(const PrefillPlan& p, int cus) {
 // GDN_FLAG_SEPARATE_LAUNCHES (allow_pipe false) turns it off.
 static bool use_pipe(const PrefillPlan& p) {
     if (!p.allow_pipe || !p.io_bf16 || p.sync.ready == nullptr || p.chunk_slots <= 0) return false;
+    int seg_chunks = 0;
+    if (seg_count(p, &seg_chunks) > 1) return false;   // GDN_FLAG_SEGMENTS asked for segments
+
     const int cus = device_cus(), ns = sweep_blocks(p);
     return 2 * ns <= cus && 4 * (ns + pipe_post_blocks(p, cus)) <= 3 * cus;
 }
@@ -2291,11 +2499,26 @@ static hipError_t run_serial(const PrefillPlan& p, bool pipe, hipStream_t s, Ker
         GDN_TRY(launch_chunk_table(p, s));
         GDN_TRY(rec.end(s));
     }
+    int seg_chunks = 0;
+    const int P = pipe ? 1 : seg_count(p, &seg_chunks);
     if (pipe) {   // prep, sweep, gated norm and conv state in one launch
         GDN_TRY(rec.begin(GDN_STAGE_PIPELINE, s));
         GDN_TRY(launch_pipe(p, s));
         GDN_TRY(rec.end(s));
         return hipSuccess;
+    } else if (P > 1) {   // segment-parallel sweep, then the start states and their part of o
+        GDN_TRY(rec.begin(GDN_STAGE_CHUNK_PREP, s));
+        GDN_TRY(launch_prep<IO>(p, p.chunk_slots, s));
+        GDN_TRY(rec.end(s));
+        GDN_TRY(rec.begin(GDN_STAGE_STATE_SWEEP, s));
+        GDN_TRY(launch_seg_sweep(p, P, seg_chunks, s));
+        GDN_TRY(rec.end(s));
+        GDN_TRY(rec.begin(GDN_STAGE_SEG_COMPOSE, s));
+        GDN_TRY(launch_seg_compose(p, P, seg_chunks, s));
+        GDN_TRY(rec.end(s));
+        GDN_TRY(rec.begin(GDN_STAGE_SEG_FIXUP, s));
+        GDN_TRY(launch_seg_fixup(p, P, seg_chunks, s));
+        GDN_TRY(rec.end(s));
     } else {
         if (p.chunk_slots > 0) {
             GDN_TRY(rec.begin(GDN_STAGE_CHUNK_PREP, s));
@@ -2347,9 +2570,11 @@ hipError_t static_scratch(void** out) {
 
 hipError_t launch_prefill(const PrefillPlan& p, hipStream_t stream, KernelRecorder& rec) {
     const bool pipe = use_pipe(p);
+    int seg_chunks = 0;
+    const bool seg = !pipe && p.io_bf16 && seg_count(p, &seg_chunks) > 1;
     const int n = (p.prep.cu != nullptr) +
                   (pipe ? 1
-                        : (p.chunk_slots > 0) + 1 + (p.gated && p.total_tokens > 0) +
+                        : (p.chunk_slots > 0) + 1 + (seg ? 2 : 0) + (p.gated && p.total_tokens > 0) +
                               (p.conv_state.conv_state_out != nullptr));
     if (rec.events != nullptr && n > rec.max) return hipErrorInvalidValue;
     GDN_TRY(rec.call_begin(stream));

@@ -89,6 +89,12 @@ typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
  * invalid outputs and gdn_prefill_wait_status reports it.  No effect on
  * separate launches. */
 #define GDN_FLAG_TEST_WAITS_GIVE_UP 0x8u
+/* Prefill launch form for one sequence (no cu_seqlens) with bf16 io, an fp32
+ * state, no state pool slots and no snapshots: segment-parallel separate
+ * launches (see gdn_prefill, "Segments").  Calls that do not qualify ignore
+ * it.  The workspace of a descriptor with this flag is larger
+ * (gdn_prefill_workspace_size takes the flag into account). */
+#define GDN_FLAG_SEGMENTS 0x10u
 
 typedef struct {
     int32_t num_seqs;       /* N >= 1 */
@@ -173,6 +179,19 @@ gdn_status gdn_prefill_workspace_size(const gdn_desc* d, size_t* bytes);
  * reports it.  Callers that cannot keep the CUs free for the call, or that
  * must not depend on the dispatch order, pass GDN_FLAG_SEPARATE_LAUNCHES: the
  * separate kernels never wait on each other.
+ * Segments (GDN_FLAG_SEGMENTS, one qualifying sequence): the recurrence is
+ * linear in the state (hyper.ai story, Gated DeltaNet paragraph: each token's
+ * update multiplies the state by a_t (I - b_t k_t k_t^T) and adds
+ * b_t v_t k_t^T), so over a run of chunks the state obeys S_end = S_start Phi
+ * + S'_end and every output o_t = o'_t + S_start r_t, where S'_end and o'_t
+ * come from a zero start and Phi, r_t from the identity start with v = 0.
+ * The chunks are cut into P segments (P from 2 to 8, as many as one round of
+ * the device's CUs takes); the sweep runs every segment from a zero state
+ * (the first from initial_state) beside one such identity chain per later
+ * segment, all at once, then one kernel chains the segments' start states
+ * and the final state, and one adds S_start r_t to the outputs of the later
+ * segments before the gated norm.  Results agree with the other forms within
+ * rounding (not bit for bit).  Separate launches: no waits.
  */
 gdn_status gdn_prefill(const gdn_desc* d,
                        const void* q, const void* k, const void* v,
@@ -199,7 +218,9 @@ enum {
     GDN_STAGE_STATE_SWEEP = 2,   /* sequential chunk sweep: U, O, state update */
     GDN_STAGE_GATED_NORM = 3,    /* z-gated RMSNorm of the output */
     GDN_STAGE_CONV_STATE = 4,    /* conv state out */
-    GDN_STAGE_PIPELINE = 5       /* chunk prep and state sweep in one launch */
+    GDN_STAGE_PIPELINE = 5,      /* chunk prep and state sweep in one launch */
+    GDN_STAGE_SEG_COMPOSE = 6,   /* segments: start states and final state */
+    GDN_STAGE_SEG_FIXUP = 7      /* segments: start-state part of the outputs */
 };
 gdn_status gdn_prefill_profiled(const gdn_desc* d,
                                 const void* q, const void* k, const void* v,

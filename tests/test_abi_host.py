@@ -52,6 +52,19 @@ def test_workspace_size_grows_with_tokens():
     assert s_f > 1.9 * s_bf
 
 
+def test_workspace_size_with_segments():
+    """GDN_FLAG_SEGMENTS adds, for one sequence, room for up to 8 segments:
+    15 + 7 state-sized buffers of Hv heads and the identity chains' bf16
+    outputs of every token; descriptors of several sequences are unchanged."""
+    T, Hv = 4096, 32
+    plain = gdn.gdn_prefill_workspace_size(B.make_desc(1, T))
+    seg = gdn.gdn_prefill_workspace_size(B.make_desc(1, T, segments=True))
+    extra = (15 + 7) * Hv * 128 * 128 * 4 + T * Hv * 128 * 2
+    assert extra <= seg - plain <= extra + 3 * 256
+    assert gdn.gdn_prefill_workspace_size(B.make_desc(3, T, segments=True)) == \
+        gdn.gdn_prefill_workspace_size(B.make_desc(3, T))
+
+
 FAKE = 1 << 40          # 256-byte aligned fake device address; never dereferenced
 STEP = 1 << 34          # distance between fake tensors (no overlaps)
 
@@ -81,8 +94,8 @@ def test_prefill_validation_errors():
         (dict(head_k_dim=64), {}, 3),
         (dict(head_v_dim=256), {}, 3),
         (dict(conv_kernel=3), {}, 3),
-        (dict(flags=0x10), {}, 3),
-        (dict(flags=0xF), dict(ws_bytes=1024), 6),        # the launch-form and test flags are accepted
+        (dict(flags=0x20), {}, 3),
+        (dict(flags=0x1F), dict(ws_bytes=1024), 6),       # the launch-form and test flags are accepted
         (dict(io_dtype=5), {}, 4),
         (dict(state_dtype=B.GDN_BF16), {}, 4),           # gdn_prefill: fp32 state (gdn_prefill_ex: either)
         (dict(scale=float("nan")), {}, 9),
