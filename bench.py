@@ -290,8 +290,9 @@ def time_calls(hip, calls, steps, warmup):
 
 def bench_options(args, hip, pres):
     """C1 prefill with bf16 state storage in a state pool and a snapshot every
-    16 chunks (gdn_prefill_ex), and multi-token decode (verify) of 4 draft
-    tokens per sequence at the C4 shape, fp32 state."""
+    16 chunks (gdn_prefill_ex), multi-token decode (verify) of 4 draft tokens
+    per sequence at the C4 shape, fp32 state, and one GPU's share of the C1
+    layer under 2-, 4- and 8-way head parallelism."""
     import numpy as np
     import gdn_synth as gs
     from gated_deltanet_layer_02_amd.tensors import PrefillCall, VerifyCall
@@ -326,7 +327,28 @@ def bench_options(args, hip, pres):
            "roofline": {"bound": "hbm", "achieved": round(moved / t / 1e9, 1), "peak": HBM_PEAK / 1e9,
                         "unit": "GB/s", "frac": round(moved / t / HBM_PEAK, 4),
                         "bytes": moved}}
-    return {"prefill_pool_bf16_snapshots": opts, "verify": ver}
+    # one GPU's share of the C1 layer under 2-, 4- and 8-way head parallelism
+    # (8 / 4 / 2 key heads, twice as many value heads, 4,096 tokens): the
+    # default call (segment-parallel form) against the plain separate launches
+    shares = {}
+    for tp, Hk in ((2, 8), (4, 4), (8, 2)):
+        ps = gs.Problem(f"tp{tp}-share", [p.T], Hk=Hk, Hv=2 * Hk, seed=1001 + tp)
+        log(f"[bench] TP-{tp} share: {Hk} key / {2 * Hk} value heads, {p.T} tokens")
+        xs = gs.generate(ps)
+        row = {"workload": f"prefill, 1 sequence of {p.T} tokens, {Hk} key / {2 * Hk} value heads "
+                           f"(one GPU's share of 16 / 32 under {tp}-way head parallelism)"}
+        for label, sep in (("default", False), ("separate_launches", True)):
+            calls = [PrefillCall(xs, Hk=Hk, Hv=2 * Hk, io_bf16=True, separate_launches=sep)
+                     for _ in range(args.buffer_sets)]
+            if label == "default":
+                row["launch"] = launch_form(hip, calls[0])
+            t = time_calls(hip, [c.run for c in calls], args.steps, args.warmup)
+            row[label] = {"us": round(t * 1e6, 2), "tokens_per_s": round(p.T / t, 1),
+                          "flop_frac_dense_tile": round(FLOP_LAYER * p.T * 2 * Hk / t / MFMA_BF16_PEAK, 4)}
+            del calls
+        row["speedup"] = round(row["separate_launches"]["us"] / row["default"]["us"], 3)
+        shares[f"tp{tp}"] = row
+    return {"prefill_pool_bf16_snapshots": opts, "verify": ver, "tp_shares": shares}
 
 
 def layer_bytes(p):
@@ -372,7 +394,10 @@ def launch_form(hip, call):
     torch.cuda.synchronize()
     for e in ev:
         hip.destroy(e)
-    return "pipelined" if "prep_sweep" in [STAGE_NAMES[i] for i in ids] else "separate launches"
+    names = [STAGE_NAMES[i] for i in ids]
+    if "prep_sweep" in names:
+        return "pipelined"
+    return "segments" if "seg_compose" in names else "separate launches"
 
 
 def bench_configs(args, hip):

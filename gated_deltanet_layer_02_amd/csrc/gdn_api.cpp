@@ -73,6 +73,21 @@ uint64_t next_epoch() {
     return e;
 }
 
+// Descriptors the segment-parallel form may serve (one sequence, bf16 io,
+// fp32 state): asked for by GDN_FLAG_SEGMENTS, or by default when the heads
+// are few (Hv <= 16: the plain sweep of one sequence then takes at most 32
+// workgroups, an eighth of the device, and its chain of chunk steps sets the
+// time) and the sequence has at least 32 chunks.  GDN_FLAG_SEPARATE_LAUNCHES
+// alone keeps the plain separate launches.
+constexpr int32_t kSegAutoMaxHv = 16;
+constexpr int64_t kSegAutoMinTokens = 32 * gdn::kChunk;
+bool seg_shape(const gdn_desc* d) {
+    if (d->num_seqs != 1 || d->io_dtype != GDN_BF16 || d->state_dtype != GDN_F32) return false;
+    if (d->flags & GDN_FLAG_SEGMENTS) return true;
+    return !(d->flags & GDN_FLAG_SEPARATE_LAUNCHES) && d->num_v_heads <= kSegAutoMaxHv &&
+           d->total_tokens >= kSegAutoMinTokens;
+}
+
 PrefillLayout prefill_layout(const gdn_desc* d, bool varlen) {
     const size_t C = (size_t)chunk_slots(d, varlen);
     const size_t Hk = d->num_k_heads, Hv = d->num_v_heads;
@@ -89,7 +104,7 @@ PrefillLayout prefill_layout(const gdn_desc* d, bool varlen) {
     L.ready = take(C * Hk * sizeof(uint64_t));
     L.oready = take(C * Hv * 8 * sizeof(uint64_t));
     L.xcc = take((size_t)d->num_seqs * Hv * (gdn::kD / 16) * sizeof(uint64_t));   // <= one per 16 dv rows
-    if ((d->flags & GDN_FLAG_SEGMENTS) && d->num_seqs == 1) {
+    if (seg_shape(d)) {
         // segment-parallel form, sized for the most segments: finals and maps,
         // start states, identity-chain outputs of every token
         const size_t st = Hv * gdn::kD * gdn::kD * sizeof(float);
@@ -163,8 +178,7 @@ gdn_status prefill_impl(const gdn_desc* d, const gdn_prefill_args& x, hipStream_
     p.io_bf16 = d->io_dtype == GDN_BF16;
     p.allow_pipe = (d->flags & GDN_FLAG_SEPARATE_LAUNCHES) == 0;
     p.l2_handoff = (d->flags & GDN_FLAG_PREP_WRITE_BACK) == 0;
-    p.seg_ok = (d->flags & GDN_FLAG_SEGMENTS) && !varlen && N == 1 && T > 0 && d->io_dtype == GDN_BF16 &&
-               d->state_dtype == GDN_F32 && x.state_slots == nullptr && !snaps && L.seg_state != 0;
+    p.seg_ok = seg_shape(d) && !varlen && T > 0 && x.state_slots == nullptr && !snaps && L.seg_state != 0;
     p.seg_state = p.seg_ok ? reinterpret_cast<float*>(ws + L.seg_state) : nullptr;
     p.seg_x = p.seg_ok ? reinterpret_cast<float*>(ws + L.seg_x) : nullptr;
     p.seg_out = p.seg_ok ? ws + L.seg_out : nullptr;

@@ -81,14 +81,18 @@ constexpr int kSegMinChunks = 4;
 //   seg_state [2 seg_n - 1][Hv][dv][dk] fp32: rows 0..seg_n-1 the segments'
 //             final states from their own start (F_s), rows seg_n.. the maps
 //             Phi_s of segments s = 1..seg_n-1;
-//   seg_x     [seg_n - 1][Hv][dv][dk] fp32: X_s, the state at the start of
-//             segment s (X_1 = F_0, X_{s+1} = F_s + X_s Phi_s); X_{seg_n} is
-//             the final state;
+//   seg_x     [seg_n - 1][Hv][dv][dk] bf16: X_s, the state at the start of
+//             segment s (X_1 = F_0, X_{s+1} = F_s + X_s Phi_s, formed in fp32),
+//             rounded for the fix-up's bf16 products; X_{seg_n} is the final
+//             state (fp32);
 //   seg_out   the identity chains' outputs r_t: [T][Hv][dk] bf16;
-//   out       o of every token, [T][Hv][dv] bf16, corrected in place.
+//   out       o of every token, [T][Hv][dv] bf16, corrected in place, and
+//             for a gated layer (z != NULL) normalised there for the tokens of
+//             segments 1.. (the gated-norm kernel takes segment 0's).
 struct SegArgs {
-    const float* seg_state; float* seg_x; float* final_state;
+    const float* seg_state; void* seg_x; float* final_state;
     const void* seg_out; void* out;
+    const void* z; const void* norm_w; float norm_eps;
     int32_t T, Hv, seg_n, seg_chunks;
 };
 // sequences up to which the chunk table also orders them by length

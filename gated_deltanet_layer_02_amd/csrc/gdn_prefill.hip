@@ -1790,93 +1790,164 @@ __global__ __launch_bounds__(256) void gdn_conv_state_kernel(ConvStateArgs a) {
 // segments) is the final state.
 // ===========================================================================
 // Workgroup (h, b) carries rows 16 b .. 16 b + 15 of value head h through the
-// segments one after the other; thread t holds rows 16 b + 2 (t / 32) + {0, 1},
-// columns 4 (t % 32) .. + 3, in fp32 (X_s in LDS while X_s Phi_s is formed).
+// segments one after the other, on fp32 MFMA (16x16x4): X_{s+1} = F_s + X_s
+// Phi_s, wave w forming columns 32 w .. 32 w + 31 (two 16-column tiles) over
+// K = dk in 32 steps of 4, where lane (l16, g4) supplies X_s[l16][4 kb + g4]
+// (from LDS) and Phi_s[4 kb + g4][column l16] (from memory; the next
+// segment's Phi is requested while this one's products run), and its
+// accumulator holds rows 4 g4 .. 4 g4 + 3 of column l16.
 __global__ __launch_bounds__(256) void gdn_seg_compose_kernel(SegArgs a) {
     __shared__ float X[16][kD + 4];
     const int h = blockIdx.x >> 3, b = blockIdx.x & 7;
-    const int t = threadIdx.x, cq = 4 * (t & 31), r0 = 2 * (t >> 5);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l16 = lane & 15, g4 = lane >> 4;
     auto mat = [&](auto* base, int i) { return base + ((size_t)i * a.Hv + h) * (size_t)(kD * kD); };
-    const size_t o0 = (size_t)(16 * b + r0) * kD + cq, o1 = o0 + kD;
-    f32x4 x0 = *reinterpret_cast<const f32x4*>(mat(a.seg_state, 0) + o0);   // X_1 = F_0
-    f32x4 x1 = *reinterpret_cast<const f32x4*>(mat(a.seg_state, 0) + o1);
-    for (int s = 1;; ++s) {
-        if (s == a.seg_n) {   // x = X_P: the final state
-            if (a.final_state != nullptr) {
-                *reinterpret_cast<f32x4*>(mat(a.final_state, 0) + o0) = x0;
-                *reinterpret_cast<f32x4*>(mat(a.final_state, 0) + o1) = x1;
+    uint16_t* xb = static_cast<uint16_t*>(a.seg_x);   // X_s as bf16, for the fix-up
+    for (int i = threadIdx.x; i < 16 * (kD / 4); i += 256) {   // X_1 = F_0
+        const int r = i / (kD / 4), c4 = 4 * (i % (kD / 4));
+        const size_t o = (size_t)(16 * b + r) * kD + c4;
+        const f32x4 v = *reinterpret_cast<const f32x4*>(mat(a.seg_state, 0) + o);
+        *reinterpret_cast<f32x4*>(&X[r][c4]) = v;
+        *reinterpret_cast<u16x4*>(mat(xb, 0) + o) =
+            u16x4{f32_to_bf16_bits(v[0]), f32_to_bf16_bits(v[1]), f32_to_bf16_bits(v[2]), f32_to_bf16_bits(v[3])};
+    }
+    __syncthreads();
+    const int col = 32 * wave + l16;   // + 16 ct
+    // B operands of Phi_s and the accumulator's start F_s, requested one
+    // segment ahead
+    float bcur[2][kD / 4], bnext[2][kD / 4];
+    f32x4 fcur[2], fnext[2];
+    auto load = [&](int s, float (&bv)[2][kD / 4], f32x4 (&fv)[2]) {
+        const float* phi = mat(a.seg_state, a.seg_n + s - 1);
+        const float* F = mat(a.seg_state, s);
+#pragma unroll
+        for (int kb = 0; kb < kD / 4; ++kb)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) bv[ct][kb] = phi[(size_t)(4 * kb + g4) * kD + col + 16 * ct];
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) fv[ct][r] = F[(size_t)(16 * b + 4 * g4 + r) * kD + col + 16 * ct];
+    };
+    load(1, bcur, fcur);
+    for (int s = 1; s < a.seg_n; ++s) {
+        if (s + 1 < a.seg_n) load(s + 1, bnext, fnext);
+        f32x4 acc[2] = {fcur[0], fcur[1]};
+#pragma unroll
+        for (int kb = 0; kb < kD / 4; ++kb) {
+            const float av = X[l16][4 * kb + g4];
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bcur[ct][kb], acc[ct], 0, 0, 0);
+        }
+        __syncthreads();   // every wave has read X_s
+        const bool last = s + 1 == a.seg_n;   // acc = X_P, the final state
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const size_t o = (size_t)(16 * b + 4 * g4 + r) * kD + col + 16 * ct;
+                X[4 * g4 + r][col + 16 * ct] = acc[ct][r];
+                if (!last) mat(xb, s)[o] = f32_to_bf16_bits(acc[ct][r]);
+                else if (a.final_state != nullptr) mat(a.final_state, 0)[o] = acc[ct][r];
             }
-            return;
-        }
-        *reinterpret_cast<f32x4*>(mat(a.seg_x, s - 1) + o0) = x0;   // X_s
-        *reinterpret_cast<f32x4*>(mat(a.seg_x, s - 1) + o1) = x1;
-        *reinterpret_cast<f32x4*>(&X[r0][cq]) = x0;
-        *reinterpret_cast<f32x4*>(&X[r0 + 1][cq]) = x1;
         __syncthreads();
-        const float* phi = mat(a.seg_state, a.seg_n + s - 1) + cq;   // Phi_s
-        f32x4 y0 = *reinterpret_cast<const f32x4*>(mat(a.seg_state, s) + o0);   // F_s
-        f32x4 y1 = *reinterpret_cast<const f32x4*>(mat(a.seg_state, s) + o1);
-#pragma unroll 8
-        for (int r = 0; r < kD; ++r) {
-            const f32x4 ph = *reinterpret_cast<const f32x4*>(phi + (size_t)r * kD);
-            y0 += X[r0][r] * ph;
-            y1 += X[r0 + 1][r] * ph;
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+            fcur[ct] = fnext[ct];
+#pragma unroll
+            for (int kb = 0; kb < kD / 4; ++kb) bcur[ct][kb] = bnext[ct][kb];
         }
-        __syncthreads();   // every thread has read X_s
-        x0 = y0;
-        x1 = y1;
     }
 }
 
-// o_t += X_s r_t for the tokens of segments 1..P-1: workgroup (chunk c of
-// segment s = c / seg_chunks >= 1, value head h), four waves.  As a product,
-// the chunk's o^T (dv x tokens) gains X_s (dv x dk) R^T (dk x tokens), R the
-// identity chain's outputs; wave w forms dv rows 32 w .. 32 w + 31 (two
-// 16-row tiles) for the four 16-token tiles on bf16 MFMA (X_s rounded to
-// bf16), K = dk in four blocks of 32 of which lane (l16, g4) supplies dk
-// 32 p + 8 g4 .. + 7 of its row in both operands.  Accumulator lane (l16, g4)
-// then holds dv 4 g4 .. + 3 of token l16: an 8-byte read-modify-write of o.
+// The later segments' outputs: o_t = o'_t + X_s r_t, then (gated) the z-gated
+// RMSNorm, out = o / sqrt(mean o^2 + eps) * w * SiLU(z), in place of o'.
+// Workgroup: value head h and up to kSegFixChunks chunks of segments >= 1;
+// wave w takes token tile w (16 tokens) of each chunk over all 128 dv rows:
+// o^T (dv x tokens) gains X_s (dv x dk) R^T (dk x tokens), R the identity
+// chain's outputs, on bf16 MFMA with X_s staged in LDS as bf16.  K = dk in
+// four blocks of 32, of which lane (l16, g4) supplies dk 32 p + 8 g4 .. + 7
+// of its row in both operands; accumulator tile dt of lane (l16, g4) then
+// holds dv 16 dt + 4 g4 .. + 3 of token l16, so a token's sum of squares is
+// the lane's own 32 values plus those of lanes l16 + 16 j.
+constexpr int kSegFixChunks = 1;
 __global__ __launch_bounds__(256) void gdn_seg_fixup_kernel(SegArgs a) {
-    const int c = a.seg_chunks + (int)(blockIdx.x / (unsigned)a.Hv), h = (int)(blockIdx.x % (unsigned)a.Hv);
-    const int s = c / a.seg_chunks;
-    const int t0 = c * kChunk, len = min(kChunk, a.T - t0);
+    constexpr int kXLd = kD + 8;   // bf16 row stride of X_s in LDS (16-byte reads of 16 rows spread over the banks)
+    __shared__ __attribute__((aligned(16))) uint16_t Xs[kD * kXLd];
+    const int h = (int)(blockIdx.x % (unsigned)a.Hv);
+    const int c0 = a.seg_chunks + kSegFixChunks * (int)(blockIdx.x / (unsigned)a.Hv);
+    const int C = (a.T + kChunk - 1) / kChunk;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l16 = lane & 15, g4 = lane >> 4;
-    const float* X = a.seg_x + ((size_t)(s - 1) * a.Hv + h) * (size_t)(kD * kD);
-    typedef Frag<bf16> F;
-    F xa[2][4];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const float* src = X + (size_t)(32 * wave + 16 * i + l16) * kD + 32 * p + 8 * g4;
-            xa[i][p] = acc_to_frag<bf16>(*reinterpret_cast<const f32x4*>(src),
-                                         *reinterpret_cast<const f32x4*>(src + 4));
-        }
     const uint16_t* R = static_cast<const uint16_t*>(a.seg_out);
     uint16_t* O = static_cast<uint16_t*>(a.out);
+    const uint16_t* Z = static_cast<const uint16_t*>(a.z);
+    float w[8][4];   // norm weight of this lane's dv 16 dt + 4 g4 + r
+    if (Z != nullptr) {
+        const uint16_t* nw = static_cast<const uint16_t*>(a.norm_w);
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-        const int tt = 16 * mt + l16;   // token of this lane's B column and accumulator column
-        const bool ok = tt < len;
-        const size_t row = ((size_t)(t0 + tt) * a.Hv + h) * kD;
+        for (int dt = 0; dt < 8; ++dt) {
+            const u16x4 v = *reinterpret_cast<const u16x4*>(nw + 16 * dt + 4 * g4);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) w[dt][r] = bf16_bits_to_f32(v[r]);
+        }
+    }
+    int loaded = 0;   // segment whose X is in LDS (0: none)
+    for (int c = c0; c < min(c0 + kSegFixChunks, C); ++c) {
+        const int s = c / a.seg_chunks;   // uniform
+        if (s != loaded) {
+            __syncthreads();   // every wave is done with the previous X
+            const uint16_t* X = static_cast<const uint16_t*>(a.seg_x) + ((size_t)(s - 1) * a.Hv + h) * (size_t)(kD * kD);
+            for (int i = threadIdx.x; i < kD * kD / 8; i += 256) {
+                const int row = i / (kD / 8), c8 = 8 * (i % (kD / 8));
+                *reinterpret_cast<u16x8*>(Xs + row * kXLd + c8) = *reinterpret_cast<const u16x8*>(X + (size_t)row * kD + c8);
+            }
+            __syncthreads();
+            loaded = s;
+        }
+        const int t = c * kChunk + 16 * wave + l16;   // this lane's token
+        const bool ok = t < a.T;
+        const size_t row = ((size_t)t * a.Hv + h) * kD;
+        typedef Frag<bf16> F;
         F rb[4];
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
             if (ok) rb[p].v = *reinterpret_cast<const bf16x8*>(R + row + 32 * p + 8 * g4);
             else rb[p].v = bf16x8{};
         }
+        f32x4 o[8];
+        float ss = 0.f;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int dt = 0; dt < 8; ++dt) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int p = 0; p < 4; ++p) mma(acc, xa[i][p], rb[p]);
-            if (ok) {
-                u16x4* op = reinterpret_cast<u16x4*>(O + row + 32 * wave + 16 * i + 4 * g4);
-                u16x4 ov = *op;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) ov[r] = f32_to_bf16_bits(bf16_bits_to_f32(ov[r]) + acc[r]);
-                *op = ov;
+            for (int p = 0; p < 4; ++p) {
+                F xa;
+                xa.v = *reinterpret_cast<const bf16x8*>(Xs + (16 * dt + l16) * kXLd + 32 * p + 8 * g4);
+                mma(acc, xa, rb[p]);
             }
+            const u16x4 ov = ok ? *reinterpret_cast<const u16x4*>(O + row + 16 * dt + 4 * g4) : u16x4{0, 0, 0, 0};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                o[dt][r] = bf16_bits_to_f32(ov[r]) + acc[r];
+                ss = fmaf(o[dt][r], o[dt][r], ss);
+            }
+        }
+        if (Z != nullptr) {
+            ss += __shfl_xor(ss, 16);
+            ss += __shfl_xor(ss, 32);
+            const float rr = rsqrt_f32(ss * (1.0f / kD) + a.norm_eps);
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+                const u16x4 zv = ok ? *reinterpret_cast<const u16x4*>(Z + row + 16 * dt + 4 * g4) : u16x4{0, 0, 0, 0};
+#pragma unroll
+                for (int r = 0; r < 4; ++r) o[dt][r] = o[dt][r] * rr * w[dt][r] * silu_f32(bf16_bits_to_f32(zv[r]));
+            }
+        }
+        if (ok) {
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt)
+                *reinterpret_cast<u16x4*>(O + row + 16 * dt + 4 * g4) =
+                    u16x4{f32_to_bf16_bits(o[dt][0]), f32_to_bf16_bits(o[dt][1]), f32_to_bf16_bits(o[dt][2]),
+                          f32_to_bf16_bits(o[dt][3])};
         }
     }
 }
@@ -2345,6 +2416,9 @@ static SegArgs seg_args(const PrefillPlan& p, int P, int chunks) {
     g.Hv = p.sweep.Hv;
     g.seg_n = P;
     g.seg_chunks = chunks;
+    g.z = p.gated ? p.z : nullptr;
+    g.norm_w = p.norm_w;
+    g.norm_eps = p.norm_eps;
     return g;
 }
 
@@ -2355,7 +2429,7 @@ static hipError_t launch_seg_compose(const PrefillPlan& p, int P, int chunks, hi
 }
 
 static hipError_t launch_seg_fixup(const PrefillPlan& p, int P, int chunks, hipStream_t s) {
-    const int64_t blocks = (int64_t)(p.chunk_slots - chunks) * p.sweep.Hv;
+    const int64_t blocks = (int64_t)(p.chunk_slots - chunks + kSegFixChunks - 1) / kSegFixChunks * p.sweep.Hv;
     if (blocks <= 0) return hipSuccess;
     if (blocks > (int64_t)INT32_MAX) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(gdn_seg_fixup_kernel, dim3((unsigned)blocks), dim3(256), 0, s, seg_args(p, P, chunks));
@@ -2529,9 +2603,10 @@ static hipError_t run_serial(const PrefillPlan& p, bool pipe, hipStream_t s, Ker
         GDN_TRY(launch_sweep(p, s));
         GDN_TRY(rec.end(s));
     }
-    if (p.gated && p.total_tokens > 0) {
+    if (p.gated && p.total_tokens > 0) {   // segments: the fix-up normalised the later segments' tokens
         GDN_TRY(rec.begin(GDN_STAGE_GATED_NORM, s));
-        GDN_TRY(launch_norm<IO>(p, 0, p.total_tokens, s));
+        GDN_TRY(launch_norm<IO>(p, 0, P > 1 ? std::min<int64_t>(p.total_tokens, (int64_t)kChunk * seg_chunks)
+                                             : p.total_tokens, s));
         GDN_TRY(rec.end(s));
     }
     if (p.conv_state.conv_state_out != nullptr) {

@@ -91,9 +91,10 @@ typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
 #define GDN_FLAG_TEST_WAITS_GIVE_UP 0x8u
 /* Prefill launch form for one sequence (no cu_seqlens) with bf16 io, an fp32
  * state, no state pool slots and no snapshots: segment-parallel separate
- * launches (see gdn_prefill, "Segments").  Calls that do not qualify ignore
- * it.  The workspace of a descriptor with this flag is larger
- * (gdn_prefill_workspace_size takes the flag into account). */
+ * launches (see gdn_prefill, "Segments") at any head count and from 8 chunks
+ * on.  Calls that do not qualify ignore it.  The workspace of a descriptor
+ * that may take this form is larger (gdn_prefill_workspace_size takes the
+ * flag and the default rule into account). */
 #define GDN_FLAG_SEGMENTS 0x10u
 
 typedef struct {
@@ -190,8 +191,13 @@ gdn_status gdn_prefill_workspace_size(const gdn_desc* d, size_t* bytes);
  * (the first from initial_state) beside one such identity chain per later
  * segment, all at once, then one kernel chains the segments' start states
  * and the final state, and one adds S_start r_t to the outputs of the later
- * segments before the gated norm.  Results agree with the other forms within
- * rounding (not bit for bit).  Separate launches: no waits.
+ * segments and applies their gated norm.  Results agree with the other forms
+ * within rounding (not bit for bit).  Separate launches: no waits.  Taken by
+ * default, without the flag, for one qualifying sequence of at least 32 chunks
+ * with at most 16 value heads (one GPU's share of the 16 key / 32 value head
+ * layer under 2-, 4- or 8-way head parallelism: the chain of chunk steps,
+ * not the device's width, sets the time there), unless
+ * GDN_FLAG_SEPARATE_LAUNCHES is given alone.
  */
 gdn_status gdn_prefill(const gdn_desc* d,
                        const void* q, const void* k, const void* v,

@@ -35,6 +35,7 @@ static size_t g_ws_bytes = 0;
 static int g_prefills = 0, g_decodes = 0, g_verifies = 0, g_commits = 0;
 static bool g_last_pipe_allowed = false, g_last_l2 = false;
 static uint64_t g_last_ticks = 0;
+static bool g_last_seg = false;
 
 static void touch(const void* p, size_t bytes) {
     if (bytes == 0) return;
@@ -66,7 +67,14 @@ hipError_t launch_prefill(const PrefillPlan& p, hipStream_t, KernelRecorder&) {
         {p.sync.ready, C * Hk * sizeof(uint64_t)},
         {p.sync.oready, C * Hv * 8 * sizeof(uint64_t)},
         {p.sync.xcc, N * Hv * (kD / 16) * sizeof(uint64_t)},
+        // segment-parallel form: finals and maps, start states, identity-chain outputs
+        {p.seg_state, p.seg_ok ? (2 * kSegMax - 1) * Hv * kD * kD * sizeof(float) : 0},
+        {p.seg_x, p.seg_ok ? (kSegMax - 1) * Hv * kD * kD * sizeof(float) : 0},
+        {p.seg_out, p.seg_ok ? (size_t)p.total_tokens * Hv * kD * 2 : 0},
     };
+    g_last_seg = p.seg_ok;
+    CHECK(!p.seg_ok || (N == 1 && p.io_bf16 && p.prep.cu == nullptr && p.sweep.slots == nullptr &&
+                        p.sweep.snap_every == 0 && p.sweep.state_bf16 == 0));
     for (const Region& r : regions) {
         CHECK(r.bytes == 0 || inside(r.at, r.bytes));
         if (r.bytes && inside(r.at, r.bytes)) touch(r.at, r.bytes);
@@ -169,7 +177,15 @@ int main() {
         {3, {100, 0, 65}, 2, 4, GDN_BF16, GDN_BF16, true, true, true, 1, GDN_FLAG_SEPARATE_LAUNCHES},
         {2, {64 * 7 + 3, 64}, 3, 6, GDN_F32, GDN_F32, true, false, true, 2, GDN_FLAG_PREP_WRITE_BACK},
         {4, {1, 2, 3, 200}, 1, 4, GDN_F32, GDN_BF16, true, true, false, 0, GDN_FLAG_TEST_WAITS_GIVE_UP},
+        // segments: asked for (16 / 32 heads), by default (2 / 4 heads, >= 32 chunks), and neither
+        {1, {64 * 9 + 5}, 16, 32, GDN_BF16, GDN_F32, false, true, true, 0, GDN_FLAG_SEGMENTS},
+        {1, {64 * 40}, 2, 4, GDN_BF16, GDN_F32, false, true, true, 0, 0},
+        {1, {64 * 40}, 2, 4, GDN_BF16, GDN_F32, false, true, true, 0, GDN_FLAG_SEPARATE_LAUNCHES},
+        {1, {64 * 31}, 2, 4, GDN_BF16, GDN_F32, false, true, true, 0, 0},
     };
+    const bool seg_expected[] = {false, false, false, false, false, false, true, true, false, false};
+    static_assert(sizeof(seg_expected) == sizeof(ps) / sizeof(ps[0]), "one expectation per case");
+    int i_case = 0;
     for (const P& p : ps) {
         int64_t T = 0;
         for (int32_t L : p.lens) T += L;
@@ -180,6 +196,8 @@ int main() {
         CHECK(g_last_pipe_allowed == !(p.flags & GDN_FLAG_SEPARATE_LAUNCHES));
         CHECK(g_last_l2 == !(p.flags & GDN_FLAG_PREP_WRITE_BACK));
         CHECK((g_last_ticks == 0) == ((p.flags & GDN_FLAG_TEST_WAITS_GIVE_UP) != 0));
+        CHECK(g_last_seg == seg_expected[i_case]);
+        ++i_case;
     }
     // a workspace one byte short is refused before any launch
     {
@@ -195,7 +213,7 @@ int main() {
     }
     // rejected descriptors
     {
-        gdn_desc d = desc(1, 10, 2, 4, GDN_BF16, GDN_F32, 0x10);
+        gdn_desc d = desc(1, 10, 2, 4, GDN_BF16, GDN_F32, 0x20);
         size_t n = 0;
         CHECK(gdn_prefill_workspace_size(&d, &n) == GDN_ERR_UNSUPPORTED);
         d = desc(1, 10, 3, 4, GDN_BF16, GDN_F32, 0);

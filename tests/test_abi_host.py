@@ -63,6 +63,14 @@ def test_workspace_size_with_segments():
     assert extra <= seg - plain <= extra + 3 * 256
     assert gdn.gdn_prefill_workspace_size(B.make_desc(3, T, segments=True)) == \
         gdn.gdn_prefill_workspace_size(B.make_desc(3, T))
+    # the default rule: one sequence of >= 32 chunks with <= 16 value heads,
+    # unless separate launches are asked for alone
+    few = dict(num_k_heads=2, num_v_heads=4)
+    grow = gdn.gdn_prefill_workspace_size(B.make_desc(1, T, **few)) - \
+        gdn.gdn_prefill_workspace_size(B.make_desc(1, T, separate_launches=True, **few))
+    assert grow >= (15 + 7) * 4 * 128 * 128 * 4 + T * 4 * 128 * 2
+    assert gdn.gdn_prefill_workspace_size(B.make_desc(1, 2047, **few)) == \
+        gdn.gdn_prefill_workspace_size(B.make_desc(1, 2047, separate_launches=True, **few))
 
 
 FAKE = 1 << 40          # 256-byte aligned fake device address; never dereferenced

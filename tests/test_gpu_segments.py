@@ -19,14 +19,15 @@ pytestmark = pytest.mark.gpu
 SEG_COMPOSE, SEG_FIXUP = 6, 7   # GDN_STAGE_SEG_COMPOSE / GDN_STAGE_SEG_FIXUP
 
 
-def stages(p, x):
-    """Stage ids of one profiled call with the segments flag."""
+def stages(p, x, segments=True, separate_launches=False):
+    """Stage ids of one profiled call (by default with the segments flag)."""
     import ctypes
 
     import torch
     from gated_deltanet_layer_02_amd.tensors import PrefillCall
     call = PrefillCall(x, Hk=p.Hk, Hv=p.Hv, io_bf16=p.io == gs.BF16, l2norm=p.l2norm, scale=p.scale,
-                       l2_eps=p.l2_eps, norm_eps=p.norm_eps, segments=True)
+                       l2_eps=p.l2_eps, norm_eps=p.norm_eps, segments=segments,
+                       separate_launches=separate_launches)
     hip = ctypes.CDLL("libamdhip64.so.7")
     hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
     hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
@@ -84,6 +85,20 @@ def test_segments_tp8_share():
     x = gs.generate(p)
     assert SEG_COMPOSE in stages(p, x)
     say(f"segments, TP-8 share: {check_prefill(p, x, segments=True)}")
+
+
+@pytest.mark.parametrize("Hk,Hv,T", [(4, 8, 2048), (8, 16, 4096)])
+def test_segments_by_default_for_few_heads(Hk, Hv, T):
+    """Without the flag, one sequence of >= 32 chunks with <= 16 value heads
+    takes the segment form (2,048 tokens at 4 key / 8 value heads: eight
+    segments of 4 chunks; 4,096 at 8 / 16: four of 16), and separate launches
+    asked for alone keep the plain form."""
+    p = gs.Problem(f"seg-default-{Hk}x{Hv}", [T], Hk=Hk, Hv=Hv, init_state_std=0.01,
+                   conv_state_std=0.01, seed=3000 + Hv)
+    x = gs.generate(p)
+    assert SEG_COMPOSE in stages(p, x, segments=False)
+    assert SEG_COMPOSE not in stages(p, x, segments=False, separate_launches=True)
+    say(f"segments by default, {Hk}x{Hv}: {check_prefill(p, x)}")
 
 
 def test_segments_c1_all_heads():
