@@ -1791,18 +1791,21 @@ __global__ __launch_bounds__(256) void gdn_conv_state_kernel(ConvStateArgs a) {
 // ===========================================================================
 // Workgroup (h, b) carries rows 16 b .. 16 b + 15 of value head h through the
 // segments one after the other, on fp32 MFMA (16x16x4): X_{s+1} = F_s + X_s
-// Phi_s, wave w forming columns 32 w .. 32 w + 31 (two 16-column tiles) over
-// K = dk in 32 steps of 4, where lane (l16, g4) supplies X_s[l16][4 kb + g4]
-// (from LDS) and Phi_s[4 kb + g4][column l16] (from memory; the next
-// segment's Phi is requested while this one's products run), and its
-// accumulator holds rows 4 g4 .. 4 g4 + 3 of column l16.
-__global__ __launch_bounds__(256) void gdn_seg_compose_kernel(SegArgs a) {
-    __shared__ float X[16][kD + 4];
+// Phi_s, wave w (of 8) forming columns 16 w .. 16 w + 15 over K = dk in 32
+// steps of 4, where in step kb lane (l16, g4) supplies X_s[l16][32 g4 + kb]
+// (its 32 values read from LDS at once) and Phi_s[32 g4 + kb][16 w + l16]
+// (from memory), and its accumulator holds rows 4 g4 .. 4 g4 + 3 of column
+// 16 w + l16.  The chain is latency-bound (one product of 16 x 128 x 128 per
+// segment and workgroup): the steps go to four accumulators, and each wave
+// requests Phi and F three segments ahead, in three register sets.
+constexpr int kSegComposeAhead = 3;
+__global__ __launch_bounds__(512) void gdn_seg_compose_kernel(SegArgs a) {
+    __shared__ __attribute__((aligned(16))) float X[16][kD + 4];
     const int h = blockIdx.x >> 3, b = blockIdx.x & 7;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l16 = lane & 15, g4 = lane >> 4;
     auto mat = [&](auto* base, int i) { return base + ((size_t)i * a.Hv + h) * (size_t)(kD * kD); };
     uint16_t* xb = static_cast<uint16_t*>(a.seg_x);   // X_s as bf16, for the fix-up
-    for (int i = threadIdx.x; i < 16 * (kD / 4); i += 256) {   // X_1 = F_0
+    for (int i = threadIdx.x; i < 16 * (kD / 4); i += 512) {   // X_1 = F_0
         const int r = i / (kD / 4), c4 = 4 * (i % (kD / 4));
         const size_t o = (size_t)(16 * b + r) * kD + c4;
         const f32x4 v = *reinterpret_cast<const f32x4*>(mat(a.seg_state, 0) + o);
@@ -1811,51 +1814,68 @@ __global__ __launch_bounds__(256) void gdn_seg_compose_kernel(SegArgs a) {
             u16x4{f32_to_bf16_bits(v[0]), f32_to_bf16_bits(v[1]), f32_to_bf16_bits(v[2]), f32_to_bf16_bits(v[3])};
     }
     __syncthreads();
-    const int col = 32 * wave + l16;   // + 16 ct
-    // B operands of Phi_s and the accumulator's start F_s, requested one
-    // segment ahead
-    float bcur[2][kD / 4], bnext[2][kD / 4];
-    f32x4 fcur[2], fnext[2];
-    auto load = [&](int s, float (&bv)[2][kD / 4], f32x4 (&fv)[2]) {
-        const float* phi = mat(a.seg_state, a.seg_n + s - 1);
-        const float* F = mat(a.seg_state, s);
+    const int col = 16 * wave + l16;
+    struct Ops {
+        float b[kD / 4];   // Phi_s[4 kb + g4][col]
+        f32x4 f;           // F_s[16 b + 4 g4 + r][col]
+    };
+    auto load = [&](int s, Ops& o) {
+        if (s >= a.seg_n) return;
+        const float* phi = mat(a.seg_state, a.seg_n + s - 1) + col;
+        const float* F = mat(a.seg_state, s) + (size_t)(16 * b + 4 * g4) * kD + col;
+#pragma unroll
+        for (int kb = 0; kb < kD / 4; ++kb) o.b[kb] = phi[(size_t)(32 * g4 + kb) * kD];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o.f[r] = F[(size_t)r * kD];
+    };
+    // Barriers between the waves' LDS accesses: LDS operations complete
+    // (lgkmcnt 0), no wait on memory, so the loads requested ahead stay in
+    // flight (__syncthreads would wait for them too).
+    auto lds_barrier = [] {
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(vm_wait(63));   // lgkmcnt 0; vmcnt 63: no wait on memory
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+    // one segment: X_{s+1} from X_s (LDS) and o; false past the last
+    auto step = [&](int s, const Ops& o) {
+        if (s >= a.seg_n) return false;
+        float xa[kD / 4];
+#pragma unroll
+        for (int i = 0; i < kD / 16; ++i) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(&X[l16][32 * g4 + 4 * i]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) xa[4 * i + e] = v[e];
+        }
+        f32x4 acc[4] = {o.f, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
         for (int kb = 0; kb < kD / 4; ++kb)
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct) bv[ct][kb] = phi[(size_t)(4 * kb + g4) * kD + col + 16 * ct];
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) fv[ct][r] = F[(size_t)(16 * b + 4 * g4 + r) * kD + col + 16 * ct];
-    };
-    load(1, bcur, fcur);
-    for (int s = 1; s < a.seg_n; ++s) {
-        if (s + 1 < a.seg_n) load(s + 1, bnext, fnext);
-        f32x4 acc[2] = {fcur[0], fcur[1]};
-#pragma unroll
-        for (int kb = 0; kb < kD / 4; ++kb) {
-            const float av = X[l16][4 * kb + g4];
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct) acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bcur[ct][kb], acc[ct], 0, 0, 0);
-        }
-        __syncthreads();   // every wave has read X_s
+            acc[kb & 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[kb], o.b[kb], acc[kb & 3], 0, 0, 0);
+        acc[0] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+        lds_barrier();   // every wave has read X_s
         const bool last = s + 1 == a.seg_n;   // acc = X_P, the final state
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const size_t o = (size_t)(16 * b + 4 * g4 + r) * kD + col + 16 * ct;
-                X[4 * g4 + r][col + 16 * ct] = acc[ct][r];
-                if (!last) mat(xb, s)[o] = f32_to_bf16_bits(acc[ct][r]);
-                else if (a.final_state != nullptr) mat(a.final_state, 0)[o] = acc[ct][r];
-            }
-        __syncthreads();
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-            fcur[ct] = fnext[ct];
-#pragma unroll
-            for (int kb = 0; kb < kD / 4; ++kb) bcur[ct][kb] = bnext[ct][kb];
+        for (int r = 0; r < 4; ++r) {
+            const size_t off = (size_t)(16 * b + 4 * g4 + r) * kD + col;
+            X[4 * g4 + r][col] = acc[0][r];
+            if (!last) mat(xb, s)[off] = f32_to_bf16_bits(acc[0][r]);
+            else if (a.final_state != nullptr) mat(a.final_state, 0)[off] = acc[0][r];
         }
+        lds_barrier();   // X_{s+1} is in LDS
+        return true;
+    };
+    static_assert(kSegComposeAhead == 3, "three register sets below");
+    Ops o0, o1, o2;
+    load(1, o0);
+    load(2, o1);
+    load(3, o2);
+    for (int s = 1; s < a.seg_n; s += 3) {
+        if (!step(s, o0)) break;
+        load(s + 3, o0);
+        if (!step(s + 1, o1)) break;
+        load(s + 4, o1);
+        if (!step(s + 2, o2)) break;
+        load(s + 5, o2);
     }
 }
 
@@ -2423,7 +2443,7 @@ static SegArgs seg_args(const PrefillPlan& p, int P, int chunks) {
 }
 
 static hipError_t launch_seg_compose(const PrefillPlan& p, int P, int chunks, hipStream_t s) {
-    hipLaunchKernelGGL(gdn_seg_compose_kernel, dim3((unsigned)(8 * p.sweep.Hv)), dim3(256), 0, s,
+    hipLaunchKernelGGL(gdn_seg_compose_kernel, dim3((unsigned)(8 * p.sweep.Hv)), dim3(512), 0, s,
                        seg_args(p, P, chunks));
     return hipGetLastError();
 }
