@@ -1797,11 +1797,15 @@ __global__ __launch_bounds__(256) void gdn_conv_state_kernel(ConvStateArgs a) {
 // (from memory), and its accumulator holds rows 4 g4 .. 4 g4 + 3 of column
 // 16 w + l16.  The chain is latency-bound (one product of 16 x 128 x 128 per
 // segment and workgroup): the steps go to four accumulators, and each wave
-// requests Phi and F three segments ahead, in three register sets.
+// requests Phi and F three segments ahead, in three register sets.  The
+// eight workgroups of a head read the same Phi_s and F_s rows: they run on
+// one XCD (workgroup x on XCD x mod 8; the grid is 64 workgroups per eight
+// heads), whose L2 fetches each row once.
 constexpr int kSegComposeAhead = 3;
 __global__ __launch_bounds__(512) void gdn_seg_compose_kernel(SegArgs a) {
     __shared__ __attribute__((aligned(16))) float X[16][kD + 4];
-    const int h = blockIdx.x >> 3, b = blockIdx.x & 7;
+    const int x = blockIdx.x, b = (x >> 3) & 7, h = 8 * (x >> 6) + (x & 7);
+    if (h >= a.Hv) return;   // padding of the last eight heads
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l16 = lane & 15, g4 = lane >> 4;
     auto mat = [&](auto* base, int i) { return base + ((size_t)i * a.Hv + h) * (size_t)(kD * kD); };
     uint16_t* xb = static_cast<uint16_t*>(a.seg_x);   // X_s as bf16, for the fix-up
@@ -2443,7 +2447,7 @@ static SegArgs seg_args(const PrefillPlan& p, int P, int chunks) {
 }
 
 static hipError_t launch_seg_compose(const PrefillPlan& p, int P, int chunks, hipStream_t s) {
-    hipLaunchKernelGGL(gdn_seg_compose_kernel, dim3((unsigned)(8 * p.sweep.Hv)), dim3(512), 0, s,
+    hipLaunchKernelGGL(gdn_seg_compose_kernel, dim3((unsigned)(64 * ((p.sweep.Hv + 7) / 8))), dim3(512), 0, s,
                        seg_args(p, P, chunks));
     return hipGetLastError();
 }
