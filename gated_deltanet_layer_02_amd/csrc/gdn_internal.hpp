@@ -77,24 +77,6 @@ struct SweepArgs {
 constexpr int kSegMax = 8;
 constexpr int kSegMinChunks = 4;
 
-// Composition and output fix-up of the segment-parallel sweep.
-//   seg_state [2 seg_n - 1][Hv][dv][dk] fp32: rows 0..seg_n-1 the segments'
-//             final states from their own start (F_s), rows seg_n.. the maps
-//             Phi_s of segments s = 1..seg_n-1;
-//   seg_x     [seg_n - 1][Hv][dv][dk] bf16: X_s, the state at the start of
-//             segment s (X_1 = F_0, X_{s+1} = F_s + X_s Phi_s, formed in fp32),
-//             rounded for the fix-up's bf16 products; X_{seg_n} is the final
-//             state (fp32);
-//   seg_out   the identity chains' outputs r_t: [T][Hv][dk] bf16;
-//   out       o of every token, [T][Hv][dv] bf16, corrected in place, and
-//             for a gated layer (z != NULL) normalised there for the tokens of
-//             segments 1.. (the gated-norm kernel takes segment 0's).
-struct SegArgs {
-    const float* seg_state; void* seg_x; float* final_state;
-    const void* seg_out; void* out;
-    const void* z; const void* norm_w; float norm_eps;
-    int32_t T, Hv, seg_n, seg_chunks;
-};
 // sequences up to which the chunk table also orders them by length
 constexpr int kOrderMaxSeqs = 1024;
 
@@ -105,6 +87,27 @@ struct ConvStateArgs {
     int32_t T, N, Hk, Hv;
 };
 
+// Composition and output fix-up of the segment-parallel sweep.
+//   seg_state [2 seg_n - 1][Hv][dv][dk] fp32: rows 0..seg_n-1 the segments'
+//             final states from their own start (F_s), rows seg_n.. the maps
+//             Phi_s of segments s = 1..seg_n-1;
+//   seg_x     [seg_n - 1][Hv][dv][dk] bf16: X_s, the state at the start of
+//             segment s (X_1 = F_0, X_{s+1} = F_s + X_s Phi_s, formed in fp32),
+//             rounded for the fix-up's bf16 products; X_{seg_n} is the final
+//             state (fp32);
+//   seg_out   the identity chains' outputs r_t: [T][Hv][dk] bf16;
+//   out       o of every token, [T][Hv][dv] bf16, corrected in place (tokens
+//             of segments 1..) and, for a gated layer (z != NULL), normalised
+//             there (every token).
+// The fix-up's grid: n_fix workgroups of (chunk, value head), then, when
+// cs.conv_state_out != NULL, the conv-state copy of the one sequence.
+struct SegArgs {
+    const float* seg_state; void* seg_x; float* final_state;
+    const void* seg_out; void* out;
+    const void* z; const void* norm_w; float norm_eps;
+    int32_t T, Hv, seg_n, seg_chunks, n_fix;
+    ConvStateArgs cs;
+};
 // Prep-to-sweep hand-off of a pipelined launch (prep and sweep in one grid).
 // Epochs are even.  ready[c * Hk + hk] == epoch or epoch + 1 once prep unit
 // (chunk slot c, key head hk) is published: epoch + 1 when its fragments are

@@ -1883,27 +1883,30 @@ __global__ __launch_bounds__(512) void gdn_seg_compose_kernel(SegArgs a) {
     }
 }
 
-// The later segments' outputs: o_t = o'_t + X_s r_t, then (gated) the z-gated
-// RMSNorm, out = o / sqrt(mean o^2 + eps) * w * SiLU(z), in place of o'.
-// Workgroup: value head h and up to kSegFixChunks chunks of segments >= 1;
-// wave w takes token tile w (16 tokens) of each chunk over all 128 dv rows:
-// o^T (dv x tokens) gains X_s (dv x dk) R^T (dk x tokens), R the identity
-// chain's outputs, on bf16 MFMA with X_s staged in LDS as bf16.  K = dk in
-// four blocks of 32, of which lane (l16, g4) supplies dk 32 p + 8 g4 .. + 7
-// of its row in both operands; accumulator tile dt of lane (l16, g4) then
-// holds dv 16 dt + 4 g4 .. + 3 of token l16, so a token's sum of squares is
-// the lane's own 32 values plus those of lanes l16 + 16 j.
-constexpr int kSegFixChunks = 1;
+// The outputs: o_t = o'_t + X_s r_t for the tokens of segments s >= 1, then
+// (gated) the z-gated RMSNorm of every token, out = o / sqrt(mean o^2 + eps)
+// * w * SiLU(z), in place of o'.  Workgroup (chunk c, value head h), four
+// waves; wave w takes token tile w (16 tokens) over all 128 dv rows: o^T (dv
+// x tokens) gains X_s (dv x dk) R^T (dk x tokens), R the identity chain's
+// outputs, on bf16 MFMA with X_s staged in LDS as bf16.  K = dk in four
+// blocks of 32, of which lane (l16, g4) supplies dk 32 p + 8 g4 .. + 7 of its
+// row in both operands; accumulator tile dt of lane (l16, g4) then holds dv
+// 16 dt + 4 g4 .. + 3 of token l16, so a token's sum of squares is the lane's
+// own 32 values plus those of lanes l16 + 16 j.  Workgroups from n_fix on
+// copy the conv state out (the prep, its only reader, has finished).
 __global__ __launch_bounds__(256) void gdn_seg_fixup_kernel(SegArgs a) {
+    if ((int)blockIdx.x >= a.n_fix) {
+        conv_state_channel<uint16_t>(a.cs, 0, ((int)blockIdx.x - a.n_fix) * 256 + (int)threadIdx.x);
+        return;
+    }
     constexpr int kXLd = kD + 8;   // bf16 row stride of X_s in LDS (16-byte reads of 16 rows spread over the banks)
     __shared__ __attribute__((aligned(16))) uint16_t Xs[kD * kXLd];
-    const int h = (int)(blockIdx.x % (unsigned)a.Hv);
-    const int c0 = a.seg_chunks + kSegFixChunks * (int)(blockIdx.x / (unsigned)a.Hv);
-    const int C = (a.T + kChunk - 1) / kChunk;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l16 = lane & 15, g4 = lane >> 4;
-    const uint16_t* R = static_cast<const uint16_t*>(a.seg_out);
-    uint16_t* O = static_cast<uint16_t*>(a.out);
+    const int h = (int)(blockIdx.x % (unsigned)a.Hv), c = (int)(blockIdx.x / (unsigned)a.Hv);
+    const int s = c / a.seg_chunks;   // uniform
     const uint16_t* Z = static_cast<const uint16_t*>(a.z);
+    if (s == 0 && Z == nullptr) return;   // first segment, no norm: o' is the output
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l16 = lane & 15, g4 = lane >> 4;
+    uint16_t* O = static_cast<uint16_t*>(a.out);
     float w[8][4];   // norm weight of this lane's dv 16 dt + 4 g4 + r
     if (Z != nullptr) {
         const uint16_t* nw = static_cast<const uint16_t*>(a.norm_w);
@@ -1914,65 +1917,64 @@ __global__ __launch_bounds__(256) void gdn_seg_fixup_kernel(SegArgs a) {
             for (int r = 0; r < 4; ++r) w[dt][r] = bf16_bits_to_f32(v[r]);
         }
     }
-    int loaded = 0;   // segment whose X is in LDS (0: none)
-    for (int c = c0; c < min(c0 + kSegFixChunks, C); ++c) {
-        const int s = c / a.seg_chunks;   // uniform
-        if (s != loaded) {
-            __syncthreads();   // every wave is done with the previous X
-            const uint16_t* X = static_cast<const uint16_t*>(a.seg_x) + ((size_t)(s - 1) * a.Hv + h) * (size_t)(kD * kD);
-            for (int i = threadIdx.x; i < kD * kD / 8; i += 256) {
-                const int row = i / (kD / 8), c8 = 8 * (i % (kD / 8));
-                *reinterpret_cast<u16x8*>(Xs + row * kXLd + c8) = *reinterpret_cast<const u16x8*>(X + (size_t)row * kD + c8);
-            }
-            __syncthreads();
-            loaded = s;
+    if (s > 0) {
+        const uint16_t* X = static_cast<const uint16_t*>(a.seg_x) + ((size_t)(s - 1) * a.Hv + h) * (size_t)(kD * kD);
+        for (int i = threadIdx.x; i < kD * kD / 8; i += 256) {
+            const int row = i / (kD / 8), c8 = 8 * (i % (kD / 8));
+            *reinterpret_cast<u16x8*>(Xs + row * kXLd + c8) = *reinterpret_cast<const u16x8*>(X + (size_t)row * kD + c8);
         }
-        const int t = c * kChunk + 16 * wave + l16;   // this lane's token
-        const bool ok = t < a.T;
-        const size_t row = ((size_t)t * a.Hv + h) * kD;
-        typedef Frag<bf16> F;
-        F rb[4];
+        __syncthreads();
+    }
+    const int t = c * kChunk + 16 * wave + l16;   // this lane's token
+    const bool ok = t < a.T;
+    const size_t row = ((size_t)t * a.Hv + h) * kD;
+    typedef Frag<bf16> F;
+    F rb[4];
+    if (s > 0) {
+        const uint16_t* R = static_cast<const uint16_t*>(a.seg_out);
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
             if (ok) rb[p].v = *reinterpret_cast<const bf16x8*>(R + row + 32 * p + 8 * g4);
             else rb[p].v = bf16x8{};
         }
-        f32x4 o[8];
-        float ss = 0.f;
+    }
+    f32x4 o[8];
+    float ss = 0.f;
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int dt = 0; dt < 8; ++dt) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        if (s > 0) {
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
                 F xa;
                 xa.v = *reinterpret_cast<const bf16x8*>(Xs + (16 * dt + l16) * kXLd + 32 * p + 8 * g4);
                 mma(acc, xa, rb[p]);
             }
-            const u16x4 ov = ok ? *reinterpret_cast<const u16x4*>(O + row + 16 * dt + 4 * g4) : u16x4{0, 0, 0, 0};
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                o[dt][r] = bf16_bits_to_f32(ov[r]) + acc[r];
-                ss = fmaf(o[dt][r], o[dt][r], ss);
-            }
         }
-        if (Z != nullptr) {
-            ss += __shfl_xor(ss, 16);
-            ss += __shfl_xor(ss, 32);
-            const float rr = rsqrt_f32(ss * (1.0f / kD) + a.norm_eps);
+        const u16x4 ov = ok ? *reinterpret_cast<const u16x4*>(O + row + 16 * dt + 4 * g4) : u16x4{0, 0, 0, 0};
 #pragma unroll
-            for (int dt = 0; dt < 8; ++dt) {
-                const u16x4 zv = ok ? *reinterpret_cast<const u16x4*>(Z + row + 16 * dt + 4 * g4) : u16x4{0, 0, 0, 0};
-#pragma unroll
-                for (int r = 0; r < 4; ++r) o[dt][r] = o[dt][r] * rr * w[dt][r] * silu_f32(bf16_bits_to_f32(zv[r]));
-            }
+        for (int r = 0; r < 4; ++r) {
+            o[dt][r] = bf16_bits_to_f32(ov[r]) + acc[r];
+            ss = fmaf(o[dt][r], o[dt][r], ss);
         }
-        if (ok) {
+    }
+    if (Z != nullptr) {
+        ss += __shfl_xor(ss, 16);
+        ss += __shfl_xor(ss, 32);
+        const float rr = rsqrt_f32(ss * (1.0f / kD) + a.norm_eps);
 #pragma unroll
-            for (int dt = 0; dt < 8; ++dt)
-                *reinterpret_cast<u16x4*>(O + row + 16 * dt + 4 * g4) =
-                    u16x4{f32_to_bf16_bits(o[dt][0]), f32_to_bf16_bits(o[dt][1]), f32_to_bf16_bits(o[dt][2]),
-                          f32_to_bf16_bits(o[dt][3])};
+        for (int dt = 0; dt < 8; ++dt) {
+            const u16x4 zv = ok ? *reinterpret_cast<const u16x4*>(Z + row + 16 * dt + 4 * g4) : u16x4{0, 0, 0, 0};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[dt][r] = o[dt][r] * rr * w[dt][r] * silu_f32(bf16_bits_to_f32(zv[r]));
         }
+    }
+    if (ok) {
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+            *reinterpret_cast<u16x4*>(O + row + 16 * dt + 4 * g4) =
+                u16x4{f32_to_bf16_bits(o[dt][0]), f32_to_bf16_bits(o[dt][1]), f32_to_bf16_bits(o[dt][2]),
+                      f32_to_bf16_bits(o[dt][3])};
     }
 }
 
@@ -2452,11 +2454,16 @@ static hipError_t launch_seg_compose(const PrefillPlan& p, int P, int chunks, hi
     return hipGetLastError();
 }
 
+// Fix-up and gated norm of every (chunk, value head), then the conv-state copy.
 static hipError_t launch_seg_fixup(const PrefillPlan& p, int P, int chunks, hipStream_t s) {
-    const int64_t blocks = (int64_t)(p.chunk_slots - chunks + kSegFixChunks - 1) / kSegFixChunks * p.sweep.Hv;
-    if (blocks <= 0) return hipSuccess;
-    if (blocks > (int64_t)INT32_MAX) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(gdn_seg_fixup_kernel, dim3((unsigned)blocks), dim3(256), 0, s, seg_args(p, P, chunks));
+    SegArgs g = seg_args(p, P, chunks);
+    const int64_t fix = (int64_t)p.chunk_slots * p.sweep.Hv;
+    const int Cch = 2 * p.conv_state.Hk * kD + p.conv_state.Hv * kD;
+    const int64_t conv = p.conv_state.conv_state_out != nullptr ? (Cch + 255) / 256 : 0;
+    if (fix + conv > (int64_t)INT32_MAX) return hipErrorInvalidConfiguration;
+    g.n_fix = (int32_t)fix;
+    g.cs = p.conv_state;
+    hipLaunchKernelGGL(gdn_seg_fixup_kernel, dim3((unsigned)(fix + conv)), dim3(256), 0, s, g);
     return hipGetLastError();
 }
 
@@ -2614,9 +2621,10 @@ static hipError_t run_serial(const PrefillPlan& p, bool pipe, hipStream_t s, Ker
         GDN_TRY(rec.begin(GDN_STAGE_SEG_COMPOSE, s));
         GDN_TRY(launch_seg_compose(p, P, seg_chunks, s));
         GDN_TRY(rec.end(s));
-        GDN_TRY(rec.begin(GDN_STAGE_SEG_FIXUP, s));
+        GDN_TRY(rec.begin(GDN_STAGE_SEG_FIXUP, s));   // with the gated norm and the conv-state copy
         GDN_TRY(launch_seg_fixup(p, P, seg_chunks, s));
         GDN_TRY(rec.end(s));
+        return hipSuccess;
     } else {
         if (p.chunk_slots > 0) {
             GDN_TRY(rec.begin(GDN_STAGE_CHUNK_PREP, s));
@@ -2627,10 +2635,9 @@ static hipError_t run_serial(const PrefillPlan& p, bool pipe, hipStream_t s, Ker
         GDN_TRY(launch_sweep(p, s));
         GDN_TRY(rec.end(s));
     }
-    if (p.gated && p.total_tokens > 0) {   // segments: the fix-up normalised the later segments' tokens
+    if (p.gated && p.total_tokens > 0) {
         GDN_TRY(rec.begin(GDN_STAGE_GATED_NORM, s));
-        GDN_TRY(launch_norm<IO>(p, 0, P > 1 ? std::min<int64_t>(p.total_tokens, (int64_t)kChunk * seg_chunks)
-                                             : p.total_tokens, s));
+        GDN_TRY(launch_norm<IO>(p, 0, p.total_tokens, s));
         GDN_TRY(rec.end(s));
     }
     if (p.conv_state.conv_state_out != nullptr) {
@@ -2673,7 +2680,8 @@ hipError_t launch_prefill(const PrefillPlan& p, hipStream_t stream, KernelRecord
     const bool seg = !pipe && p.io_bf16 && seg_count(p, &seg_chunks) > 1;
     const int n = (p.prep.cu != nullptr) +
                   (pipe ? 1
-                        : (p.chunk_slots > 0) + 1 + (seg ? 2 : 0) + (p.gated && p.total_tokens > 0) +
+                  : seg  ? 4   // prep, sweep, compose, fix-up (with the gated norm and the conv state)
+                        : (p.chunk_slots > 0) + 1 + (p.gated && p.total_tokens > 0) +
                               (p.conv_state.conv_state_out != nullptr));
     if (rec.events != nullptr && n > rec.max) return hipErrorInvalidValue;
     GDN_TRY(rec.call_begin(stream));

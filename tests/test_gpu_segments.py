@@ -108,7 +108,20 @@ def test_segments_c1_all_heads():
     say(f"segments, C1: {check_prefill(p, x, segments=True)}")
 
 
+def test_segments_c1_shape_weak_decay():
+    """16 key / 32 value heads, 4,096 tokens, log-decay scaled by 0.01 and a
+    seeded state: the first segment's final state still weighs on the second
+    segment's outputs, so the correction is exercised at full width (with the
+    workloads' decay it is negligible after a few tokens)."""
+    p = gs.Problem("seg-c1-weak", [4096], init_state_std=0.01, conv_state_std=0.01, g_scale=0.01,
+                   seed=4096)
+    x = gs.generate(p)
+    assert SEG_COMPOSE in stages(p, x)
+    say(f"segments, 16 / 32 heads, weak decay: {check_prefill(p, x, batch=16, segments=True)}")
+
+
 def test_segments_c2_all_heads():
     p = gs.configs()["C2"]
     x = gs.generate(p)
+    assert SEG_COMPOSE in stages(p, x)
     say(f"segments, C2: {check_prefill(p, x, batch=16, segments=True)}")
