@@ -341,6 +341,39 @@ def test_linearity_in_values_and_state():
     np.testing.assert_allclose(f3, a * f1 + b * f2, rtol=1e-12, atol=1e-12)
 
 
+@pytest.mark.parametrize("weak", [False, True])
+def test_segment_decomposition(weak):
+    """One sequence cut into three segments and recomposed from per-segment
+    runs: every segment from a zero state (F_s, o'_t) and from the identity
+    with v = 0 (Phi_s, r_t: the rows of the state are the basis vectors e_r,
+    so dv = dk), then X_0 = S0, X_{s+1} = F_s + X_s Phi_s and o_t = o'_t +
+    X_s r_t give the whole run's outputs and final state.  The update is
+    linear in the state (Gated DeltaNet paragraph of the hyper.ai story), and
+    this is the form the segment-parallel prefill computes."""
+    rng = np.random.default_rng(31 + weak)
+    d, T = 16, 90
+    bounds = [0, 30, 55, 90]
+    q, k = unit_rows(rng, T, d), unit_rows(rng, T, d)
+    g, beta = rand_gates(rng, T, weak)
+    v = rng.standard_normal((T, d))
+    S0 = 0.5 * rng.standard_normal((d, d))
+    o_all, f_all, _ = run1(q, k, v, g, beta, S0)
+    X, outs, part = S0, [], []
+    for s in range(3):
+        sl = slice(bounds[s], bounds[s + 1])
+        n = bounds[s + 1] - bounds[s]
+        o_z, F, _ = run1(q[sl], k[sl], v[sl], g[sl], beta[sl], np.zeros((d, d)))
+        r, Phi, _ = run1(q[sl], k[sl], np.zeros((n, d)), g[sl], beta[sl], np.eye(d))
+        corr = r.reshape(n, d) @ X.T
+        part.append(np.linalg.norm(corr) / np.linalg.norm(o_z))
+        outs.append(o_z.reshape(n, d) + corr)
+        X = F.reshape(d, d) + X @ Phi.reshape(d, d)
+    np.testing.assert_allclose(np.concatenate(outs), o_all.reshape(T, d), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(X, f_all.reshape(d, d), rtol=1e-10, atol=1e-12)
+    # the start state's part is not negligible here (a dropped X_s r_t term fails)
+    assert min(part) > 1e-3, part
+
+
 def _rand_layer(rng, T, Hk, Hv, dk, dv, K=4):
     Cch = 2 * Hk * dk + Hv * dv
     return dict(q=rng.standard_normal((T, Hk, dk)), k=rng.standard_normal((T, Hk, dk)),
