@@ -330,24 +330,29 @@ def bench_options(args, hip, pres):
     # one GPU's share of the C1 layer under 2-, 4- and 8-way head parallelism
     # (8 / 4 / 2 key heads, twice as many value heads, 4,096 tokens): the
     # default call (segment-parallel form) against the plain separate launches
+    # (and of the 65,536-token layer with seeded states under 8-way parallelism)
     shares = {}
-    for tp, Hk in ((2, 8), (4, 4), (8, 2)):
-        ps = gs.Problem(f"tp{tp}-share", [p.T], Hk=Hk, Hv=2 * Hk, seed=1001 + tp)
-        log(f"[bench] TP-{tp} share: {Hk} key / {2 * Hk} value heads, {p.T} tokens")
+    for tp, Hk, T, name in ((2, 8, p.T, "tp2"), (4, 4, p.T, "tp4"), (8, 2, p.T, "tp8"),
+                            (8, 2, 65536, "tp8_65536")):
+        states = dict(init_state_std=0.01, conv_state_std=0.01) if T != p.T else {}
+        ps = gs.Problem(f"{name}-share", [T], Hk=Hk, Hv=2 * Hk, seed=1001 + tp + T, **states)
+        log(f"[bench] TP-{tp} share: {Hk} key / {2 * Hk} value heads, {T} tokens")
         xs = gs.generate(ps)
-        row = {"workload": f"prefill, 1 sequence of {p.T} tokens, {Hk} key / {2 * Hk} value heads "
-                           f"(one GPU's share of 16 / 32 under {tp}-way head parallelism)"}
+        row = {"workload": f"prefill, 1 sequence of {T} tokens, {Hk} key / {2 * Hk} value heads "
+                           f"(one GPU's share of 16 / 32 under {tp}-way head parallelism)"
+                           + (", seeded states" if states else "")}
         for label, sep in (("default", False), ("separate_launches", True)):
             calls = [PrefillCall(xs, Hk=Hk, Hv=2 * Hk, io_bf16=True, separate_launches=sep)
                      for _ in range(args.buffer_sets)]
             if label == "default":
                 row["launch"] = launch_form(hip, calls[0])
-            t = time_calls(hip, [c.run for c in calls], args.steps, args.warmup)
-            row[label] = {"us": round(t * 1e6, 2), "tokens_per_s": round(p.T / t, 1),
-                          "flop_frac_dense_tile": round(FLOP_LAYER * p.T * 2 * Hk / t / MFMA_BF16_PEAK, 4)}
+            steps = args.steps if T == p.T else max(5, args.steps // 5)
+            t = time_calls(hip, [c.run for c in calls], steps, min(args.warmup, steps))
+            row[label] = {"us": round(t * 1e6, 2), "tokens_per_s": round(T / t, 1),
+                          "flop_frac_dense_tile": round(FLOP_LAYER * T * 2 * Hk / t / MFMA_BF16_PEAK, 4)}
             del calls
         row["speedup"] = round(row["separate_launches"]["us"] / row["default"]["us"], 3)
-        shares[f"tp{tp}"] = row
+        shares[name] = row
     return {"prefill_pool_bf16_snapshots": opts, "verify": ver, "tp_shares": shares}
 
 

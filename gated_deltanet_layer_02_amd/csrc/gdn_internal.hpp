@@ -74,7 +74,7 @@ struct SweepArgs {
     int32_t seg_n, seg_chunks;
 };
 // Segments per call at most, and the least chunks of a segment.
-constexpr int kSegMax = 8;
+constexpr int kSegMax = 16;
 constexpr int kSegMinChunks = 4;
 
 // sequences up to which the chunk table also orders them by length

@@ -32,6 +32,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <atomic>
 #include <type_traits>
 
@@ -2363,17 +2364,20 @@ static int sweep_blocks(const PrefillPlan& p) {
     return sweep_grid(p.io_bf16 ? SweepCfg::kGroups : 8 / kF32SW, a.N, a.Hk, a.Hv);
 }
 
-// Segments of a segment-parallel call (GDN_FLAG_SEGMENTS, one qualifying
-// sequence): as many as fit one round of CUs with their identity chains
-// (2 P - 1 sweep sequences), at most kSegMax, each at least kSegMinChunks
-// chunks long; 1 when the form does not apply.  *chunks: chunks per segment
-// (every segment non-empty: P = ceil(C / chunks)).
+// Segments of a segment-parallel call (one qualifying sequence of C chunks):
+// the time goes as C / P sweep steps (~2 us each) plus P - 1 composition
+// steps (~1.5 us each), least near P = sqrt(4 C / 3) (C = 64: 8; C = 256:
+// 16); P is that, at most kSegMax and at most what fits one round of CUs with
+// the identity chains (2 P - 1 sweep sequences), with segments of at least
+// kSegMinChunks chunks; 1 when the form does not apply.  *chunks: chunks per
+// segment (every segment non-empty: P = ceil(C / chunks)).
 static int seg_count(const PrefillPlan& p, int* chunks) {
     *chunks = p.chunk_slots;
     if (!p.seg_ok || p.chunk_slots < 2 * kSegMinChunks) return 1;
     const int cus = device_cus();
+    const int want = std::max(2, (int)std::lround(std::sqrt(4.0 * p.chunk_slots / 3.0)));
     int best = 1;
-    for (int P = 2; P <= kSegMax; ++P)
+    for (int P = 2; P <= std::min(kSegMax, want); ++P)
         if (sweep_grid(SweepCfg::kGroups, 2 * P - 1, p.sweep.Hk, p.sweep.Hv) <= cus &&
             P * kSegMinChunks <= p.chunk_slots)
             best = P;

@@ -186,8 +186,9 @@ gdn_status gdn_prefill_workspace_size(const gdn_desc* d, size_t* bytes);
  * b_t v_t k_t^T), so over a run of chunks the state obeys S_end = S_start Phi
  * + S'_end and every output o_t = o'_t + S_start r_t, where S'_end and o'_t
  * come from a zero start and Phi, r_t from the identity start with v = 0.
- * The chunks are cut into P segments (P from 2 to 8, as many as one round of
- * the device's CUs takes); the sweep runs every segment from a zero state
+ * The chunks are cut into P segments (P from 2 to 16: about sqrt(4 C / 3) for
+ * C chunks, at most as many as one round of the device's CUs takes with
+ * their identity chains); the sweep runs every segment from a zero state
  * (the first from initial_state) beside one such identity chain per later
  * segment, all at once, then one kernel chains the segments' start states
  * and the final state, and one adds S_start r_t to the outputs of the later

@@ -53,13 +53,13 @@ def test_workspace_size_grows_with_tokens():
 
 
 def test_workspace_size_with_segments():
-    """GDN_FLAG_SEGMENTS adds, for one sequence, room for up to 8 segments:
-    15 + 7 state-sized buffers of Hv heads and the identity chains' bf16
+    """GDN_FLAG_SEGMENTS adds, for one sequence, room for up to 16 segments:
+    31 + 15 state-sized buffers of Hv heads and the identity chains' bf16
     outputs of every token; descriptors of several sequences are unchanged."""
     T, Hv = 4096, 32
     plain = gdn.gdn_prefill_workspace_size(B.make_desc(1, T))
     seg = gdn.gdn_prefill_workspace_size(B.make_desc(1, T, segments=True))
-    extra = (15 + 7) * Hv * 128 * 128 * 4 + T * Hv * 128 * 2
+    extra = (31 + 15) * Hv * 128 * 128 * 4 + T * Hv * 128 * 2
     assert extra <= seg - plain <= extra + 3 * 256
     assert gdn.gdn_prefill_workspace_size(B.make_desc(3, T, segments=True)) == \
         gdn.gdn_prefill_workspace_size(B.make_desc(3, T))
@@ -68,7 +68,7 @@ def test_workspace_size_with_segments():
     few = dict(num_k_heads=2, num_v_heads=4)
     grow = gdn.gdn_prefill_workspace_size(B.make_desc(1, T, **few)) - \
         gdn.gdn_prefill_workspace_size(B.make_desc(1, T, separate_launches=True, **few))
-    assert grow >= (15 + 7) * 4 * 128 * 128 * 4 + T * 4 * 128 * 2
+    assert grow >= (31 + 15) * 4 * 128 * 128 * 4 + T * 4 * 128 * 2
     assert gdn.gdn_prefill_workspace_size(B.make_desc(1, 2047, **few)) == \
         gdn.gdn_prefill_workspace_size(B.make_desc(1, 2047, separate_launches=True, **few))
 

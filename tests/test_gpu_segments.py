@@ -90,15 +90,26 @@ def test_segments_tp8_share():
 @pytest.mark.parametrize("Hk,Hv,T", [(4, 8, 2048), (8, 16, 4096)])
 def test_segments_by_default_for_few_heads(Hk, Hv, T):
     """Without the flag, one sequence of >= 32 chunks with <= 16 value heads
-    takes the segment form (2,048 tokens at 4 key / 8 value heads: eight
-    segments of 4 chunks; 4,096 at 8 / 16: four of 16), and separate launches
-    asked for alone keep the plain form."""
+    takes the segment form (2,048 tokens at 4 key / 8 value heads: seven
+    segments of 5 chunks, the last of 2; 4,096 at 8 / 16: four of 16), and
+    separate launches asked for alone keep the plain form."""
     p = gs.Problem(f"seg-default-{Hk}x{Hv}", [T], Hk=Hk, Hv=Hv, init_state_std=0.01,
                    conv_state_std=0.01, seed=3000 + Hv)
     x = gs.generate(p)
     assert SEG_COMPOSE in stages(p, x, segments=False)
     assert SEG_COMPOSE not in stages(p, x, segments=False, separate_launches=True)
     say(f"segments by default, {Hk}x{Hv}: {check_prefill(p, x)}")
+
+
+def test_segments_tp8_share_long_context():
+    """One GPU's share of the 65,536-token layer under eight-way head
+    parallelism (2 key / 4 value heads, seeded states), the default call:
+    sixteen segments of 64 chunks."""
+    p = gs.Problem("seg-tp8-65k", [65536], Hk=2, Hv=4, init_state_std=0.01, conv_state_std=0.01,
+                   seed=6553)
+    x = gs.generate(p)
+    assert SEG_COMPOSE in stages(p, x, segments=False)
+    say(f"segments, TP-8 share, 65,536 tokens: {check_prefill(p, x)}")
 
 
 def test_segments_c1_all_heads():
