@@ -78,7 +78,8 @@ typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
  * they leave the conv (or as given, without conv); scale is still applied. */
 #define GDN_FLAG_L2NORM_QK 0x1u
 /* Prefill launch form (see gdn_prefill, "Launches"): never the pipelined
- * single launch, always the separate kernels one after another. */
+ * single launch, always separate kernels one after another (the plain ones,
+ * or with GDN_FLAG_SEGMENTS also given, the segment-parallel ones). */
 #define GDN_FLAG_SEPARATE_LAUNCHES 0x2u
 /* Pipelined prefill: every prep unit writes its results back to memory
  * before publishing them, instead of leaving them in the L2 of the XCD that
@@ -128,7 +129,11 @@ gdn_status gdn_prefill_wait_status(const void* workspace, size_t workspace_bytes
                                    hipStream_t stream, int32_t* failed);
 
 /* Bytes of device workspace gdn_prefill needs for descriptor d (a bound that
- * depends on N and T_total only through total_tokens / 64 + N chunks). */
+ * depends on N and T_total only through total_tokens / 64 + N chunks, plus,
+ * for a descriptor the segment-parallel form may serve (one sequence, bf16
+ * io, fp32 state; GDN_FLAG_SEGMENTS, or at most 16 value heads and at least
+ * 2,048 tokens without GDN_FLAG_SEPARATE_LAUNCHES), 46 state-sized buffers
+ * and 256 bytes per token and value head). */
 gdn_status gdn_prefill_workspace_size(const gdn_desc* d, size_t* bytes);
 
 
