@@ -444,9 +444,14 @@ template <> struct PrepStore<true> {
 // next value head's v rows, and the K K^T / K Q^T cells formed from fragments
 // read when each cell needs them, so that the unit fits 168 VGPRs and three
 // units share a CU.
-template <class IO, bool kConv, bool kCo = false, bool kLean = false, bool kNT = false>
+// kOneV (separate prep kernel, few units): the unit takes value head
+// hk * group + vh_only only, repeating its key head's q / k phases, and the
+// unit of the key head's first value head stores the key head's Q and K^T
+// fragments; two such units take about two thirds of one whole unit's time.
+template <class IO, bool kConv, bool kCo = false, bool kLean = false, bool kNT = false, bool kOneV = false>
 __device__ __forceinline__ bool prep_unit(const PrepArgs& a, int c, int hk, unsigned char* smem, int tid,
-                                          const PipeSync* ps = nullptr, bool* local = nullptr) {
+                                          const PipeSync* ps = nullptr, bool* local = nullptr,
+                                          int vh_only = 0) {
     typedef typename MathOf<IO>::T MT;
     typedef Frag<MT> F;
     static_assert(!kLean || sizeof(MT) == 2, "the lean layout is for bf16 operands");
@@ -473,7 +478,8 @@ __device__ __forceinline__ bool prep_unit(const PrepArgs& a, int c, int hk, unsi
     const IO* csin = static_cast<const IO*>(a.conv_state_in);
 
     // ---- 1. q and k: conv + SiLU, L2 normalisation, scale ----
-    const int h0 = hk * group;
+    const int vh_lo = kOneV ? vh_only : 0, vh_hi = kOneV ? vh_only + 1 : group;   // value heads of the unit
+    const int h0 = hk * group + vh_lo;
     // v rows are prefetched one phase early on interior chunks (bf16 rows:
     // the fp32 layer keeps its registers for the math instead)
     // interior chunk: the conv window of every token lies inside the sequence,
@@ -557,7 +563,7 @@ __device__ __forceinline__ bool prep_unit(const PrepArgs& a, int c, int hk, unsi
             F fr;
 #pragma unroll
             for (int j = 0; j < 8; ++j) fr.v[j] = sm.qrow(row)[kb + kidx(g4, j)];
-            St::frag(KB + (kKB_Q + fi) * 64, lane, fr);
+            if (!kOneV || vh_lo == 0) St::frag(KB + (kKB_Q + fi) * 64, lane, fr);
         }
         {   // K^T: rows = dk (tile fi / 2), K = token block fi % 2
             const int row = 16 * (fi >> 1) + l16, kb = 32 * (fi & 1);
@@ -567,7 +573,7 @@ __device__ __forceinline__ bool prep_unit(const PrepArgs& a, int c, int hk, unsi
                 const int t = kb + kidx(g4, j);
                 fr.v[j] = sm.ktrow(row)[tsw(row, t >> 2) + (t & 3)];
             }
-            St::frag(KB + (kKB_KT + fi) * 64, lane, fr);
+            if (!kOneV || vh_lo == 0) St::frag(KB + (kKB_KT + fi) * 64, lane, fr);
         }
     }
     // K K^T and K Q^T by 16x16 cells (token tile tt, tile ti), ti <= tt: the ten
@@ -694,7 +700,7 @@ __device__ __forceinline__ bool prep_unit(const PrepArgs& a, int c, int hk, unsi
 
     // ---- 3. per value head of this key head ----
 #pragma unroll 1
-    for (int vh = 0; vh < group; ++vh) {
+    for (int vh = vh_lo; vh < vh_hi; ++vh) {
         const int h = hk * group + vh;
         const size_t cv = (size_t)c * Hv + h;
         F* VB = static_cast<F*>(a.VB) + cv * kVBUnits * 64;   // unit base (uniform)
@@ -722,7 +728,7 @@ __device__ __forceinline__ bool prep_unit(const PrepArgs& a, int c, int hk, unsi
                 }
             }
             const float gcur = gl, bcur = bl;
-            if (vh + 1 < group) {
+            if (vh + 1 < vh_hi) {
                 if (inner)
                     xv.load_inner(v, Hv, (h + 1) * kD + 8 * cg, 2 * Hk * kD + (h + 1) * kD + 8 * cg, t0,
                                   tq, conv_w);
@@ -890,6 +896,20 @@ __global__ __launch_bounds__(256, prep_lean<IO>() ? 3 : 2) void gdn_chunk_prep_k
     int c, hk;
     prep_slot(blockIdx.x, slots, a.Hk, c, hk);
     prep_unit<IO, kConv, false, prep_lean<IO>(), kNT>(a, c, hk, gdn_prep_smem, threadIdx.x);
+}
+
+// The same with one value head per workgroup (kOneV): workgroup w takes the
+// unit of workgroup w / group of the kernel above and its value head w %
+// group.  For few units (at most one per CU), where a unit's latency, not the
+// device's throughput, sets the kernel's time.
+template <class IO, bool kConv>
+__global__ __launch_bounds__(256, prep_lean<IO>() ? 3 : 2) void gdn_chunk_prep_v_kernel(PrepArgs a, int32_t slots) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char gdn_prep_smem[];
+    const int group = a.Hv / a.Hk;
+    int c, hk;
+    prep_slot((int)blockIdx.x / group, slots, a.Hk, c, hk);
+    prep_unit<IO, kConv, false, prep_lean<IO>(), false, true>(a, c, hk, gdn_prep_smem, threadIdx.x, nullptr,
+                                                              nullptr, (int)blockIdx.x % group);
 }
 
 // ===========================================================================
@@ -2292,6 +2312,12 @@ static hipError_t allow_dynamic_lds(const void* kern, unsigned bytes) {
     static const hipError_t bf16_noconv_nt = hipFuncSetAttribute(
         reinterpret_cast<const void*>(gdn_chunk_prep_kernel<uint16_t, false, true>),
         hipFuncAttributeMaxDynamicSharedMemorySize, prep_smem_bytes<uint16_t>());
+    static const hipError_t bf16_conv_v = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(gdn_chunk_prep_v_kernel<uint16_t, true>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, prep_smem_bytes<uint16_t>());
+    static const hipError_t bf16_noconv_v = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(gdn_chunk_prep_v_kernel<uint16_t, false>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, prep_smem_bytes<uint16_t>());
     static const hipError_t f32_conv = hipFuncSetAttribute(
         reinterpret_cast<const void*>(gdn_chunk_prep_kernel<float, true>),
         hipFuncAttributeMaxDynamicSharedMemorySize, prep_smem_bytes<float>());
@@ -2324,7 +2350,8 @@ static hipError_t allow_dynamic_lds(const void* kern, unsigned bytes) {
         kF32Lds);
     (void)kern;
     (void)bytes;
-    for (hipError_t e : {bf16_conv, bf16_noconv, bf16_conv_nt, bf16_noconv_nt, f32_conv, f32_noconv, sweep,
+    for (hipError_t e : {bf16_conv, bf16_noconv, bf16_conv_nt, bf16_noconv_nt, bf16_conv_v, bf16_noconv_v,
+                         f32_conv, f32_noconv, sweep,
                          sweep_split, sweep_seg, pipe_conv, pipe_noconv, pipe_conv_lean, pipe_noconv_lean,
                          sweep_f32})
         if (e != hipSuccess) return e;
@@ -2355,6 +2382,15 @@ static hipError_t launch_prep(const PrefillPlan& p, int slots, hipStream_t s) {
     if (units > (int64_t)(UINT32_MAX / 256)) return hipErrorInvalidConfiguration;
     hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(kern), smem);
     if (e != hipSuccess) return e;
+    // At most one unit per CU (one long sequence with few heads): a unit's
+    // latency sets the kernel's time, so each value head takes a workgroup of
+    // its own (2 key / 4 value heads, 4,096 tokens: 128 units).
+    const int group = p.prep.Hv / p.prep.Hk;
+    if (sizeof(IO) == 2 && !nt && group > 1 && units <= device_cus()) {
+        auto kv = p.conv ? gdn_chunk_prep_v_kernel<IO, true> : gdn_chunk_prep_v_kernel<IO, false>;
+        hipLaunchKernelGGL(kv, dim3((uint32_t)(units * group)), dim3(256), smem, s, p.prep, slots);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(kern, dim3((uint32_t)units), dim3(256), smem, s, p.prep, slots);
     return hipGetLastError();
 }
