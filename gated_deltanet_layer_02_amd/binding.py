@@ -20,6 +20,7 @@ GDN_FLAG_SEPARATE_LAUNCHES = 0x2
 GDN_FLAG_PREP_WRITE_BACK = 0x4
 GDN_FLAG_TEST_WAITS_GIVE_UP = 0x8
 GDN_FLAG_SEGMENTS = 0x10
+GDN_FLAG_PIPELINED = 0x20
 PREFILL_MAX_KERNELS = 64   # kernels a profiled call may record (the caller's choice)
 STAGE_NAMES = {0: "chunk_table", 1: "chunk_prep", 2: "state_sweep", 3: "gated_norm",
                4: "conv_state", 5: "prep_sweep", 6: "seg_compose", 7: "seg_fixup"}
@@ -81,10 +82,11 @@ def make_desc(num_seqs: int, total_tokens: int, num_k_heads: int = 16, num_v_hea
               io_dtype: int = GDN_BF16, state_dtype: int = GDN_F32, scale: float = 1.0,
               l2_eps: float = 1e-6, norm_eps: float = 1e-6, l2norm: bool = True,
               head_dim: int = 128, conv_kernel: int = 4, separate_launches: bool = False,
-              prep_write_back: bool = False, segments: bool = False, flags: int = 0) -> Desc:
+              prep_write_back: bool = False, segments: bool = False, pipelined: bool = False,
+              flags: int = 0) -> Desc:
     f = (GDN_FLAG_L2NORM_QK if l2norm else 0) | (GDN_FLAG_SEPARATE_LAUNCHES if separate_launches else 0) \
         | (GDN_FLAG_PREP_WRITE_BACK if prep_write_back else 0) | (GDN_FLAG_SEGMENTS if segments else 0) \
-        | int(flags)
+        | (GDN_FLAG_PIPELINED if pipelined else 0) | int(flags)
     return Desc(num_seqs=num_seqs, total_tokens=total_tokens, num_k_heads=num_k_heads,
                 num_v_heads=num_v_heads, head_k_dim=head_dim, head_v_dim=head_dim,
                 conv_kernel=conv_kernel, io_dtype=io_dtype, state_dtype=state_dtype,

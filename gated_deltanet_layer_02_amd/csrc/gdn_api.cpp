@@ -43,7 +43,7 @@ gdn_status check_desc_common(const gdn_desc* d) {
     if (d->head_k_dim != gdn::kD || d->head_v_dim != gdn::kD) return GDN_ERR_UNSUPPORTED;
     if (d->conv_kernel != gdn::kConvK) return GDN_ERR_UNSUPPORTED;
     if (d->flags & ~(GDN_FLAG_L2NORM_QK | GDN_FLAG_SEPARATE_LAUNCHES | GDN_FLAG_PREP_WRITE_BACK |
-                     GDN_FLAG_TEST_WAITS_GIVE_UP | GDN_FLAG_SEGMENTS))
+                     GDN_FLAG_TEST_WAITS_GIVE_UP | GDN_FLAG_SEGMENTS | GDN_FLAG_PIPELINED))
         return GDN_ERR_UNSUPPORTED;
     if (d->io_dtype != GDN_F32 && d->io_dtype != GDN_BF16) return GDN_ERR_BAD_DTYPE;
     if (d->state_dtype != GDN_F32 && d->state_dtype != GDN_BF16) return GDN_ERR_BAD_DTYPE;
@@ -78,13 +78,13 @@ uint64_t next_epoch() {
 // are few (Hv <= 16: the plain sweep of one sequence then takes at most 32
 // workgroups, an eighth of the device, and its chain of chunk steps sets the
 // time) and the sequence has at least 32 chunks.  GDN_FLAG_SEPARATE_LAUNCHES
-// alone keeps the plain separate launches.
+// or GDN_FLAG_PIPELINED alone keeps the form it names.
 constexpr int32_t kSegAutoMaxHv = 16;
 constexpr int64_t kSegAutoMinTokens = 32 * gdn::kChunk;
 bool seg_shape(const gdn_desc* d) {
     if (d->num_seqs != 1 || d->io_dtype != GDN_BF16 || d->state_dtype != GDN_F32) return false;
     if (d->flags & GDN_FLAG_SEGMENTS) return true;
-    return !(d->flags & GDN_FLAG_SEPARATE_LAUNCHES) && d->num_v_heads <= kSegAutoMaxHv &&
+    return !(d->flags & (GDN_FLAG_SEPARATE_LAUNCHES | GDN_FLAG_PIPELINED)) && d->num_v_heads <= kSegAutoMaxHv &&
            d->total_tokens >= kSegAutoMinTokens;
 }
 
@@ -177,6 +177,7 @@ gdn_status prefill_impl(const gdn_desc* d, const gdn_prefill_args& x, hipStream_
     gdn::PrefillPlan p{};
     p.io_bf16 = d->io_dtype == GDN_BF16;
     p.allow_pipe = (d->flags & GDN_FLAG_SEPARATE_LAUNCHES) == 0;
+    p.force_pipe = (d->flags & GDN_FLAG_PIPELINED) != 0;
     p.l2_handoff = (d->flags & GDN_FLAG_PREP_WRITE_BACK) == 0;
     p.seg_ok = seg_shape(d) && !varlen && T > 0 && x.state_slots == nullptr && !snaps && L.seg_state != 0;
     p.seg_state = p.seg_ok ? reinterpret_cast<float*>(ws + L.seg_state) : nullptr;

@@ -149,6 +149,7 @@ struct PipeArgs {
 struct PrefillPlan {
     bool io_bf16, conv, gated;
     bool allow_pipe;              // the pipelined launch may serve this call
+    bool force_pipe;              // ... and serves it wherever it can run (GDN_FLAG_PIPELINED)
     bool l2_handoff;              // pipelined prep units may leave their results in L2
     bool seg_ok;                  // the segment-parallel form may serve this call
     float* seg_state; float* seg_x; void* seg_out;   // its workspace buffers

@@ -2578,13 +2578,24 @@ static int pipe_post_blocks(const PrefillPlan& p, int cus) {
 // also wait), at most three quarters, so that prep workgroups always find
 // CUs.  Workgroup x is dispatched to XCD x % 8 from that XCD's own share; the
 // sweep and post counts are multiples of 8, so the bound holds on every XCD.
-// GDN_FLAG_SEPARATE_LAUNCHES (allow_pipe false) turns it off.
+// GDN_FLAG_SEPARATE_LAUNCHES (allow_pipe false) turns it off.  Small calls
+// take separate launches unless GDN_FLAG_PIPELINED (force_pipe) asks for the
+// pipelined one: a sweep of at most an eighth of the CUs (one sequence with
+// at most 16 value heads) or at most kPipeMinChunks chunk slots, where the
+// launch's waits and its prep workgroups' wider footprint cost more than the
+// overlap gains (one sequence of 128 / 320 / 1,024 / 1,984 tokens, separate
+// against pipelined: 2 key / 4 value heads 22.6 / 26.1 / 41.1 / 57.9 us
+// against 28.7 / 33.4 / 47.7 / 66.2; 8 / 16 23.8 / 29.2 / 44.1 / 66.5 against
+// 29.5 / 34.1 / 50.2 / 68.6; 16 / 32 25.5 / 30.3 / 51.2 / 82.8 against
+// 30.7 / 36.7 / 51.5 / 79.4).
+constexpr int kPipeMinChunks = 17;
 static bool use_pipe(const PrefillPlan& p) {
     if (!p.allow_pipe || !p.io_bf16 || p.sync.ready == nullptr || p.chunk_slots <= 0) return false;
     int seg_chunks = 0;
-    if (seg_count(p, &seg_chunks) > 1) return false;   // GDN_FLAG_SEGMENTS asked for segments
+    if (seg_count(p, &seg_chunks) > 1) return false;   // the segment-parallel form serves this call
 
     const int cus = device_cus(), ns = sweep_blocks(p);
+    if (!p.force_pipe && (8 * ns <= cus || p.chunk_slots < kPipeMinChunks)) return false;
     return 2 * ns <= cus && 4 * (ns + pipe_post_blocks(p, cus)) <= 3 * cus;
 }
 

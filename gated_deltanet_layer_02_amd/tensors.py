@@ -46,12 +46,13 @@ class PrefillCall:
                  slots: Optional[np.ndarray] = None, num_state_slots: int = 0,
                  snapshot_every: int = 0, snapshot_base: Optional[np.ndarray] = None,
                  num_snapshot_slots: int = 0, separate_launches: bool = False,
-                 prep_write_back: bool = False, segments: bool = False, device="cuda"):
+                 prep_write_back: bool = False, segments: bool = False, pipelined: bool = False,
+                 device="cuda"):
         """x["state"] / x["conv_state"] hold num_state_slots rows (a pool)
         when `slots` is given, else N rows; x["state"] is float32 or, with
         state_bf16, uint16 bf16 bits.  separate_launches / prep_write_back /
-        segments set GDN_FLAG_SEPARATE_LAUNCHES / GDN_FLAG_PREP_WRITE_BACK /
-        GDN_FLAG_SEGMENTS."""
+        segments / pipelined set GDN_FLAG_SEPARATE_LAUNCHES /
+        GDN_FLAG_PREP_WRITE_BACK / GDN_FLAG_SEGMENTS / GDN_FLAG_PIPELINED."""
         import torch
         self.cu_host = np.asarray(x["cu_seqlens"], dtype=np.int32)
         self.N = len(self.cu_host) - 1
@@ -78,7 +79,7 @@ class PrefillCall:
         self.desc = B.make_desc(self.N, self.T, Hk, Hv, B.GDN_BF16 if io_bf16 else B.GDN_F32,
                                 B.GDN_BF16 if state_bf16 else B.GDN_F32, scale, l2_eps, norm_eps, l2norm,
                                 separate_launches=separate_launches, prep_write_back=prep_write_back,
-                                segments=segments)
+                                segments=segments, pipelined=pipelined)
         self.out = empty_like_io((max(self.T, 1), Hv, 128), io_bf16, d)
         self.final_state = (torch.empty((rows, Hv, 128, 128), dtype=sdt, device=d)
                             if want_final_state else None)

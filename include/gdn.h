@@ -97,6 +97,12 @@ typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
  * that may take this form is larger (gdn_prefill_workspace_size takes the
  * flag and the default rule into account). */
 #define GDN_FLAG_SEGMENTS 0x10u
+/* Prefill launch form: the pipelined single launch wherever its conditions
+ * hold (see gdn_prefill, "Launches"), also for the small calls that otherwise
+ * take separate launches (one sequence with at most 16 value heads, or at
+ * most 16 chunk slots, where separate launches are faster) and instead of the
+ * default segment-parallel form.  GDN_FLAG_SEPARATE_LAUNCHES wins over it. */
+#define GDN_FLAG_PIPELINED 0x20u
 
 typedef struct {
     int32_t num_seqs;       /* N >= 1 */
@@ -160,9 +166,10 @@ gdn_status gdn_prefill_workspace_size(const gdn_desc* d, size_t* bytes);
  * between outputs and inputs is GDN_ERR_ALIAS (out against q, k, v, z) or
  * undefined.
  *
- * Launches: with bf16 io, when the sweep's workgroups need at most half of
- * the device's CUs (one or a few long sequences), the chunk prep and the
- * sweep run as one launch whose sweep workgroups wait for each chunk's prep
+ * Launches: with bf16 io, when the sweep's workgroups need more than an
+ * eighth and at most half of the device's CUs and there are more than 16
+ * chunk slots (one or a few long sequences at 32 value heads), the chunk prep
+ * and the sweep run as one launch whose sweep workgroups wait for each chunk's prep
  * units, and whose gated-norm workgroups wait for the sweep's output, through
  * flags in the workspace (GDN_FLAG_SEPARATE_LAUNCHES selects separate
  * launches instead).  A chunk's prep results stay in the L2 of the XCD that
@@ -203,7 +210,7 @@ gdn_status gdn_prefill_workspace_size(const gdn_desc* d, size_t* bytes);
  * with at most 16 value heads (one GPU's share of the 16 key / 32 value head
  * layer under 2-, 4- or 8-way head parallelism: the chain of chunk steps,
  * not the device's width, sets the time there), unless
- * GDN_FLAG_SEPARATE_LAUNCHES is given alone.
+ * GDN_FLAG_SEPARATE_LAUNCHES or GDN_FLAG_PIPELINED is given without it.
  */
 gdn_status gdn_prefill(const gdn_desc* d,
                        const void* q, const void* k, const void* v,

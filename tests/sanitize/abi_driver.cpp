@@ -213,7 +213,7 @@ int main() {
     }
     // rejected descriptors
     {
-        gdn_desc d = desc(1, 10, 2, 4, GDN_BF16, GDN_F32, 0x20);
+        gdn_desc d = desc(1, 10, 2, 4, GDN_BF16, GDN_F32, 0x40);
         size_t n = 0;
         CHECK(gdn_prefill_workspace_size(&d, &n) == GDN_ERR_UNSUPPORTED);
         d = desc(1, 10, 3, 4, GDN_BF16, GDN_F32, 0);

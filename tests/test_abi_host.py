@@ -102,8 +102,8 @@ def test_prefill_validation_errors():
         (dict(head_k_dim=64), {}, 3),
         (dict(head_v_dim=256), {}, 3),
         (dict(conv_kernel=3), {}, 3),
-        (dict(flags=0x20), {}, 3),
-        (dict(flags=0x1F), dict(ws_bytes=1024), 6),       # the launch-form and test flags are accepted
+        (dict(flags=0x40), {}, 3),
+        (dict(flags=0x3F), dict(ws_bytes=1024), 6),       # the launch-form and test flags are accepted
         (dict(io_dtype=5), {}, 4),
         (dict(state_dtype=B.GDN_BF16), {}, 4),           # gdn_prefill: fp32 state (gdn_prefill_ex: either)
         (dict(scale=float("nan")), {}, 9),

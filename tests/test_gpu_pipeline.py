@@ -69,7 +69,7 @@ def _run_both(p, x, expect_pipe, **kw):
     from gated_deltanet_layer_02_amd.tensors import PrefillCall
     res = {}
     for pipe in (True, False):
-        call = PrefillCall(x, Hk=p.Hk, Hv=p.Hv, io_bf16=True, separate_launches=not pipe, **kw)
+        call = PrefillCall(x, Hk=p.Hk, Hv=p.Hv, io_bf16=True, separate_launches=not pipe, pipelined=pipe, **kw)
         if not call.extended:
             st = _stages(call)
             say(f"  pipeline={int(pipe)}: stages {st}")
@@ -125,9 +125,29 @@ def test_pipeline_matches_separate_launches(name, lens, heads, opts, expect_pipe
     assert np.array_equal(res[True][0]["conv_state_out"], r_cs)
 
 
+@pytest.mark.parametrize("lens,heads", [([1000], (2, 4)), ([320], (16, 32)), ([1024], (16, 32)),
+                                         ([1984], (8, 16))], ids=["1000x2-4", "320x16-32", "1024x16-32", "1984x8-16"])
+def test_small_calls_take_separate_launches(lens, heads):
+    """One sequence whose sweep takes at most an eighth of the CUs (at most
+    16 value heads) or with at most 16 chunk slots: the plain call takes
+    separate launches (faster there), GDN_FLAG_PIPELINED the pipelined one,
+    with the same bits; every value head against the oracle."""
+    from gated_deltanet_layer_02_amd.tensors import PrefillCall
+    p = _problem(f"small-call-{lens[0]}-{heads[1]}", lens, Hk=heads[0], Hv=heads[1])
+    x = gs.generate(p)
+    assert "prep_sweep" not in _stages(PrefillCall(x, Hk=p.Hk, Hv=p.Hv, io_bf16=True))
+    res = _run_both(p, x, True)
+    _assert_same(res)
+    r_out, r_fs, r_cs = oracle.run_problem(p, x)
+    rep_ = compare_heads(p, io_to_f64(res[True][0]["out"]), res[True][0]["final_state"], r_out, r_fs,
+                         TOL_BF16, chunk_check=p.gate)
+    say(f"  {rep_}")
+
+
 def test_pipeline_pool_bf16_state_snapshots():
     """State pool rows by slot, bf16 state storage and chunk snapshots through
-    the pipelined launch (the same shape's plain call is pipelined)."""
+    the pipelined launch (asked for: the same shape's plain call, a small one,
+    takes separate launches)."""
     lens = [64 * 6 + 10, 64 * 4]
     p = _problem("pipe-pool", lens, Hk=2, Hv=4)
     x = gs.generate(p)
@@ -142,10 +162,12 @@ def test_pipeline_pool_bf16_state_snapshots():
     res = _run_both(p, x, True, state_bf16=True, slots=slots, num_state_slots=rows,
                     snapshot_every=every, snapshot_base=base, num_snapshot_slots=sum(counts))
     _assert_same(res)
-    # the same shape as a plain call takes the pipelined form
+    # the same shape as a plain call takes separate launches, and the
+    # pipelined form when asked for
     from gated_deltanet_layer_02_amd.tensors import PrefillCall
-    assert "prep_sweep" in _stages(PrefillCall(x | {"state": None, "conv_state": None}, Hk=p.Hk,
-                                               Hv=p.Hv, io_bf16=True))
+    plain = x | {"state": None, "conv_state": None}
+    assert "prep_sweep" not in _stages(PrefillCall(plain, Hk=p.Hk, Hv=p.Hv, io_bf16=True))
+    assert "prep_sweep" in _stages(PrefillCall(plain, Hk=p.Hk, Hv=p.Hv, io_bf16=True, pipelined=True))
     xo = dict(x, state=x["state"][slots], conv_state=x["conv_state"][slots])
     r_out, r_fs, r_cs = oracle.run_problem(p, xo)
     out = io_to_f64(res[True][0]["out"])
@@ -221,7 +243,7 @@ def test_pipeline_write_back_fallback():
     from gated_deltanet_layer_02_amd.tensors import PrefillCall
     p = _problem("pipe-fallback", [64 * 20 + 11], Hk=2, Hv=4)
     x = gs.generate(p)
-    call = PrefillCall(x, Hk=p.Hk, Hv=p.Hv, io_bf16=True)
+    call = PrefillCall(x, Hk=p.Hk, Hv=p.Hv, io_bf16=True, pipelined=True)
     assert "prep_sweep" in _stages(call)
     res, kept = [], []
     for write_back in (False, True):
@@ -253,7 +275,7 @@ def test_wait_failure_is_reported_per_call():
     ref.run()
     torch.cuda.synchronize()
     assert ref.wait_status() == 0
-    call = PrefillCall(x, Hk=p.Hk, Hv=p.Hv, io_bf16=True)
+    call = PrefillCall(x, Hk=p.Hk, Hv=p.Hv, io_bf16=True, pipelined=True)
     assert "prep_sweep" in _stages(call)
     assert call.wait_status() == 0
     say("pipeline: every wait gives up at once (forced), then a normal call")
