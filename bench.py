@@ -353,7 +353,43 @@ def bench_options(args, hip, pres):
             del calls
         row["speedup"] = round(row["separate_launches"]["us"] / row["default"]["us"], 3)
         shares[name] = row
-    return {"prefill_pool_bf16_snapshots": opts, "verify": ver, "tp_shares": shares}
+    # the serving stand-ins (93 new prompts of 250-350 tokens; a decode step of
+    # 93 sequences, fp32 state)
+    from gated_deltanet_layer_02_amd.binding import STAGE_NAMES
+    from gated_deltanet_layer_02_amd.tensors import DecodeCall
+    import torch
+    sv = gs.serving()
+    pp, pd = sv["prefill"], sv["decode"]
+    log(f"[bench] serving: {pp.name}; {pd.name}")
+    xp = gs.generate(pp)
+    calls = [PrefillCall(xp, Hk=pp.Hk, Hv=pp.Hv, io_bf16=True) for _ in range(args.buffer_sets)]
+    t = time_calls(hip, [c.run for c in calls], args.steps, args.warmup)
+    stream = torch.cuda.current_stream().cuda_stream
+    stages = {}
+    for r in range(4):
+        ev = [hip.event() for _ in range(2 + 2 * 16)]
+        ids = calls[r % len(calls)].run_profiled(ev, stream=stream)
+        torch.cuda.synchronize()
+        if r > 0:
+            for i, sid in enumerate(ids):
+                stages.setdefault(STAGE_NAMES[sid], []).append(hip.ms(ev[2 + 2 * i], ev[3 + 2 * i]) * 1e3)
+        for e in ev:
+            hip.destroy(e)
+    serve = {"prefill": {"workload": pp.name, "tokens": pp.T, "sequences": pp.N, "us": round(t * 1e6, 2),
+                         "tokens_per_s": round(pp.T / t, 1), "launch": launch_form(hip, calls[0]),
+                         "flop_frac_dense_tile": round(FLOP_LAYER * pp.T * pp.Hv / t / MFMA_BF16_PEAK, 4),
+                         "hbm_frac": round(layer_bytes(pp) / t / HBM_PEAK, 4),
+                         "stages_us_profiled": {k: round(sorted(v)[len(v) // 2], 2) for k, v in stages.items()}}}
+    del calls
+    xd = gs.generate(pd)
+    dc = DecodeCall(xd, Hk=pd.Hk, Hv=pd.Hv, io_bf16=True, state_bf16=False)
+    t = time_calls(hip, [dc.run], args.steps, args.warmup)
+    d = pd.dk   # head dim (D above is the verify leg's draft count)
+    moved = 2 * pd.N * pd.Hv * d * d * 4 + (2 * pd.N * pd.Hk * d + 3 * pd.N * pd.Hv * d) * 2 \
+        + 2 * pd.N * pd.Hv * 4 + 2 * pd.N * 3 * pd.Cch * 2 + pd.Cch * 4 * 2
+    serve["decode"] = {"workload": pd.name, "us": round(t * 1e6, 2), "tokens_per_s": round(pd.N / t, 1),
+                       "total_GBps": round(moved / t / 1e9, 1), "hbm_frac": round(moved / t / HBM_PEAK, 4)}
+    return {"prefill_pool_bf16_snapshots": opts, "verify": ver, "tp_shares": shares, "serving": serve}
 
 
 def layer_bytes(p):

@@ -150,6 +150,19 @@ def configs() -> dict:
     return c
 
 
+def serving() -> dict:
+    """Stand-ins for the serving benchmark of the SGLang cookbook's Qwen3-Next
+    page (ShareGPT prompts of about 300 tokens on average, about 93 requests in
+    flight; the dataset itself is not used): a prefill of 93 new prompts packed
+    with cu_seqlens, lengths uniform in [250, 350], zero initial states; and a
+    decode step of 93 sequences against seeded fp32 states."""
+    rng = np.random.default_rng(2001 + 7919)
+    lens = rng.integers(250, 350, size=93, endpoint=True).tolist()
+    return {"prefill": Problem("serving prefill, 93 prompts of 250-350 tokens", lens, seed=2001),
+            "decode": Problem("serving decode, 93 sequences, fp32 state", [1] * 93, init_state_std=0.01,
+                              conv_state_std=0.01, seed=2002, decode=True)}
+
+
 def generate(p: Problem) -> dict:
     """Draw every input of problem ``p``; fixed draw order per seed."""
     rng = np.random.default_rng(p.seed)

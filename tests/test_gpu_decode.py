@@ -57,6 +57,13 @@ def test_decode_configs(cfg):
     say(f"{cfg}: rel_l2 out {e_out:.2e} state {e_st:.2e}")
 
 
+def test_serving_decode():
+    """The serving stand-in: one decode step of 93 sequences, fp32 state."""
+    p = gs.serving()["decode"]
+    e_out, e_st = check_decode(p, gs.generate(p))
+    say(f"serving decode: rel_l2 out {e_out:.2e} state {e_st:.2e}")
+
+
 def test_decode_state_slots():
     p = gs.Problem("slots", [1] * 5, Hk=2, Hv=4, init_state_std=0.01, conv_state_std=0.01,
                    seed=21, decode=True)

@@ -93,6 +93,14 @@ def test_many_sequences_chunk_table(N):
     say(f"{N} sequences, {sum(lens)} tokens {check_prefill(p, gs.generate(p))}")
 
 
+def test_serving_prefill_all_heads():
+    """The serving stand-in: 93 new prompts of 250-350 tokens packed with
+    cu_seqlens at 16 key / 32 value heads (separate launches: 5,952 sweep
+    workgroups), every value head against the oracle."""
+    p = gs.serving()["prefill"]
+    say(f"serving prefill {check_prefill(p, gs.generate(p), batch=16)}")
+
+
 # Full sizes, every value head against the oracle (the bench's launch
 # configuration: plain calls, which take the pipelined form for C1 and C2 and
 # separate launches for C3).
