@@ -147,3 +147,51 @@ def test_snapshots_c1_shape_all_heads():
         worst = int(np.argmax(per_head))
         say(f"  snapshot {j}: rel_l2 {e:.2e}, worst head {worst}: {per_head[worst]:.2e}")
         assert e <= TOL_BF16 and max(per_head) <= TOL_BF16
+
+
+def test_short_packed_batch_pool_snapshots():
+    """40 packed sequences of 0 to 300 tokens at 16 key / 32 value heads (more
+    sweep workgroups than CUs, a few chunks each: the split-buffer sweep), with a
+    bf16 state pool of 48 rows updated through slots and a snapshot after
+    every chunk: outputs, pool rows and snapshots against the oracle, untouched
+    pool rows bitwise unchanged."""
+    from gated_deltanet_layer_02_amd.tensors import PrefillCall, to_host
+    import torch
+    rng = np.random.default_rng(4040)
+    lens = [int(L) for L in rng.choice([0, 1, 63, 64, 65, 130, 200, 257, 300], size=40)]
+    rows = 48
+    slots = rng.permutation(rows)[:40].astype(np.int32)
+    p = gs.Problem("short-pool", lens, init_state_std=0.01, conv_state_std=0.01, seed=4041)
+    x = gs.generate(p)
+    pool = gs.f32_to_bf16_bits((0.01 * rng.standard_normal((rows, p.Hv, 128, 128))).astype(np.float32))
+    cpool = gs.f32_to_bf16_bits((0.01 * rng.standard_normal((rows, 3, p.Cch))).astype(np.float32))
+    counts = [(L - 1) // 64 if L > 0 else 0 for L in lens]
+    base = np.concatenate([[0], np.cumsum(counts)[:-1]]).astype(np.int32)
+    total = int(sum(counts))
+    say(f"short packed batch, pool and snapshots: {sum(lens)} tokens, {total} snapshots")
+    xp = dict(x, state=pool, conv_state=cpool)
+    call = PrefillCall(xp, Hk=p.Hk, Hv=p.Hv, io_bf16=True, state_bf16=True, slots=slots,
+                       num_state_slots=rows, snapshot_every=1, snapshot_base=base,
+                       num_snapshot_slots=max(total, 1))
+    # the pool is updated in place: final state and conv state are the pool tensors
+    call.final_state = call.initial_state
+    call.conv_state_out = call.conv_state_in
+    call.run()
+    torch.cuda.synchronize()
+    assert call.wait_status() == 0
+    fs, cs = to_host(call.final_state), to_host(call.conv_state_out)
+    untouched = np.setdiff1d(np.arange(rows), slots)
+    assert np.array_equal(fs[untouched], pool[untouched]) and np.array_equal(cs[untouched], cpool[untouched])
+    xo = dict(x, state=gs.bf16_bits_to_f32(pool[slots]), conv_state=cpool[slots])
+    r_out, r_fs, r_cs = oracle.run_problem(p, xo)
+    out = io_to_f64(to_host(call.out))[: p.T]
+    e_out, e_fs = rel_l2(out, r_out), rel_l2(_state_f64(fs[slots]), r_fs)
+    assert np.array_equal(cs[slots], r_cs), "conv states not bit-exact"
+    snaps = _state_f64(to_host(call.snapshots))
+    worst = 0.0
+    for n, L in enumerate(lens):
+        for j in range(1, counts[n] + 1):
+            _, r_s, _ = _oracle_seq(p, xo, n, 64 * j, xo["state"][n], xo["conv_state"][n], heads=(0, p.Hv))
+            worst = max(worst, rel_l2(snaps[base[n] + j - 1], r_s[0]))
+    say(f"  rel_l2 out {e_out:.2e} state {e_fs:.2e} worst snapshot {worst:.2e}")
+    assert e_out <= TOL_BF16 and e_fs <= TOL_BF16 and worst <= TOL_BF16
