@@ -64,6 +64,15 @@ def test_serving_decode():
     say(f"serving decode: rel_l2 out {e_out:.2e} state {e_st:.2e}")
 
 
+def test_serving_decode_bf16_state():
+    """The same step of 93 sequences with the state stored in bf16 (the
+    cookbook's --mamba-ssm-dtype option)."""
+    p = gs.Problem("serving decode, 93 sequences, bf16 state", [1] * 93, state_dtype=gs.BF16,
+                   init_state_std=0.01, conv_state_std=0.01, seed=2003, decode=True)
+    e_out, e_st = check_decode(p, gs.generate(p))
+    say(f"serving decode, bf16 state: rel_l2 out {e_out:.2e} state {e_st:.2e}")
+
+
 def test_decode_state_slots():
     p = gs.Problem("slots", [1] * 5, Hk=2, Hv=4, init_state_std=0.01, conv_state_std=0.01,
                    seed=21, decode=True)
